@@ -1,0 +1,275 @@
+"""Seeded synthetic inputs for the grouped quantized MoE matmul + finalize-routing.
+
+This module only draws and encodes inputs (numpy, host memory).  It holds none
+of the method's arithmetic: no matmul, no dequantisation, no combine.  Both the
+GPU path's tests and the CPU oracle's tests take their inputs from here.
+
+Layouts follow the operator's parameter description
+("aclnnGroupedMatmulFinalizeRoutingWeightNzV2", parameter notes for Atlas
+A2/A3 and the Atlas 350 common constraints):
+  x1 int8 (m,k); x2 int8 (e,k,n) or int4 packed eight per int32 (e,k,n/8);
+  scale fp32 or bf16 (e,1,n); pertokenScale fp32 (m); logit fp32 (m);
+  groupList int64 (e) of type 0 (cumulative) or 1 (counts); rowIndex int64 or
+  int32 (m); sharedInput bf16 (bsdp,n) placed at sharedInputOffset inside an
+  output of outputBS rows.
+
+bf16 arrays are carried as their raw uint16 bit patterns.
+
+Every draw uses ``numpy.random.default_rng(seed)`` in a fixed order:
+counts -> rowIndex -> logit -> x1 -> x2 -> scale -> pertokenScale -> sharedInput.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+# ---------------------------------------------------------------- encodings
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit pattern, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit pattern -> fp32 (exact widening)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def pack_int4(values: np.ndarray) -> np.ndarray:
+    """Pack signed int4 values (..., n) in [-8, 7] into int32 words (..., n/8).
+
+    Column 8w+t goes to bits [4t, 4t+4) of word w (low nibble first), two's
+    complement -- the (e,k,n) <-> (e,k,n/8) correspondence of the operator's
+    parameter notes, with the nibble order read as little-endian.
+    """
+    v = np.asarray(values)
+    if v.shape[-1] % 8:
+        raise ValueError("last dimension must be a multiple of 8")
+    if v.min(initial=0) < -8 or v.max(initial=0) > 7:
+        raise ValueError("int4 values must lie in [-8, 7]")
+    nib = (v.astype(np.int64) & 0xF).astype(np.uint64)
+    nib = nib.reshape(*v.shape[:-1], v.shape[-1] // 8, 8)
+    shifts = (np.arange(8, dtype=np.uint64) * 4)
+    words = (nib << shifts).sum(axis=-1, dtype=np.uint64).astype(np.uint32)
+    return words.view(np.int32)
+
+
+# ---------------------------------------------------------------- container
+
+
+@dataclasses.dataclass
+class Problem:
+    """One set of operator inputs, host-resident, in the operator's layouts."""
+
+    name: str
+    m: int
+    k: int
+    n: int
+    e: int
+    x1: np.ndarray                       # int8 (m,k)
+    x2: np.ndarray                       # int8 (e,k,n) or int32 (e,k,n/8)
+    x2_int4: bool                        # True -> x2 is the packed int4 form
+    scale: Optional[np.ndarray]          # float32 or uint16(bf16) (e,1,n)
+    scale_bf16: bool
+    pertoken_scale: Optional[np.ndarray]  # float32 (m)
+    logit: Optional[np.ndarray]          # float32 (m)
+    group_list: np.ndarray               # int64 (e)
+    group_list_type: int                 # 0 cumulative, 1 counts
+    row_index: Optional[np.ndarray]      # int64 or int32 (m)
+    shared_input: Optional[np.ndarray]   # uint16(bf16) (bsdp,n)
+    shared_input_offset: int
+    output_bs: int
+    seed: int = 0
+    counts: Optional[np.ndarray] = None  # rows per expert (for statistics)
+
+    @property
+    def bsdp(self) -> int:
+        return 0 if self.shared_input is None else int(self.shared_input.shape[0])
+
+    @property
+    def covered_rows(self) -> int:
+        return int(self.counts.sum()) if self.counts is not None else self.m
+
+    @property
+    def nonempty_experts(self) -> int:
+        return int((self.counts > 0).sum()) if self.counts is not None else self.e
+
+
+def _group_list(counts: np.ndarray, group_list_type: int) -> np.ndarray:
+    counts = np.asarray(counts, dtype=np.int64)
+    return np.cumsum(counts).astype(np.int64) if group_list_type == 0 else counts.copy()
+
+
+def _row_index(rng, T: int, K: int, dtype) -> np.ndarray:
+    """Every token receives exactly K rows; rows are laid over the expert-sorted
+    order at random, so a (token, expert) pair may repeat."""
+    return rng.permutation(np.repeat(np.arange(T, dtype=np.int64), K)).astype(dtype)
+
+
+def _topk_softmax_logit(rng, T: int, K: int, row_index: np.ndarray, n_gate: int = 256) -> np.ndarray:
+    """Routing weights: per token, K largest of n_gate N(0,1) gate scores,
+    softmax in float64, stored as fp32; a token's j-th row (ascending row order)
+    takes weight j."""
+    scores = rng.standard_normal((T, n_gate))
+    top = -np.sort(-scores, axis=1)[:, :K]
+    w = np.exp(top - top[:, :1])
+    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    logit = np.empty(row_index.shape[0], dtype=np.float32)
+    seen = np.zeros(T, dtype=np.int64)
+    ri = row_index.astype(np.int64)
+    for i in range(ri.shape[0]):
+        t = ri[i]
+        logit[i] = w[t, seen[t] % K]
+        seen[t] += 1
+    return logit
+
+
+def _largest_remainder(weights: np.ndarray, total: int) -> np.ndarray:
+    q = weights / weights.sum() * total
+    base = np.floor(q).astype(np.int64)
+    rem = total - int(base.sum())
+    order = np.argsort(-(q - base), kind="stable")
+    base[order[:rem]] += 1
+    return base
+
+
+def _int8(rng, shape, lo, hi) -> np.ndarray:
+    return rng.integers(lo, hi + 1, size=shape, dtype=np.int8)
+
+
+# ---------------------------------------------------------------- named configs
+
+CONFIG_NAMES = ("tiny", "decode", "skewed", "prefill", "int4")
+
+
+def make_config(name: str, seed: int = 0) -> Problem:
+    """The five named workloads (sizes from the operator's A2/A3 limits:
+    k = 2048, n = 7168, e <= 256, m <= 131072)."""
+    rng = np.random.default_rng(seed)
+    if name == "tiny":
+        T, K, e, k, n, obs = 16, 2, 4, 256, 256, 16
+        counts = np.array([8, 8, 8, 8], dtype=np.int64)
+        glt = 0
+        ri = _row_index(rng, T, K, np.int64)
+        logit = rng.uniform(0.0, 1.0, size=T * K).astype(np.float32)
+        x1 = _int8(rng, (T * K, k), -8, 7)
+        x2 = _int8(rng, (e, k, n), -8, 7)
+        scale = rng.uniform(0.5, 1.5, size=(e, 1, n)).astype(np.float32)
+        pts = rng.uniform(0.5, 1.5, size=T * K).astype(np.float32)
+        return Problem(name, T * K, k, n, e, x1, x2, False, scale, False, pts, logit,
+                       _group_list(counts, glt), glt, ri, None, 0, obs, seed, counts)
+    if name == "decode":
+        T, K, e, k, n, obs = 512, 8, 8, 2048, 7168, 512
+        m = T * K
+        counts = rng.multinomial(m, np.full(e, 1.0 / e)).astype(np.int64)
+        glt = 1
+        ri = _row_index(rng, T, K, np.int64)
+        logit = _topk_softmax_logit(rng, T, K, ri)
+        x1 = _int8(rng, (m, k), -127, 127)
+        x2 = _int8(rng, (e, k, n), -127, 127)
+        scale = rng.uniform(1e-3, 1e-2, size=(e, 1, n)).astype(np.float32)
+        pts = rng.uniform(1e-3, 1e-2, size=m).astype(np.float32)
+        shared = f32_to_bf16_bits(rng.standard_normal((obs, n)).astype(np.float32))
+        return Problem(name, m, k, n, e, x1, x2, False, scale, False, pts, logit,
+                       _group_list(counts, glt), glt, ri, shared, 0, obs, seed, counts)
+    if name == "skewed":
+        T, K, e, k, n, obs = 256, 8, 256, 2048, 7168, 256
+        m = T * K
+        ranks = np.arange(1, e + 1, dtype=np.float64)
+        p_rank = ranks ** -1.2
+        p_rank /= p_rank.sum()
+        perm = rng.permutation(e)
+        p = np.empty(e)
+        p[perm] = p_rank
+        counts = rng.multinomial(m, p).astype(np.int64)
+        glt = 0
+        ri = _row_index(rng, T, K, np.int32)
+        logit = _topk_softmax_logit(rng, T, K, ri)
+        x1 = _int8(rng, (m, k), -127, 127)
+        x2 = _int8(rng, (e, k, n), -127, 127)
+        scale = rng.uniform(1e-3, 1e-2, size=(e, 1, n)).astype(np.float32)
+        pts = rng.uniform(1e-3, 1e-2, size=m).astype(np.float32)
+        return Problem(name, m, k, n, e, x1, x2, False, scale, False, pts, logit,
+                       _group_list(counts, glt), glt, ri, None, 0, obs, seed, counts)
+    if name == "prefill":
+        T, K, e, k, n, obs = 16384, 8, 32, 2048, 7168, 16384
+        m = T * K
+        u = rng.uniform(-0.2, 0.2, size=e)
+        counts = _largest_remainder(4096.0 * (1.0 + u), m)
+        glt = 0
+        ri = _row_index(rng, T, K, np.int64)
+        logit = _topk_softmax_logit(rng, T, K, ri)
+        x1 = _int8(rng, (m, k), -127, 127)
+        x2 = _int8(rng, (e, k, n), -127, 127)
+        scale = f32_to_bf16_bits(rng.uniform(1e-3, 1e-2, size=(e, 1, n)).astype(np.float32))
+        pts = rng.uniform(1e-3, 1e-2, size=m).astype(np.float32)
+        shared = f32_to_bf16_bits(rng.standard_normal((8192, n)).astype(np.float32))
+        return Problem(name, m, k, n, e, x1, x2, False, scale, True, pts, logit,
+                       _group_list(counts, glt), glt, ri, shared, 4096, obs, seed, counts)
+    if name == "int4":
+        T, K, e, k, n, obs = 4096, 8, 64, 2048, 7168, 4096
+        m = T * K
+        counts = rng.multinomial(m, rng.dirichlet(np.full(e, 0.5))).astype(np.int64)
+        glt = 1
+        ri = _row_index(rng, T, K, np.int64)
+        logit = _topk_softmax_logit(rng, T, K, ri)
+        x1 = _int8(rng, (m, k), -127, 127)
+        x2 = pack_int4(_int8(rng, (e, k, n), -8, 7))
+        scale = rng.uniform(1e-3, 1e-2, size=(e, 1, n)).astype(np.float32)
+        pts = rng.uniform(1e-3, 1e-2, size=m).astype(np.float32)
+        return Problem(name, m, k, n, e, x1, x2, True, scale, False, pts, logit,
+                       _group_list(counts, glt), glt, ri, None, 0, obs, seed, counts)
+    raise ValueError(f"unknown config {name!r}; choose from {CONFIG_NAMES}")
+
+
+# ---------------------------------------------------------------- random small cases
+
+
+def random_problem(seed: int, m: int, k: int, n: int, e: int, *,
+                   int4: bool = False, scale_bf16: bool = False,
+                   group_list_type: int = 0, row_index_dtype=np.int64,
+                   with_scale: bool = True, with_pts: bool = True,
+                   with_logit: bool = True, with_row_index: bool = True,
+                   bsdp: int = 0, shared_offset: int = 0, output_bs: Optional[int] = None,
+                   empty_frac: float = 0.25, uncovered: int = 0,
+                   lo: int = -128, hi: int = 127) -> Problem:
+    """A random problem of the given size for parity and invariant tests.
+
+    Rows per expert are random (some experts empty, with probability
+    ``empty_frac``); the last ``uncovered`` rows lie outside every group.
+    Destinations are uniform in [0, output_bs), so a destination may receive
+    any number of rows, including two from the same expert.
+    """
+    rng = np.random.default_rng(seed)
+    covered = m - uncovered
+    if covered < 0:
+        raise ValueError("uncovered > m")
+    w = rng.uniform(0.2, 1.0, size=e) * (rng.uniform(size=e) >= empty_frac)
+    if w.sum() == 0:
+        w[rng.integers(e)] = 1.0
+    counts = _largest_remainder(w, covered) if covered > 0 else np.zeros(e, dtype=np.int64)
+    if output_bs is None:
+        output_bs = max(1, m // 2)
+    ri = rng.integers(0, output_bs, size=m).astype(row_index_dtype) if with_row_index else None
+    logit = rng.uniform(0.0, 1.0, size=m).astype(np.float32) if with_logit else None
+    x1 = _int8(rng, (m, k), lo, hi)
+    if int4:
+        x2 = pack_int4(_int8(rng, (e, k, n), -8, 7))
+    else:
+        x2 = _int8(rng, (e, k, n), lo, hi)
+    scale = None
+    if with_scale:
+        s = rng.uniform(0.25, 2.0, size=(e, 1, n)).astype(np.float32)
+        scale = f32_to_bf16_bits(s) if scale_bf16 else s
+    pts = rng.uniform(0.25, 2.0, size=m).astype(np.float32) if with_pts else None
+    shared = None
+    if bsdp > 0:
+        shared = f32_to_bf16_bits(rng.standard_normal((bsdp, n)).astype(np.float32) * 64.0)
+    return Problem(f"random{seed}", m, k, n, e, x1, x2, int4, scale, scale_bf16 and with_scale,
+                   pts, logit, _group_list(counts, group_list_type), group_list_type, ri,
+                   shared, shared_offset, output_bs, seed, counts)
