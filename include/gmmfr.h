@@ -1,0 +1,182 @@
+/*
+ * gmmfr -- fused quantized MoE grouped matmul with finalize-routing combine,
+ * for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * Operation ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2", CANN operator
+ * documentation, function description): a GroupedMatmul whose output rows
+ * are combined by index (MoeFinalizeRouting), in one call.
+ *
+ *   Rows of x1 (m,k) int8 are sorted by expert and split into e groups by
+ *   groupList.  Row i of group g is multiplied by x2[g] (k,n) with int32
+ *   accumulation:   acc[i][j] = sum_kk x1[i][kk] * x2[g][kk][j].
+ *   It is dequantised and weighted, each product rounded to fp32:
+ *       y[i][j] = ((float(acc[i][j]) * scale[g][0][j]) * pertokenScale[i]) * logit[i]
+ *   (the order (acc * deqScale) * perTokenScale is the one spelled out by
+ *   the worked example of "matmul支持pertoken量化模式", ATB per-token quant
+ *   linear; the routing weight is applied last).
+ *   The output out (outputBS,n) fp32 starts at +0.0 with rows
+ *   [sharedInputOffset, sharedInputOffset + bsdp) set to the widened bf16
+ *   sharedInput, and every covered row i is added into out[rowIndex[i]].
+ *
+ * Two-stage use ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2", interface
+ * description: a first call validates and sizes the workspace, a second call
+ * runs on a stream):
+ *     size_t ws;  gmm_finalize_routing_workspace(&args, &ws);
+ *     ... allocate ws bytes of device memory ...
+ *     gmm_finalize_routing(&args, workspace, ws, stream);
+ *
+ * Ownership: every buffer, the workspace included, belongs to the caller and
+ * is device memory (except tuning_config, a host array read during the call).
+ * The library allocates and frees nothing, keeps no state between calls and
+ * is safe to call from several host threads.  gmm_finalize_routing only
+ * enqueues work on `stream` and returns; the caller keeps all buffers alive
+ * until the stream passes that point.
+ */
+#ifndef GMMFR_H
+#define GMMFR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ status codes
+ * The first call validates the arguments and reports the first rule broken
+ * ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2", return value of the first
+ * stage: errors are raised on invalid inputs).  Nothing is enqueued when a
+ * call returns a non-zero status. */
+typedef enum {
+  GMMFR_OK = 0,
+  GMMFR_ERR_NULLPTR = 1,      /* a required tensor, args or out-pointer is NULL   */
+  GMMFR_ERR_DTYPE = 2,        /* element type not accepted for that tensor        */
+  GMMFR_ERR_SHAPE = 3,        /* ranks or sizes inconsistent, or outside limits   */
+  GMMFR_ERR_ATTR = 4,         /* groupListType, offsets, transposes, flags        */
+  GMMFR_ERR_UNSUPPORTED = 5,  /* bias / offset / antiquant given, INT64 scale     */
+  GMMFR_ERR_ALIGN = 6,        /* a base pointer is not 16-byte aligned            */
+  GMMFR_ERR_WORKSPACE = 7,    /* workspace missing or smaller than required       */
+  GMMFR_ERR_HIP = 8           /* the HIP runtime refused a launch                 */
+} gmmfr_status;
+
+/* ------------------------------------------------------------ element types */
+typedef enum {
+  GMMFR_DT_NONE = 0,
+  GMMFR_DT_INT8 = 1,
+  GMMFR_DT_INT4 = 2,     /* signed 4-bit, two per byte, low nibble = lower column */
+  GMMFR_DT_INT32 = 3,
+  GMMFR_DT_INT64 = 4,
+  GMMFR_DT_FLOAT32 = 5,
+  GMMFR_DT_BFLOAT16 = 6
+} gmmfr_dtype;
+
+/* A dense, row-major, contiguous device tensor.  data == NULL means "absent",
+ * unless a dimension is 0 (an empty tensor may have a null pointer). */
+typedef struct {
+  void* data;
+  int32_t dtype;      /* gmmfr_dtype */
+  int32_t ndim;       /* 1..4        */
+  int64_t dims[4];
+} gmmfr_tensor;
+
+/* Combine strategy (our addition; the operator is non-deterministic by
+ * default and deterministic on request -- "aclnnGroupedMatmulFinalizeRouting
+ * WeightNzV2", determinism notes for Atlas A2/A3). */
+typedef enum {
+  GMMFR_COMBINE_AUTO = 0,     /* library picks the fastest strategy            */
+  GMMFR_COMBINE_ATOMIC = 1,   /* fp32 atomic adds from the GEMM epilogue       */
+  GMMFR_COMBINE_ORDERED = 2   /* rows sorted by destination, ordered reduction */
+} gmmfr_combine;
+
+/* Arguments.  Names follow the operator's parameter list. */
+typedef struct {
+  /* x1: INT8 (m,k), rows sorted by expert.                              required */
+  gmmfr_tensor x1;
+  /* x2: INT8 (e,k,n); or INT32 (e,k,n/8) holding eight int4 per word, column
+   * 8w+t in bits [4t,4t+4); or INT4 (e,k,n), the same bytes.          required */
+  gmmfr_tensor x2;
+  /* scale: FLOAT32 or BFLOAT16 (e,1,n) per-channel dequant scale.      optional
+   * (INT64 scale is listed by the operator without an encoding: UNSUPPORTED) */
+  gmmfr_tensor scale;
+  /* bias, offset, antiquantScale, antiquantOffset: reserved by the operator
+   * ("pass a null pointer"); must be absent, else UNSUPPORTED.                 */
+  gmmfr_tensor bias, offset, antiquant_scale, antiquant_offset;
+  /* pertokenScale: FLOAT32 (m).                                        optional */
+  gmmfr_tensor pertoken_scale;
+  /* groupList: INT64 (e); type 0 cumulative ends, type 1 counts.       required */
+  gmmfr_tensor group_list;
+  /* sharedInput: BFLOAT16 (bsdp,n), bsdp <= outputBS.                  optional */
+  gmmfr_tensor shared_input;
+  /* logit: FLOAT32 (m) routing weight of each row.                     optional */
+  gmmfr_tensor logit;
+  /* rowIndex: INT64 or INT32 (m), destination row of each source row;
+   * absent means the identity.                                         optional */
+  gmmfr_tensor row_index;
+  /* out: FLOAT32 (outputBS,n); every element is written.               required */
+  gmmfr_tensor out;
+  /* acc_out: INT32 (m,n) copy of the int32 accumulators of covered rows
+   * (other rows untouched).  A diagnostic for tests.                   optional */
+  gmmfr_tensor acc_out;
+
+  int64_t group_list_type;      /* 0 or 1                                        */
+  int64_t shared_input_offset;  /* >= 0, offset + bsdp <= outputBS               */
+  int64_t output_bs;            /* rows of out                                   */
+  int32_t transpose_x1;         /* must be 0                                     */
+  int32_t transpose_x2;         /* must be 0                                     */
+  int32_t deterministic;        /* 0: order of additions unspecified (default);
+                                   1: bit-reproducible, rows folded in ascending
+                                   source order onto the seed                    */
+  int32_t combine;              /* gmmfr_combine; ATOMIC with deterministic=1 is
+                                   rejected (ATTR)                               */
+  /* tuningConfig: host array; element 0 = expected rows per expert, used only
+   * to choose tiles ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2", function
+   * description: the first value is the expected token count per expert and
+   * the tiling follows it).  Results never depend on it.  May be NULL.        */
+  const int64_t* tuning_config;
+  int64_t tuning_config_len;
+} gmmfr_args;
+
+/*
+ * Limits of this implementation (beyond the operator's own rules):
+ *   1 <= e <= 1024, 0 <= m < 2^31, 1 <= n, n % 16 == 0 (n % 32 == 0 for int4
+ *   weights), 64 <= k <= 65536 with k % 64 == 0, outputBS >= 1,
+ *   m * n < 2^40, every base pointer 16-byte aligned.
+ * Device data are not validated (that would need a device-to-host read):
+ *   a groupList that breaks its rule is clamped to [0, m] and made
+ *   non-decreasing, rows whose rowIndex lies outside [0, outputBS) are
+ *   skipped.  Such inputs give an unspecified result but no out-of-bounds
+ *   access.
+ */
+
+/* Stage 1: validate `args` (host-side checks only, no device access, no HIP
+ * call) and report the workspace size in bytes for stage 2.
+ * Returns GMMFR_OK or the first rule broken. */
+int gmm_finalize_routing_workspace(const gmmfr_args* args, size_t* workspace_bytes);
+
+/* Stage 2: validate again, then enqueue the computation on `stream`
+ * (a hipStream_t; NULL = the null stream).  `workspace` is device memory of
+ * at least the stage-1 size (may be NULL when that size is 0).
+ * Returns GMMFR_OK, a validation status, GMMFR_ERR_WORKSPACE, or
+ * GMMFR_ERR_HIP when a launch fails. */
+int gmm_finalize_routing(const gmmfr_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Description of the plan stage 2 would use for `args` (host only). */
+typedef struct {
+  int32_t combine;          /* gmmfr_combine actually used (ATOMIC or ORDERED) */
+  int32_t tile_m, tile_n;   /* GEMM block tile                                 */
+  int32_t tile_k;           /* k step per pipeline stage                       */
+  int32_t grid;             /* workgroups of the grouped GEMM launch           */
+  int32_t int4_weights;     /* 1 if x2 is int4                                 */
+  int64_t workspace_bytes;
+  char gemm_kernel[96];     /* symbol-like name of the GEMM kernel variant     */
+} gmmfr_plan_info;
+
+int gmm_finalize_routing_plan(const gmmfr_args* args, gmmfr_plan_info* info);
+
+/* Short static text for a status code. */
+const char* gmmfr_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GMMFR_H */

@@ -1,0 +1,277 @@
+// C-ABI entry points: argument validation, planning, launch.
+//
+// Two-stage use as in "aclnnGroupedMatmulFinalizeRoutingWeightNzV2"
+// (interface description): the first call validates the arguments and sizes
+// the workspace, the second enqueues the work on a stream.  No executor object
+// is kept: the second call re-derives the same plan from the same arguments.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/gmmfr.h"
+#include "gmmfr_internal.h"
+
+namespace {
+
+using namespace gmmfr;
+
+struct Derived {
+  int64_t m, k, n, e, bsdp, output_bs;
+  bool int4;
+  bool scale_bf16;
+  bool row_index_i32;
+};
+
+// A tensor is given when it has data, or when it has no elements at all (an
+// allocator may hand out a null pointer for zero bytes).
+bool present(const gmmfr_tensor& t) {
+  if (t.data != nullptr) return true;
+  for (int i = 0; i < t.ndim && i < 4; ++i)
+    if (t.dims[i] == 0) return true;
+  return false;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool dims_are(const gmmfr_tensor& t, int nd, int64_t d0, int64_t d1 = -1, int64_t d2 = -1) {
+  if (t.ndim != nd) return false;
+  const int64_t want[3] = {d0, d1, d2};
+  for (int i = 0; i < nd; ++i)
+    if (t.dims[i] != want[i]) return false;
+  return true;
+}
+
+// Rules, in the order they are checked.  Operator rules cite
+// "aclnnGroupedMatmulFinalizeRoutingWeightNzV2" (parameter notes, common
+// constraints); the rest are this implementation's limits.
+int validate(const gmmfr_args* a, Derived* d) {
+  if (!a) return GMMFR_ERR_NULLPTR;
+  // x1, x2, groupList are required; out is where the result goes.
+  if (!present(a->x1) || !present(a->x2) || !present(a->group_list) || !present(a->out)) return GMMFR_ERR_NULLPTR;
+  // reserved parameters must be null; bias placement is not specified
+  if (present(a->bias) || present(a->offset) || present(a->antiquant_scale) || present(a->antiquant_offset))
+    return GMMFR_ERR_UNSUPPORTED;
+  if (present(a->scale) && a->scale.dtype == GMMFR_DT_INT64) return GMMFR_ERR_UNSUPPORTED;
+
+  // element types
+  if (a->x1.dtype != GMMFR_DT_INT8) return GMMFR_ERR_DTYPE;
+  if (a->x2.dtype != GMMFR_DT_INT8 && a->x2.dtype != GMMFR_DT_INT32 && a->x2.dtype != GMMFR_DT_INT4) return GMMFR_ERR_DTYPE;
+  if (present(a->scale) && a->scale.dtype != GMMFR_DT_FLOAT32 && a->scale.dtype != GMMFR_DT_BFLOAT16) return GMMFR_ERR_DTYPE;
+  if (present(a->pertoken_scale) && a->pertoken_scale.dtype != GMMFR_DT_FLOAT32) return GMMFR_ERR_DTYPE;
+  if (a->group_list.dtype != GMMFR_DT_INT64) return GMMFR_ERR_DTYPE;
+  if (present(a->shared_input) && a->shared_input.dtype != GMMFR_DT_BFLOAT16) return GMMFR_ERR_DTYPE;
+  if (present(a->logit) && a->logit.dtype != GMMFR_DT_FLOAT32) return GMMFR_ERR_DTYPE;
+  if (present(a->row_index) && a->row_index.dtype != GMMFR_DT_INT64 && a->row_index.dtype != GMMFR_DT_INT32)
+    return GMMFR_ERR_DTYPE;
+  if (a->out.dtype != GMMFR_DT_FLOAT32) return GMMFR_ERR_DTYPE;
+  if (present(a->acc_out) && a->acc_out.dtype != GMMFR_DT_INT32) return GMMFR_ERR_DTYPE;
+
+  // attributes
+  if (a->group_list_type != 0 && a->group_list_type != 1) return GMMFR_ERR_ATTR;
+  if (a->transpose_x1 != 0 || a->transpose_x2 != 0) return GMMFR_ERR_ATTR;
+  if (a->deterministic != 0 && a->deterministic != 1) return GMMFR_ERR_ATTR;
+  if (a->combine != GMMFR_COMBINE_AUTO && a->combine != GMMFR_COMBINE_ATOMIC && a->combine != GMMFR_COMBINE_ORDERED)
+    return GMMFR_ERR_ATTR;
+  if (a->deterministic == 1 && a->combine == GMMFR_COMBINE_ATOMIC) return GMMFR_ERR_ATTR;
+  if (a->tuning_config_len < 0 || (a->tuning_config_len > 0 && !a->tuning_config)) return GMMFR_ERR_ATTR;
+
+  // shapes
+  if (a->x1.ndim != 2) return GMMFR_ERR_SHAPE;
+  const int64_t m = a->x1.dims[0], k = a->x1.dims[1];
+  if (a->x2.ndim != 3) return GMMFR_ERR_SHAPE;
+  const int64_t e = a->x2.dims[0];
+  int64_t n;
+  if (a->x2.dtype == GMMFR_DT_INT32) n = a->x2.dims[2] * 8;
+  else n = a->x2.dims[2];
+  const bool int4 = a->x2.dtype != GMMFR_DT_INT8;
+  if (a->x2.dims[1] != k) return GMMFR_ERR_SHAPE;
+  if (m < 0 || m >= (int64_t(1) << 31)) return GMMFR_ERR_SHAPE;
+  if (e < 1 || e > kMaxExperts) return GMMFR_ERR_SHAPE;
+  if (k < 64 || k > 65536 || k % 64 != 0) return GMMFR_ERR_SHAPE;
+  if (n < 16 || n % 16 != 0 || (int4 && n % 32 != 0)) return GMMFR_ERR_SHAPE;
+  if (n > (int64_t(1) << 24) || m * n >= (int64_t(1) << 40)) return GMMFR_ERR_SHAPE;
+  if (present(a->scale) && !dims_are(a->scale, 3, e, 1, n)) return GMMFR_ERR_SHAPE;
+  if (present(a->pertoken_scale) && !dims_are(a->pertoken_scale, 1, m)) return GMMFR_ERR_SHAPE;
+  if (!dims_are(a->group_list, 1, e)) return GMMFR_ERR_SHAPE;
+  if (present(a->logit) && !dims_are(a->logit, 1, m)) return GMMFR_ERR_SHAPE;
+  if (present(a->row_index) && !dims_are(a->row_index, 1, m)) return GMMFR_ERR_SHAPE;
+  const int64_t obs = a->output_bs;
+  if (obs < 1 || obs >= (int64_t(1) << 31)) return GMMFR_ERR_SHAPE;
+  if (!dims_are(a->out, 2, obs, n)) return GMMFR_ERR_SHAPE;
+  if (present(a->acc_out) && !dims_are(a->acc_out, 2, m, n)) return GMMFR_ERR_SHAPE;
+  int64_t bsdp = 0;
+  if (present(a->shared_input)) {
+    if (a->shared_input.ndim != 2 || a->shared_input.dims[1] != n) return GMMFR_ERR_SHAPE;
+    bsdp = a->shared_input.dims[0];
+    // bsdp <= outputBS and sharedInputOffset + bsdp <= outputBS (Atlas 350 common constraints)
+    if (bsdp < 0 || bsdp > obs) return GMMFR_ERR_ATTR;
+    if (a->shared_input_offset < 0 || a->shared_input_offset + bsdp > obs) return GMMFR_ERR_ATTR;
+  } else if (a->shared_input_offset < 0) {
+    return GMMFR_ERR_ATTR;
+  }
+
+  // alignment of every present base pointer
+  const gmmfr_tensor* all[] = {&a->x1, &a->x2, &a->scale, &a->pertoken_scale, &a->group_list, &a->shared_input,
+                               &a->logit, &a->row_index, &a->out, &a->acc_out};
+  for (const gmmfr_tensor* t : all)
+    if (present(*t) && !aligned16(t->data)) return GMMFR_ERR_ALIGN;
+
+  if (d) {
+    d->m = m;
+    d->k = k;
+    d->n = n;
+    d->e = e;
+    d->bsdp = bsdp;
+    d->output_bs = obs;
+    d->int4 = int4;
+    d->scale_bf16 = present(a->scale) && a->scale.dtype == GMMFR_DT_BFLOAT16;
+    d->row_index_i32 = present(a->row_index) && a->row_index.dtype == GMMFR_DT_INT32;
+  }
+  return GMMFR_OK;
+}
+
+// Tile choice from the expected rows per expert: tuningConfig[0] when given
+// (the operator's tiling hint), else m / e.  Results do not depend on it.
+TileId choose_tile(const gmmfr_args* a, const Derived& d) {
+  int64_t expect = (d.m + d.e - 1) / d.e;
+  if (a->tuning_config_len > 0 && a->tuning_config[0] > 0) expect = a->tuning_config[0];
+  if (expect >= 1024) return kTile256x256;
+  if (expect >= 256) return kTile128x256;
+  if (expect >= 64) return kTile64x256;
+  return kTile32x256;
+}
+
+Combine choose_combine(const gmmfr_args* a, const Derived& d) {
+  if (a->deterministic == 1 || a->combine == GMMFR_COMBINE_ORDERED) return kCombineOrdered;
+  if (a->combine == GMMFR_COMBINE_ATOMIC) return kCombineAtomic;
+  // fp32 atomics retire at a fixed rate per L2 channel; past about a million
+  // contributions the ordered reduction (extra y traffic) is the faster path.
+  return d.m * d.n >= (int64_t(1) << 20) ? kCombineOrdered : kCombineAtomic;
+}
+
+int make_plan(const gmmfr_args* a, const Derived& d, int cu_count, Plan* plan) {
+  plan->combine = choose_combine(a, d);
+  plan->tile = choose_tile(a, d);
+  const TileShape ts = tile_shape(plan->tile);
+  const int64_t ntn = (d.n + ts.bn - 1) / ts.bn;
+  const int64_t max_tiles = ((d.m + ts.bm - 1) / ts.bm + d.e) * ntn;
+  if (max_tiles >= (int64_t(1) << 31)) return GMMFR_ERR_SHAPE;
+  const int64_t resident = (int64_t)std::max(cu_count, 1) * tile_occupancy(plan->tile);
+  plan->grid = d.m > 0 ? (int32_t)std::min(max_tiles, resident) : 0;
+  plan->workspace_bytes = plan->combine == kCombineOrdered ? ordered_workspace(d.m, d.n, d.output_bs).total : 0;
+  return GMMFR_OK;
+}
+
+LaunchArgs to_launch(const gmmfr_args* a, const Derived& d) {
+  LaunchArgs l;
+  l.x1 = (const int8_t*)a->x1.data;
+  l.x2 = a->x2.data;
+  l.scale = a->scale.data;
+  l.pertoken = (const float*)a->pertoken_scale.data;
+  l.logit = (const float*)a->logit.data;
+  l.group_list = (const int64_t*)a->group_list.data;
+  l.row_index = a->row_index.data;
+  l.shared = (const uint16_t*)a->shared_input.data;
+  l.out = (float*)a->out.data;
+  l.acc_out = (int32_t*)a->acc_out.data;
+  l.m = d.m;
+  l.k = d.k;
+  l.n = d.n;
+  l.e = (int32_t)d.e;
+  l.group_list_type = (int32_t)a->group_list_type;
+  l.scale_bf16 = d.scale_bf16;
+  l.row_index_i32 = d.row_index_i32;
+  l.int4 = d.int4;
+  l.bsdp = d.bsdp;
+  l.shared_offset = present(a->shared_input) ? a->shared_input_offset : 0;
+  l.output_bs = d.output_bs;
+  return l;
+}
+
+int device_cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return cus;
+}
+
+bool log_enabled() {
+  const char* v = std::getenv("GMMFR_LOG");
+  return v && v[0] == '1';
+}
+
+}  // namespace
+
+extern "C" {
+
+int gmm_finalize_routing_workspace(const gmmfr_args* args, size_t* workspace_bytes) {
+  if (!workspace_bytes) return GMMFR_ERR_NULLPTR;
+  Derived d;
+  int st = validate(args, &d);
+  if (st != GMMFR_OK) return st;
+  Plan plan;
+  st = make_plan(args, d, 1, &plan);
+  if (st != GMMFR_OK) return st;
+  *workspace_bytes = plan.workspace_bytes;
+  return GMMFR_OK;
+}
+
+int gmm_finalize_routing(const gmmfr_args* args, void* workspace, size_t workspace_bytes, void* stream) {
+  Derived d;
+  int st = validate(args, &d);
+  if (st != GMMFR_OK) return st;
+  const int cus = device_cu_count();
+  if (cus <= 0) return GMMFR_ERR_HIP;
+  Plan plan;
+  st = make_plan(args, d, cus, &plan);
+  if (st != GMMFR_OK) return st;
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes)) return GMMFR_ERR_WORKSPACE;
+  if (plan.workspace_bytes > 0 && !aligned16(workspace)) return GMMFR_ERR_ALIGN;
+  if (log_enabled())
+    std::fprintf(stderr, "[gmmfr] m=%lld k=%lld n=%lld e=%lld combine=%s %s grid=%d ws=%zu\n", (long long)d.m,
+                 (long long)d.k, (long long)d.n, (long long)d.e, plan.combine == kCombineOrdered ? "ordered" : "atomic",
+                 tile_kernel_name(plan.tile, d.int4), plan.grid, plan.workspace_bytes);
+  const int err = launch_all(to_launch(args, d), plan, workspace, stream);
+  return err == 0 ? GMMFR_OK : GMMFR_ERR_HIP;
+}
+
+int gmm_finalize_routing_plan(const gmmfr_args* args, gmmfr_plan_info* info) {
+  if (!info) return GMMFR_ERR_NULLPTR;
+  Derived d;
+  int st = validate(args, &d);
+  if (st != GMMFR_OK) return st;
+  Plan plan;
+  st = make_plan(args, d, 256, &plan);
+  if (st != GMMFR_OK) return st;
+  const TileShape ts = tile_shape(plan.tile);
+  std::memset(info, 0, sizeof(*info));
+  info->combine = plan.combine == kCombineOrdered ? GMMFR_COMBINE_ORDERED : GMMFR_COMBINE_ATOMIC;
+  info->tile_m = ts.bm;
+  info->tile_n = ts.bn;
+  info->tile_k = ts.bk;
+  info->grid = plan.grid;
+  info->int4_weights = d.int4 ? 1 : 0;
+  info->workspace_bytes = (int64_t)plan.workspace_bytes;
+  std::snprintf(info->gemm_kernel, sizeof(info->gemm_kernel), "%s", tile_kernel_name(plan.tile, d.int4));
+  return GMMFR_OK;
+}
+
+const char* gmmfr_status_string(int status) {
+  switch (status) {
+    case GMMFR_OK: return "ok";
+    case GMMFR_ERR_NULLPTR: return "null pointer";
+    case GMMFR_ERR_DTYPE: return "unsupported element type";
+    case GMMFR_ERR_SHAPE: return "inconsistent or unsupported shape";
+    case GMMFR_ERR_ATTR: return "invalid attribute";
+    case GMMFR_ERR_UNSUPPORTED: return "unsupported optional input";
+    case GMMFR_ERR_ALIGN: return "misaligned pointer";
+    case GMMFR_ERR_WORKSPACE: return "workspace missing or too small";
+    case GMMFR_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

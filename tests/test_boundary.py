@@ -1,0 +1,183 @@
+"""C-ABI boundary on the CPU: the library loads, exports every function the
+header declares, and the first stage validates arguments without touching a
+device (pointers here are fake, aligned, never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_moe_grouped_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for f in sorted(os.listdir(inc)):
+        if f.endswith(".h"):
+            text = open(os.path.join(inc, f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\([^;{]*\)\s*;", text, flags=re.M)
+    return names
+
+
+def test_library_exports_every_declared_function():
+    lib = B.lib()
+    declared = _declared_functions()
+    assert set(B.EXPORTED) <= set(declared)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+# ---------------------------------------------------------------- fake descriptors
+
+_next = [0x10000]
+
+
+def _fake(dtype, *dims, ptr=None):
+    t = B.Tensor()
+    if ptr is None:
+        _next[0] += 0x100000
+        ptr = _next[0]
+    t.data = ptr
+    t.dtype = dtype
+    t.ndim = len(dims)
+    for i, d in enumerate(dims):
+        t.dims[i] = d
+    return t
+
+
+def _args(m=512, k=2048, n=7168, e=8, obs=256, int4=False, **over):
+    a = B.Args()
+    a.x1 = _fake(B.DT_INT8, m, k)
+    a.x2 = _fake(B.DT_INT32, e, k, n // 8) if int4 else _fake(B.DT_INT8, e, k, n)
+    a.scale = _fake(B.DT_FLOAT32, e, 1, n)
+    a.pertoken_scale = _fake(B.DT_FLOAT32, m)
+    a.group_list = _fake(B.DT_INT64, e)
+    a.logit = _fake(B.DT_FLOAT32, m)
+    a.row_index = _fake(B.DT_INT64, m)
+    a.out = _fake(B.DT_FLOAT32, obs, n)
+    a.output_bs = obs
+    for key, v in over.items():
+        setattr(a, key, v)
+    return a
+
+
+def _ws(a):
+    n = ctypes.c_size_t(12345)
+    st = B.lib().gmm_finalize_routing_workspace(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+def test_valid_atomic_needs_no_workspace():
+    a = _args(m=32, k=256, n=256, e=4, obs=16)
+    a.combine = B.COMBINE["atomic"]
+    assert _ws(a) == (B.OK, 0)
+
+
+def test_ordered_workspace_formula():
+    m, n, obs = 4096, 7168, 512
+    a = _args(m=m, n=n, obs=obs)
+    a.deterministic = 1
+
+    def al(x):
+        return (x + 255) // 256 * 256
+    want = al(m * n * 4) + al(obs * 4) * 2 + al((obs + 1) * 4) + al(m * 4)
+    assert _ws(a) == (B.OK, want)
+
+
+def test_auto_picks_ordered_for_large_problems():
+    a = _args(m=131072, n=7168, obs=16384, e=32)
+    info = B.PlanInfo()
+    assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
+    assert info.combine == B.COMBINE["ordered"]
+    assert info.tile_m == 256
+
+
+def test_plan_does_not_depend_on_data_and_follows_hint():
+    a = _args(m=4096, n=7168, obs=512, e=8)
+    info = B.PlanInfo()
+    B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info))
+    base = info.tile_m
+    hint = (ctypes.c_int64 * 1)(8)
+    a.tuning_config = ctypes.cast(hint, ctypes.POINTER(ctypes.c_int64))
+    a.tuning_config_len = 1
+    B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info))
+    assert info.tile_m == 32 and base != 32
+
+
+CASES = [
+    ("nullptr_x1", dict(x1=B.Tensor()), B.ERR_NULLPTR),
+    ("nullptr_group_list", dict(group_list=B.Tensor()), B.ERR_NULLPTR),
+    ("nullptr_out", dict(out=B.Tensor()), B.ERR_NULLPTR),
+    ("bias_reserved", dict(bias=_fake(B.DT_FLOAT32, 8, 7168)), B.ERR_UNSUPPORTED),
+    ("offset_reserved", dict(offset=_fake(B.DT_FLOAT32, 8, 1, 7168)), B.ERR_UNSUPPORTED),
+    ("antiquant_reserved", dict(antiquant_scale=_fake(B.DT_FLOAT32, 8, 1, 7168)), B.ERR_UNSUPPORTED),
+    ("scale_int64", dict(scale=_fake(B.DT_INT64, 8, 1, 7168)), B.ERR_UNSUPPORTED),
+    ("x1_dtype", dict(x1=_fake(B.DT_FLOAT32, 512, 2048)), B.ERR_DTYPE),
+    ("x2_dtype", dict(x2=_fake(B.DT_BFLOAT16, 8, 2048, 7168)), B.ERR_DTYPE),
+    ("group_list_dtype", dict(group_list=_fake(B.DT_INT32, 8)), B.ERR_DTYPE),
+    ("row_index_dtype", dict(row_index=_fake(B.DT_FLOAT32, 512)), B.ERR_DTYPE),
+    ("shared_dtype", dict(shared_input=_fake(B.DT_FLOAT32, 128, 7168)), B.ERR_DTYPE),
+    ("out_dtype", dict(out=_fake(B.DT_BFLOAT16, 256, 7168)), B.ERR_DTYPE),
+    ("group_list_type", dict(group_list_type=2), B.ERR_ATTR),
+    ("transpose_x2", dict(transpose_x2=1), B.ERR_ATTR),
+    ("transpose_x1", dict(transpose_x1=1), B.ERR_ATTR),
+    ("det_with_atomic", dict(deterministic=1, combine=1), B.ERR_ATTR),
+    ("k_mismatch", dict(x2=_fake(B.DT_INT8, 8, 1024, 7168)), B.ERR_SHAPE),
+    ("k_not_mult_64", dict(x1=_fake(B.DT_INT8, 512, 2000), x2=_fake(B.DT_INT8, 8, 2000, 7168)), B.ERR_SHAPE),
+    ("n_not_mult_16", dict(x2=_fake(B.DT_INT8, 8, 2048, 7160), scale=B.Tensor(),
+                           out=_fake(B.DT_FLOAT32, 256, 7160)), B.ERR_SHAPE),
+    ("too_many_experts", dict(x2=_fake(B.DT_INT8, 1025, 2048, 16), scale=B.Tensor(), group_list=_fake(B.DT_INT64, 1025),
+                              out=_fake(B.DT_FLOAT32, 256, 16)), B.ERR_SHAPE),
+    ("scale_shape", dict(scale=_fake(B.DT_FLOAT32, 8, 7168)), B.ERR_SHAPE),
+    ("group_list_len", dict(group_list=_fake(B.DT_INT64, 7)), B.ERR_SHAPE),
+    ("pts_len", dict(pertoken_scale=_fake(B.DT_FLOAT32, 511)), B.ERR_SHAPE),
+    ("out_rows", dict(out=_fake(B.DT_FLOAT32, 255, 7168)), B.ERR_SHAPE),
+    ("shared_too_tall", dict(shared_input=_fake(B.DT_BFLOAT16, 257, 7168)), B.ERR_ATTR),
+    ("shared_offset", dict(shared_input=_fake(B.DT_BFLOAT16, 128, 7168), shared_input_offset=129), B.ERR_ATTR),
+    ("negative_offset", dict(shared_input=_fake(B.DT_BFLOAT16, 128, 7168), shared_input_offset=-1), B.ERR_ATTR),
+    ("misaligned", dict(logit=_fake(B.DT_FLOAT32, 512, ptr=0x7000004)), B.ERR_ALIGN),
+]
+
+
+@pytest.mark.parametrize("name,over,code", CASES, ids=[c[0] for c in CASES])
+def test_stage_one_rejects(name, over, code):
+    a = _args()
+    for key, v in over.items():
+        setattr(a, key, v)
+    st, ws = _ws(a)
+    assert st == code, (B.STATUS_NAMES.get(st), B.STATUS_NAMES.get(code))
+    assert ws == 12345  # untouched on error
+
+
+def test_int4_shapes_accepted_and_checked():
+    assert _ws(_args(int4=True))[0] == B.OK
+    a = _args(int4=True)
+    a.x2 = _fake(B.DT_INT4, 8, 2048, 7168)   # same bytes, logical int4 shape
+    assert _ws(a)[0] == B.OK
+    a = _args(n=7168 + 16)                    # int8 accepts n % 16 == 0
+    assert _ws(a)[0] == B.OK
+    a = _args(n=7168 + 16, int4=True)         # int4 needs n % 32 == 0
+    assert _ws(a)[0] == B.ERR_SHAPE
+
+
+def test_zero_rows_accepted():
+    assert _ws(_args(m=0))[0] == B.OK
+
+
+def test_status_strings():
+    for code in range(9):
+        assert B.lib().gmmfr_status_string(code)
+    assert B.lib().gmmfr_status_string(99) == b"unknown status"
+
+
+def test_stage_two_rejects_before_any_launch():
+    """Validation in stage two runs before any HIP call, so a bad argument
+    returns its status even on a host without a GPU."""
+    a = _args()
+    a.group_list_type = 5
+    st = B.lib().gmm_finalize_routing(ctypes.byref(a), None, 0, None)
+    assert st == B.ERR_ATTR
