@@ -1,0 +1,253 @@
+"""Benchmark: int8 TOPS of the fused grouped MoE GEMM + finalize-routing on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config prefill]
+                    [--combine auto|atomic|ordered] [--no-cpu-baseline]
+
+A step is one library call (seed, grouped int8 GEMM with fused dequant, combine
+by rowIndex) over the whole workload, inputs resident in HBM.  The default
+workload is the prefill-shaped one (m = 131072 rows from 16384 tokens x top-8,
+e = 32, k = 2048, n = 7168, bf16 scale, sharedInput (8192, 7168) at offset
+4096), synthetic and seeded.  Prints one JSON line.
+
+ops per step = 2 * M_eff * k * n (multiply and add of the covered rows).
+The roofline entry is the grouped GEMM kernel alone, timed with HIP events
+recorded on the launch stream right around it, against the dense int8 MFMA
+peak (5.0 POP/s).  The cpu_baseline entry times the CPU oracle on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 MFMA, TOP/s
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, GB/s
+KERNEL_SRC = os.path.join(ROOT, "quantized_moe_grouped_amd", "csrc", "gmmfr_kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="prefill", choices=["tiny", "decode", "skewed", "prefill", "int4"])
+    ap.add_argument("--combine", default="auto", choices=["auto", "atomic", "ordered"])
+    ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=0, help="rows in the oracle sample (0 = auto)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (torch copy_) 5 times: the reference kernel whose "
+                         "FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic figures")
+    return ap.parse_args()
+
+
+class Hip:
+    """The HIP runtime already loaded in this process (torch's), for events."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev
+
+    def record(self, ev, stream):
+        assert self.lib.hipEventRecord(ev, ctypes.c_void_p(stream)) == 0
+
+    def elapsed_ms(self, a, b):
+        assert self.lib.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+
+def algorithmic_bytes(p):
+    """Each input read once, the output written once (no atomics, no y)."""
+    wbytes = p.k * p.n // 2 if p.x2_int4 else p.k * p.n
+    sbytes = 0 if p.scale is None else (2 if p.scale_bf16 else 4) * p.n
+    return (p.covered_rows * p.k + p.nonempty_experts * (wbytes + sbytes) + p.m * (4 + 4 + p.row_index.itemsize)
+            + p.e * 8 + p.bsdp * p.n * 2 + p.output_bs * p.n * 4)
+
+
+def cpu_baseline(p, rows_wanted: int):
+    """Time the oracle (whole computation) on a sample: the first rows of every
+    expert group, all k and n, same destinations and output size."""
+    import numpy as np
+    import oracle
+    from quantized_moe_grouped_amd import workloads as W
+
+    counts = np.diff(np.concatenate([[0], np.cumsum(p.counts)]))
+    frac = rows_wanted / max(p.covered_rows, 1)
+    take = np.minimum(counts, np.ceil(counts * frac).astype(np.int64))
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    idx = np.concatenate([np.arange(s, s + t) for s, t in zip(starts, take)]) if take.sum() else np.zeros(0, np.int64)
+    q = W.Problem(p.name + "-sample", int(idx.size), p.k, p.n, p.e, p.x1[idx], p.x2, p.x2_int4, p.scale,
+                  p.scale_bf16, None if p.pertoken_scale is None else p.pertoken_scale[idx],
+                  None if p.logit is None else p.logit[idx], np.cumsum(take).astype(np.int64), 0,
+                  None if p.row_index is None else p.row_index[idx], p.shared_input, p.shared_input_offset,
+                  p.output_bs, p.seed, take)
+    oracle.load()
+    t0 = time.perf_counter()
+    oracle.run(q, want_acc=False)
+    dt = time.perf_counter() - t0
+    ops = 2.0 * q.m * q.k * q.n
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": f"{q.m} of {p.covered_rows} rows (first rows of each of the {p.e} experts), full k={p.k}, "
+                      f"n={p.n}, seed + combine into outputBS={p.output_bs}; {dt:.2f} s wall",
+            "seconds": dt}
+
+
+def traffic_from_profiles(kernel_name: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"gmm_kernel_{workload}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        if rec.get("kernel_source_sha256") != src_hash or rec.get("kernel") != kernel_name:
+            return None
+        return rec.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path runs on one GPU's share; see the design notes for sharding).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from quantized_moe_grouped_amd import binding as B
+    from quantized_moe_grouped_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 5
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30,
+                          "copy_GBps_read_plus_write": round(2 * (1 << 30) / dt / 1e9, 1)}), flush=True)
+        return
+    print(f"[bench] generating {args.config} seed {args.seed}", file=sys.stderr, flush=True)
+    p = W.make_config(args.config, args.seed)
+    dev = "cuda"
+
+    def T(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def bf16(a):
+        return None if a is None else T(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+    x1, x2 = T(p.x1), T(p.x2)
+    scale = None if p.scale is None else (bf16(p.scale) if p.scale_bf16 else T(p.scale))
+    pts, logit, gl, ri = T(p.pertoken_scale), T(p.logit), T(p.group_list), T(p.row_index)
+    shared = bf16(p.shared_input)
+    out = torch.empty((p.output_bs, p.n), dtype=torch.float32, device=dev)
+    cargs, keep = B.make_args(x1, x2, gl, out, scale=scale, pertoken_scale=pts, logit=logit, row_index=ri,
+                              shared_input=shared, shared_input_offset=p.shared_input_offset,
+                              group_list_type=p.group_list_type, deterministic=args.deterministic,
+                              combine=args.combine)
+    plan = B.plan(cargs)
+    ws_bytes = B.workspace_size(cargs)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = Hip()
+    ev_all = (hip.event(), hip.event())
+    ev_g = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    print(f"[bench] plan {plan}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        B.run(cargs, ws, stream)
+    torch.cuda.synchronize()
+    hip.record(ev_all[0], stream)
+    for s in range(args.steps):
+        st = B.lib().gmm_finalize_routing_profiled(ctypes.byref(cargs), ctypes.c_void_p(ws.data_ptr()),
+                                                    ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream),
+                                                    ev_g[s][0], ev_g[s][1])
+        if st != 0:
+            raise B.GmmfrError(st, "gmm_finalize_routing_profiled")
+    hip.record(ev_all[1], stream)
+    torch.cuda.synchronize()
+    total_ms = hip.elapsed_ms(ev_all[0], ev_all[1])
+    gemm_ms = [hip.elapsed_ms(a, b) for a, b in ev_g]
+    ms_step = total_ms / args.steps
+    gemm_avg = sum(gemm_ms) / len(gemm_ms)
+    print(f"[bench] step {ms_step:.4f} ms, gemm kernel {gemm_avg:.4f} ms "
+          f"(min {min(gemm_ms):.4f}, max {max(gemm_ms):.4f})", file=sys.stderr, flush=True)
+
+    ops = 2.0 * p.covered_rows * p.k * p.n
+    tops = ops / (ms_step * 1e-3) / 1e12
+    gemm_tops = ops / (gemm_avg * 1e-3) / 1e12
+    abytes = algorithmic_bytes(p)
+    t_roof_ms = max(ops / (PEAK_INT8_TOPS * 1e12), abytes / (PEAK_HBM_GBS * 1e9)) * 1e3
+    kname = plan["gemm_kernel"]
+    res = {
+        "metric": "int8 TOPS (and % of MFMA/HBM roofline) for GMM+finalize-routing at 1 GPU",
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded generator; random int8 weights/activations, routing and scales of the stated shapes)",
+        "config": {"workload": p.name, "tokens": p.output_bs, "top_k": p.m // max(p.output_bs, 1), "m": p.m,
+                   "e": p.e, "k": p.k, "n": p.n, "weights": "int4" if p.x2_int4 else "int8",
+                   "output_bs": p.output_bs, "shared_rows": p.bsdp, "combine": plan["combine"],
+                   "deterministic": bool(args.deterministic), "seed": args.seed,
+                   "ops_per_step": ops, "algorithmic_bytes_per_step": abytes,
+                   "path_roofline_frac": round(t_roof_ms / ms_step, 4)},
+        "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS,
+                     "unit": "TOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+                     "launch_ms": round(gemm_avg, 5),
+                     "traffic": traffic_from_profiles(kname, p.name)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rows = args.cpu_sample_rows
+        if not rows:
+            # size the sample for about 15 s of oracle time from a short calibration run
+            cal = cpu_baseline(p, min(p.covered_rows, 256))
+            rate_rows = min(p.covered_rows, 256) / max(cal["seconds"], 1e-3)
+            rows = int(max(256, min(p.covered_rows, 15.0 * rate_rows)))
+        print(f"[bench] cpu oracle on a {rows}-row sample", file=sys.stderr, flush=True)
+        cb = cpu_baseline(p, rows)
+        cb.pop("seconds")
+        res["cpu_baseline"] = cb
+    print(json.dumps(res), flush=True)
+    del keep
+
+
+if __name__ == "__main__":
+    main()

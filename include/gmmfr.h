@@ -160,6 +160,14 @@ int gmm_finalize_routing_workspace(const gmmfr_args* args, size_t* workspace_byt
  * GMMFR_ERR_HIP when a launch fails. */
 int gmm_finalize_routing(const gmmfr_args* args, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Diagnostic variant of stage 2 for measurement: identical work, plus
+ * hipEventRecord(gemm_start) right before and hipEventRecord(gemm_stop) right
+ * after the grouped GEMM launch, on `stream`.  Both events are hipEvent_t
+ * created by the caller (either may be NULL).  No event is recorded when the
+ * call returns an error or when there is no GEMM launch (m == 0). */
+int gmm_finalize_routing_profiled(const gmmfr_args* args, void* workspace, size_t workspace_bytes, void* stream,
+                                  void* gemm_start, void* gemm_stop);
+
 /* Description of the plan stage 2 would use for `args` (host only). */
 typedef struct {
   int32_t combine;          /* gmmfr_combine actually used (ATOMIC or ORDERED) */

@@ -21,8 +21,8 @@ STATUS_NAMES = {0: "OK", 1: "NULLPTR", 2: "DTYPE", 3: "SHAPE", 4: "ATTR", 5: "UN
 DT_NONE, DT_INT8, DT_INT4, DT_INT32, DT_INT64, DT_FLOAT32, DT_BFLOAT16 = range(7)
 COMBINE = {"auto": 0, "atomic": 1, "ordered": 2}
 
-EXPORTED = ("gmm_finalize_routing_workspace", "gmm_finalize_routing", "gmm_finalize_routing_plan",
-            "gmmfr_status_string")
+EXPORTED = ("gmm_finalize_routing_workspace", "gmm_finalize_routing", "gmm_finalize_routing_profiled",
+            "gmm_finalize_routing_plan", "gmmfr_status_string")
 
 
 class GmmfrError(RuntimeError):
@@ -70,6 +70,9 @@ def lib():
         L.gmm_finalize_routing_workspace.restype = ctypes.c_int
         L.gmm_finalize_routing.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.gmm_finalize_routing.restype = ctypes.c_int
+        L.gmm_finalize_routing_profiled.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_size_t,
+                                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.gmm_finalize_routing_profiled.restype = ctypes.c_int
         L.gmm_finalize_routing_plan.argtypes = [ctypes.POINTER(Args), ctypes.POINTER(PlanInfo)]
         L.gmm_finalize_routing_plan.restype = ctypes.c_int
         L.gmmfr_status_string.argtypes = [ctypes.c_int]

@@ -138,7 +138,6 @@ int validate(const gmmfr_args* a, Derived* d) {
 TileId choose_tile(const gmmfr_args* a, const Derived& d) {
   int64_t expect = (d.m + d.e - 1) / d.e;
   if (a->tuning_config_len > 0 && a->tuning_config[0] > 0) expect = a->tuning_config[0];
-  if (expect >= 1024) return kTile256x256;
   if (expect >= 256) return kTile128x256;
   if (expect >= 64) return kTile64x256;
   return kTile32x256;
@@ -160,7 +159,9 @@ int make_plan(const gmmfr_args* a, const Derived& d, int cu_count, Plan* plan) {
   const int64_t max_tiles = ((d.m + ts.bm - 1) / ts.bm + d.e) * ntn;
   if (max_tiles >= (int64_t(1) << 31)) return GMMFR_ERR_SHAPE;
   const int64_t resident = (int64_t)std::max(cu_count, 1) * tile_occupancy(plan->tile);
-  plan->grid = d.m > 0 ? (int32_t)std::min(max_tiles, resident) : 0;
+  int64_t grid = std::min(max_tiles, resident);
+  if (grid > 8) grid -= grid % 8;  // whole XCD rounds: workgroups are dealt to the 8 XCDs in turn
+  plan->grid = d.m > 0 ? (int32_t)grid : 0;
   plan->workspace_bytes = plan->combine == kCombineOrdered ? ordered_workspace(d.m, d.n, d.output_bs).total : 0;
   return GMMFR_OK;
 }
@@ -219,7 +220,8 @@ int gmm_finalize_routing_workspace(const gmmfr_args* args, size_t* workspace_byt
   return GMMFR_OK;
 }
 
-int gmm_finalize_routing(const gmmfr_args* args, void* workspace, size_t workspace_bytes, void* stream) {
+static int run_stage2(const gmmfr_args* args, void* workspace, size_t workspace_bytes, void* stream,
+                      void* const* gemm_events) {
   Derived d;
   int st = validate(args, &d);
   if (st != GMMFR_OK) return st;
@@ -234,8 +236,18 @@ int gmm_finalize_routing(const gmmfr_args* args, void* workspace, size_t workspa
     std::fprintf(stderr, "[gmmfr] m=%lld k=%lld n=%lld e=%lld combine=%s %s grid=%d ws=%zu\n", (long long)d.m,
                  (long long)d.k, (long long)d.n, (long long)d.e, plan.combine == kCombineOrdered ? "ordered" : "atomic",
                  tile_kernel_name(plan.tile, d.int4), plan.grid, plan.workspace_bytes);
-  const int err = launch_all(to_launch(args, d), plan, workspace, stream);
+  const int err = launch_all(to_launch(args, d), plan, workspace, stream, gemm_events);
   return err == 0 ? GMMFR_OK : GMMFR_ERR_HIP;
+}
+
+int gmm_finalize_routing(const gmmfr_args* args, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_stage2(args, workspace, workspace_bytes, stream, nullptr);
+}
+
+int gmm_finalize_routing_profiled(const gmmfr_args* args, void* workspace, size_t workspace_bytes, void* stream,
+                                  void* gemm_start, void* gemm_stop) {
+  void* ev[2] = {gemm_start, gemm_stop};
+  return run_stage2(args, workspace, workspace_bytes, stream, ev);
 }
 
 int gmm_finalize_routing_plan(const gmmfr_args* args, gmmfr_plan_info* info) {

@@ -12,11 +12,10 @@ enum Combine : int32_t { kCombineAtomic = 1, kCombineOrdered = 2 };
 
 // GEMM tile variants compiled into the library.
 enum TileId : int32_t {
-  kTile256x256 = 0,   // BM=256 BN=256, 2x2 waves of 128x128
-  kTile128x256 = 1,   // BM=128 BN=256, 1x4 waves of 128x64
-  kTile64x256 = 2,    // BM=64  BN=256, 1x4 waves of 64x64
-  kTile32x256 = 3,    // BM=32  BN=256, 1x4 waves of 32x64
-  kNumTiles = 4
+  kTile128x256 = 0,   // BM=128 BN=256, 2x2 waves of 64x128, 3 stages
+  kTile64x256 = 1,    // BM=64  BN=256, 1x4 waves of 64x64, 3 stages
+  kTile32x256 = 2,    // BM=32  BN=256, 1x4 waves of 32x64, 3 stages
+  kNumTiles = 3
 };
 
 struct TileShape {
@@ -59,7 +58,8 @@ struct Plan {
 };
 
 // Enqueue the whole computation.  Returns 0 or a hipError_t value.
-int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* stream);
+// gemm_events: optional {start, stop} hipEvent_t recorded around the GEMM.
+int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* stream, void* const* gemm_events);
 
 // Workgroups per CU the GEMM variant is compiled for.
 int tile_occupancy(TileId id);

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "gmmfr_internal.h"
 
@@ -160,9 +161,30 @@ __device__ __forceinline__ int swz_a(int r) {
 }
 __device__ __forceinline__ int swz_b(int r) { return r & 7; }
 
-__device__ __forceinline__ void lds_dma16(const void* gsrc, LDS_PTR(void) ldst) {
-  __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
+// HBM -> LDS copy of 16 bytes per lane: lane i of the wave writes LDS bytes
+// [lds_base + 16 i, lds_base + 16 i + 16).  lds_base must be wave-uniform.
+// Written as inline asm so that the compiler does not track these LDS writes
+// (it would otherwise wait for every copy in flight before each LDS read and
+// each barrier); completion is awaited explicitly with wait_vmcnt before the
+// workgroup barrier that publishes a stage.  M0 is set here and used by
+// nothing else in these kernels.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gsrc) : "memory");
 }
+// Same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (saddr form): one VGPR per copy instead of two.
+__device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const LDS_PTR(void))p;
+}
+
+// Workgroup barrier that publishes LDS written by ds_write (lgkmcnt) but does
+// not wait for copies in flight (the caller waits for those it needs).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // int4 word -> 8 int8 holding 16 * value, in column order (two dwords).
 __device__ __forceinline__ void unpack_int4_x16(uint32_t w, uint32_t& d0, uint32_t& d1) {
@@ -172,117 +194,288 @@ __device__ __forceinline__ void unpack_int4_x16(uint32_t w, uint32_t& d0, uint32
   d1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // t4 t5 t6 t7
 }
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int OCC, bool INT4>
+// Compile-time loop helper.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Tile order inside one expert: groups of kGroupM m-tiles, n-tiles swept
+// inside a group with the m-tile fastest, so 64 consecutive tiles (the
+// tiles resident on one XCD at a time) form an 8 x 8 block that shares A row
+// panels and B column panels in that XCD's L2.
+constexpr int kGroupM = 8;
+
+// Position of one output tile.
+struct TileCoord {
+  int g;            // expert
+  int64_t row0;     // first row of the tile in x1
+  int64_t col0;     // first column
+  int valid_rows;   // rows of the tile inside the expert's group (<= BM)
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ TileCoord tile_coord(const KParams& p, const int32_t* s_ends, const int32_t* s_tile_pre,
+                                                int t) {
+  TileCoord c;
+  c.g = find_group(s_tile_pre, p.e, t);
+  const int local = t - s_tile_pre[c.g];
+  const int64_t row_start = c.g ? s_ends[c.g - 1] : 0;
+  const int64_t row_end = s_ends[c.g];
+  const int mtiles = (int)((row_end - row_start + BM - 1) / BM);
+  const int grp = local / (kGroupM * p.n_tiles_n);
+  const int in_grp = local - grp * kGroupM * p.n_tiles_n;
+  const int gsize = min(kGroupM, mtiles - grp * kGroupM);
+  const int mt = grp * kGroupM + in_grp % gsize;
+  const int nt = in_grp / gsize;
+  c.row0 = row_start + (int64_t)mt * BM;
+  c.col0 = (int64_t)nt * BN;
+  c.valid_rows = (int)min((int64_t)BM, row_end - c.row0);
+  return c;
+}
+
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int OCC, bool INT4, int COMBINE>
 __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int KK = BK / 32;
   constexpr int CPR_A = BK / 16, CPR_B = BN / 16;
   constexpr int A_BYTES = BM * BK, B_BYTES = BK * BN;
   constexpr int A_SLOTS = BM * CPR_A, B_SLOTS = BK * CPR_B;
   constexpr int NWAVES = kThreads / 64;
+  constexpr int A_INSTR = (A_SLOTS + kThreads - 1) / kThreads;    // per thread (whole waves may idle)
+  constexpr int B_INSTR = (B_SLOTS + kThreads - 1) / kThreads;
+  constexpr int B4_CHUNKS = BK * (BN / 32);                       // 16-byte packed chunks
+  constexpr int B4_PER = (B4_CHUNKS + kThreads - 1) / kThreads;
+  // vector-memory ops one thread issues per stage (DMA and int4 register
+  // loads).  When A_SLOTS is not a multiple of the block, the last A copy is
+  // issued by the first waves only; those waves wait with the larger count.
+  constexpr int B_ISSUED = INT4 ? B4_PER : B_INSTR;
+  constexpr int LOADS_FULL = A_INSTR + B_ISSUED;
+  constexpr int LOADS_SHORT = A_INSTR - 1 + B_ISSUED;
   static_assert(WAVES_M * WAVES_N == NWAVES, "4 waves");
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(BN >= 128, "B swizzle needs 8 chunks per row");
   static_assert(A_SLOTS % 64 == 0 && B_SLOTS % 64 == 0, "whole waves per copy");
+  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert((STAGES - 2) * LOADS_FULL < 64, "vmcnt range");
+  static_assert(KK % 2 == 0, "fragment double buffer alternates within a stage");
 
-  __shared__ __attribute__((aligned(16))) int8_t smA[2 * A_BYTES];
-  __shared__ __attribute__((aligned(16))) int8_t smB[2 * B_BYTES];
-  __shared__ int32_t s_ends[kMaxExperts];
-  __shared__ int32_t s_tile_pre[kMaxExperts + 1];
-  __shared__ int64_t s_scan[kThreads];
-  __shared__ float s_pts[BM], s_logit[BM];
-  __shared__ int32_t s_dest[BM];
+  __shared__ __attribute__((aligned(16))) int8_t sA[STAGES * A_BYTES];
+  __shared__ __attribute__((aligned(16))) int8_t sB[STAGES * B_BYTES];
+  // per-expert tables, sized by e at launch: ends[e], tile prefix[e + 1]
+  extern __shared__ __attribute__((aligned(16))) int32_t s_dyn[];
+  int32_t* s_ends = s_dyn;
+  int32_t* s_tile_pre = s_dyn + p.e;
+  int64_t* s_scan = (int64_t*)sA;  // scan scratch, used before the first copy into sA
+  static_assert(STAGES * A_BYTES >= kThreads * 8, "scan scratch fits in the A stages");
+  // per-row epilogue factors, double-buffered across consecutive tiles
+  __shared__ __attribute__((aligned(16))) float s_pts[2][BM];
+  __shared__ __attribute__((aligned(16))) float s_logit[2][BM];
+  __shared__ __attribute__((aligned(16))) int32_t s_dest[2][BM];
 
   build_group_table(p, BM, s_ends, s_tile_pre, s_scan);
   const int total_tiles = s_tile_pre[p.e];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const bool a_full = ((A_INSTR - 1) * NWAVES + wave) * 64 < A_SLOTS;  // wave-uniform
   const int64_t k = p.k, n = p.n;
   const int ktiles = (int)(k / BK);
 
-  for (int t = blockIdx.x; t < total_tiles; t += gridDim.x) {
-    const int g = find_group(s_tile_pre, p.e, t);
-    const int local = t - s_tile_pre[g];
-    const int mt = local / p.n_tiles_n, nt = local % p.n_tiles_n;
-    const int64_t row_start = g ? s_ends[g - 1] : 0;
-    const int64_t row_end = s_ends[g];
-    const int64_t row0 = row_start + (int64_t)mt * BM;
-    const int64_t col0 = (int64_t)nt * BN;
+  // consecutive logical tiles on one XCD (workgroups are dealt round-robin to the 8 XCDs)
+  const int G = gridDim.x;
+  int t = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  if (t >= total_tiles) return;
 
-    // per-row epilogue factors for this tile
-    for (int r = tid; r < BM; r += kThreads) {
-      const int64_t row = row0 + r;
-      const bool valid = row < row_end;
-      s_pts[r] = (valid && p.pertoken) ? p.pertoken[row] : 1.0f;
-      s_logit[r] = (valid && p.logit) ? p.logit[row] : 1.0f;
-      s_dest[r] = valid ? (int32_t)dest_row(p, row) : -1;
+  auto coord = [&](int tt) { return tile_coord<BM, BN>(p, s_ends, s_tile_pre, tt); };
+
+  // ---- per-tile copy sources: wave-uniform bases plus per-lane offsets
+  // (bytes, < BM*k resp. < BK*n, so they fit in 32 bits)
+  uint32_t a_off[A_INSTR];
+  uint32_t b_off[INT4 ? 1 : B_INSTR];
+  const int8_t* a_base = p.x1;
+  const int8_t* b_base = nullptr;
+  const uint32_t* w4 = nullptr;
+  int64_t b4_col0 = 0;
+  uint4 b4reg[INT4 ? B4_PER : 1];
+  auto set_sources = [&](const TileCoord& c) {
+    a_base = p.x1 + c.row0 * k;
+#pragma unroll
+    for (int q = 0; q < A_INSTR; ++q) {
+      const int slot = (q * NWAVES + wave) * 64 + lane;
+      const int r = (slot / CPR_A) % BM, cpos = slot % CPR_A;
+      const int64_t row = min(c.row0 + r, p.m - 1);  // rows past the group: loaded, never stored
+      a_off[q] = (uint32_t)((row - c.row0) * k + ((cpos ^ swz_a<BK>(r)) * 16));
     }
+    if constexpr (!INT4) {
+      b_base = (const int8_t*)p.x2 + (int64_t)c.g * k * n + c.col0;
+#pragma unroll
+      for (int q = 0; q < B_INSTR; ++q) {
+        const int slot = (q * NWAVES + wave) * 64 + lane;
+        const int r = (slot / CPR_B) % BK, cpos = slot % CPR_B;
+        const int64_t col = min(c.col0 + ((cpos ^ swz_b(r)) * 16), n - 16);  // past n: loaded, never stored
+        b_off[q] = (uint32_t)((int64_t)r * n + (col - c.col0));
+      }
+    } else {
+      w4 = (const uint32_t*)p.x2 + (int64_t)c.g * k * (n / 8);
+      b4_col0 = c.col0;
+    }
+  };
 
-    // ---- global -> LDS copy of one k-stage
-    const int8_t* x1 = p.x1;
-    auto load_a = [&](int stage, int64_t k0) {
+  auto issue_a = [&](int sc, int kt) {
+    const int8_t* base = a_base + (int64_t)kt * BK;
 #pragma unroll
-      for (int q = 0; q < (A_SLOTS + kThreads - 1) / kThreads; ++q) {
-        const int slot_base = (q * NWAVES + wave) * 64;
-        if (slot_base < A_SLOTS) {
-          const int slot = slot_base + lane;
-          const int r = slot / CPR_A, cpos = slot % CPR_A;
-          const int c = cpos ^ swz_a<BK>(r);
-          const int64_t row = min(row0 + r, p.m - 1);  // rows past the group: discarded later
-          lds_dma16(x1 + row * k + k0 + c * 16, (LDS_PTR(void))(smA + stage * A_BYTES + slot_base * 16));
-        }
-      }
-    };
-    auto load_b8 = [&](int stage, int64_t k0) {
-      const int8_t* w = (const int8_t*)p.x2 + (int64_t)g * k * n;
+    for (int q = 0; q < A_INSTR; ++q) {
+      const int slot_base = (q * NWAVES + wave) * 64;
+      if ((A_SLOTS % (NWAVES * 64)) == 0 || slot_base < A_SLOTS)
+        lds_dma16_sv(base, a_off[q], __builtin_amdgcn_readfirstlane(lds_addr(sA + sc * A_BYTES + slot_base * 16)));
+    }
+  };
+  auto issue_b8 = [&](int sc, int kt) {
+    const int8_t* base = b_base + (int64_t)kt * BK * n;
 #pragma unroll
-      for (int q = 0; q < (B_SLOTS + kThreads - 1) / kThreads; ++q) {
-        const int slot_base = (q * NWAVES + wave) * 64;
-        if (slot_base < B_SLOTS) {
-          const int slot = slot_base + lane;
-          const int r = slot / CPR_B, cpos = slot % CPR_B;
-          const int c = cpos ^ swz_b(r);
-          const int64_t col = min(col0 + c * 16, n - 16);  // columns past n: discarded later
-          lds_dma16(w + (k0 + r) * n + col, (LDS_PTR(void))(smB + stage * B_BYTES + slot_base * 16));
-        }
-      }
-    };
-    // int4: each lane fetches 16 bytes = 32 packed columns, unpacks to two
-    // 16-byte int8 chunks (values x16) and writes them to LDS itself.
-    constexpr int B4_CHUNKS = BK * (BN / 32);
-    constexpr int B4_PER_THREAD = (B4_CHUNKS + kThreads - 1) / kThreads;
-    uint4 b4reg[INT4 ? B4_PER_THREAD : 1];
-    auto fetch_b4 = [&](int64_t k0) {
-      const uint32_t* w = (const uint32_t*)p.x2 + (int64_t)g * k * (n / 8);
+    for (int q = 0; q < B_INSTR; ++q) {
+      const int slot_base = (q * NWAVES + wave) * 64;
+      if ((B_SLOTS % (NWAVES * 64)) == 0 || slot_base < B_SLOTS)
+        lds_dma16_sv(base, b_off[q], __builtin_amdgcn_readfirstlane(lds_addr(sB + sc * B_BYTES + slot_base * 16)));
+    }
+  };
+  auto fetch_b4 = [&](int kt) {
+    const int64_t k0 = (int64_t)kt * BK;
 #pragma unroll
-      for (int q = 0; q < B4_PER_THREAD; ++q) {
-        const int s = q * kThreads + tid;
-        if (s < B4_CHUNKS) {
-          const int r = s / (BN / 32), cc = s % (BN / 32);
-          const int64_t col = min(col0 + cc * 32, n - 32);
-          b4reg[q] = *(const uint4*)(w + (k0 + r) * (n / 8) + col / 8);
-        }
+    for (int q = 0; q < B4_PER; ++q) {
+      const int s = q * kThreads + tid;
+      if (s < B4_CHUNKS) {
+        const int r = s / (BN / 32), cc = s % (BN / 32);
+        const int64_t col = min(b4_col0 + cc * 32, n - 32);
+        b4reg[q] = *(const uint4*)(w4 + (k0 + r) * (n / 8) + col / 8);
       }
-    };
-    auto store_b4 = [&](int stage) {
+    }
+  };
+  auto store_b4 = [&](int sc) {
 #pragma unroll
-      for (int q = 0; q < B4_PER_THREAD; ++q) {
-        const int s = q * kThreads + tid;
-        if (s < B4_CHUNKS) {
-          const int r = s / (BN / 32), cc = s % (BN / 32);
-          uint4 c0, c1;
-          unpack_int4_x16(b4reg[q].x, c0.x, c0.y);
-          unpack_int4_x16(b4reg[q].y, c0.z, c0.w);
-          unpack_int4_x16(b4reg[q].z, c1.x, c1.y);
-          unpack_int4_x16(b4reg[q].w, c1.z, c1.w);
-          int8_t* base = smB + stage * B_BYTES + r * BN;
-          *(uint4*)(base + (((2 * cc) ^ swz_b(r)) << 4)) = c0;
-          *(uint4*)(base + (((2 * cc + 1) ^ swz_b(r)) << 4)) = c1;
-        }
+    for (int q = 0; q < B4_PER; ++q) {
+      const int s = q * kThreads + tid;
+      if (s < B4_CHUNKS) {
+        const int r = s / (BN / 32), cc = s % (BN / 32);
+        uint4 c0, c1;
+        unpack_int4_x16(b4reg[q].x, c0.x, c0.y);
+        unpack_int4_x16(b4reg[q].y, c0.z, c0.w);
+        unpack_int4_x16(b4reg[q].z, c1.x, c1.y);
+        unpack_int4_x16(b4reg[q].w, c1.z, c1.w);
+        int8_t* base = sB + sc * B_BYTES + r * BN;
+        *(uint4*)(base + (((2 * cc) ^ swz_b(r)) << 4)) = c0;
+        *(uint4*)(base + (((2 * cc + 1) ^ swz_b(r)) << 4)) = c1;
       }
-    };
+    }
+  };
+  // stage fill: int4 issues its register loads first so that waiting for
+  // them later does not also wait for the A copy issued after them
+  auto issue_stage = [&](int sc, int kt) {
+    if constexpr (INT4) {
+      fetch_b4(kt);
+      issue_a(sc, kt);
+    } else {
+      issue_a(sc, kt);
+      issue_b8(sc, kt);
+    }
+  };
+  // stages 0 .. STAGES-2 of a tile (the buffers must be free)
+  auto prologue = [&]() {
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st) {
+      if (st < ktiles) {
+        issue_stage(st, st);
+        if constexpr (INT4) store_b4(st);
+      }
+    }
+  };
+  // per-row factors of a tile into buffer `pb`: loads first, LDS writes later
+  float fp_pts = 1.0f, fp_logit = 1.0f;
+  int32_t fp_dest = -1;
+  auto fetch_rows = [&](const TileCoord& c) {
+    fp_pts = 1.0f;
+    fp_logit = 1.0f;
+    fp_dest = -1;
+    if (tid < BM && tid < c.valid_rows) {
+      const int64_t row = c.row0 + tid;
+      if (p.pertoken) fp_pts = p.pertoken[row];
+      if (p.logit) fp_logit = p.logit[row];
+      fp_dest = (int32_t)dest_row(p, row);
+    }
+  };
+  auto store_rows = [&](int pb) {
+    if (tid < BM) {
+      s_pts[pb][tid] = fp_pts;
+      s_logit[pb][tid] = fp_logit;
+      s_dest[pb][tid] = fp_dest;
+    }
+  };
+  static_assert(BM <= kThreads, "one thread per tile row");
+
+  auto load_frags = [&](int sc, int kk, v4i (&af)[FM], v4i (&bf)[FN]) {
+    const int8_t* As = sA + sc * A_BYTES;
+    const int8_t* Bs = sB + sc * B_BYTES;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + i * 32 + (lane & 31);
+      const int c = kk * 2 + (lane >> 5);
+      af[i] = *(const LDS_PTR(v4i))(As + r * BK + ((c ^ swz_a<BK>(r)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = kk * 32 + (lane >> 5) * 16 + ((lane & 15) >> 1);
+      const int col = wn * WTN + j * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+      const int8_t* a0 = Bs + r * BN + (((col >> 4) ^ swz_b(r)) << 4) + (col & 15);
+      const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0));
+      const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0 + 8 * BN));  // same swizzle
+      bf[j] = v4i{lo.x, lo.y, hi.x, hi.y};
+    }
+  };
+
+  // Entering stage j of the current tile: its copies are complete, every wave
+  // has finished reading stage j-1 (its fragments are in registers), so stage
+  // j+STAGES-1 may overwrite stage j-1's buffer.  Stage 0 of a tile waits for
+  // everything (the previous tile's stores are counted by the same counter).
+  auto enter_stage = [&](int j) {
+    if (j > 0 && j + STAGES - 2 < ktiles) {
+      if (a_full) wait_vmcnt<(STAGES - 2) * LOADS_FULL>();
+      else wait_vmcnt<(STAGES - 2) * LOADS_SHORT>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    if (j + STAGES - 1 < ktiles) issue_stage((j + STAGES - 1) % STAGES, j + STAGES - 1);
+  };
+
+  // ---- first tile
+  TileCoord cur = coord(t);
+  int pb = 0;
+  set_sources(cur);
+  prologue();
+  fetch_rows(cur);
+  wait_vmcnt<0>();
+  store_rows(pb);
+
+  while (true) {
+    const int t_next = t + G;
+    const bool has_next = t_next < total_tiles;
+    TileCoord nxt = cur;
+    if (has_next) nxt = coord(t_next);
 
     v16i acc[FM][FN];
 #pragma unroll
@@ -290,90 +483,120 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = v16i{0};
 
-    // prologue: stage 0
-    load_a(0, 0);
-    if constexpr (INT4) {
-      fetch_b4(0);
-      store_b4(0);
-    } else {
-      load_b8(0, 0);
-    }
+    enter_stage(0);
+    // the next tile's row factors go to the other buffer while this one runs
+    if (has_next) fetch_rows(nxt);
+    v4i af[2][FM], bf[2][FN];
+    load_frags(0, 0, af[0], bf[0]);
 
+    int stage = 0;
     for (int kt = 0; kt < ktiles; ++kt) {
-      const int cur = kt & 1;
-      __syncthreads();  // stage `cur` landed; everyone is done with stage cur^1
-      const bool more = kt + 1 < ktiles;
-      if (more) {
-        load_a(cur ^ 1, (int64_t)(kt + 1) * BK);
-        if constexpr (INT4) fetch_b4((int64_t)(kt + 1) * BK);
-        else load_b8(cur ^ 1, (int64_t)(kt + 1) * BK);
-      }
-      const int8_t* As = smA + cur * A_BYTES;
-      const int8_t* Bs = smB + cur * B_BYTES;
+      const int stage_next = stage + 1 == STAGES ? 0 : stage + 1;
 #pragma unroll
-      for (int kk = 0; kk < BK / 32; ++kk) {
-        v4i af[FM], bf[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int r = wm * WTM + i * 32 + (lane & 31);
-          const int c = kk * 2 + (lane >> 5);
-          af[i] = *(const LDS_PTR(v4i))(As + r * BK + ((c ^ swz_a<BK>(r)) << 4));
+      for (int kk = 0; kk < KK; ++kk) {
+        const int cur_f = kk & 1, nxt_f = cur_f ^ 1;
+        if (kk + 1 < KK) {
+          load_frags(stage, kk + 1, af[nxt_f], bf[nxt_f]);
+        } else {
+          if constexpr (INT4) {
+            // int4 weights fetched on entering this stage, for the stage
+            // STAGES-1 ahead, go to LDS before the next fetch reuses b4reg
+            if (kt + STAGES - 1 < ktiles) store_b4(stage == 0 ? STAGES - 1 : stage - 1);
+          }
+          if (kt + 1 < ktiles) {
+            enter_stage(kt + 1);
+            load_frags(stage_next, 0, af[nxt_f], bf[nxt_f]);
+          } else if (has_next) {
+            // last stage: every wave has its fragments; start the next tile's
+            // copies now so that they land while this tile's epilogue runs
+            lds_barrier();
+            set_sources(nxt);
+            prologue();
+          }
         }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int r = kk * 32 + (lane >> 5) * 16 + ((lane & 15) >> 1);
-          const int col = wn * WTN + j * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-          const int8_t* a0 = Bs + r * BN + (((col >> 4) ^ swz_b(r)) << 4) + (col & 15);
-          // rows r and r+8 share the same swizzle (r & 7)
-          const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0));
-          const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0 + 8 * BN));
-          bf[j] = v4i{lo.x, lo.y, hi.x, hi.y};
-        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur_f][i], bf[cur_f][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (INT4) {
-        if (more) store_b4(cur ^ 1);
-      }
+      stage = stage_next;
     }
+    if (has_next) store_rows(pb ^ 1);  // visible to all waves after the next tile's first barrier
 
-    // ---- epilogue: lane holds rows (r/4)*8 + (lane/32)*4 + r%4, column lane%32
+    // ---- epilogue.  Lane holds column lane%32 and rows (r/4)*8 + (lane/32)*4 + r%4
+    // of each 32x32 block; four consecutive registers are four consecutive rows.
+    // The tile coordinates pass through an opaque point here so that no
+    // epilogue address is computed (and kept live, or spilled) across the
+    // mainloop.
+    int64_t e_row0 = cur.row0, e_col0 = cur.col0;
+    int e_valid = cur.valid_rows, e_g = cur.g;
+    asm volatile("" : "+s"(e_row0), "+s"(e_col0), "+s"(e_valid), "+s"(e_g));
+    const bool dump = p.acc_out != nullptr;
+    // full tiles (all rows in the group, all columns < n) take the unguarded path
+    const bool full = e_valid == BM && e_col0 + BN <= n;
+    const int64_t lane_col = e_col0 + wn * WTN + (lane & 31);
+    const float* rp_pts = s_pts[pb];
+    const float* rp_logit = s_logit[pb];
+    const int32_t* rp_dest = s_dest[pb];
+    float scv[FN];
+    bool col_ok[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int lc = wn * WTN + j * 32 + (lane & 31);
-      const int64_t col = col0 + lc;
-      const bool col_ok = col < n;
-      float s = 1.0f;
-      if (p.scale && col_ok)
-        s = p.scale_bf16 ? bf16_to_f32(((const uint16_t*)p.scale)[(int64_t)g * n + col])
-                         : ((const float*)p.scale)[(int64_t)g * n + col];
+      const int64_t col = lane_col + j * 32;
+      col_ok[j] = col < n;
+      scv[j] = 1.0f;
+      if (p.scale && col_ok[j])
+        scv[j] = p.scale_bf16 ? bf16_to_f32(((const uint16_t*)p.scale)[(int64_t)e_g * n + col])
+                              : ((const float*)p.scale)[(int64_t)e_g * n + col];
+    }
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int lr = wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const int64_t row = row0 + lr;
-          if (!col_ok || row >= row_end) continue;
-          int32_t a = acc[i][j][r];
-          if constexpr (INT4) a >>= 4;  // weights were staged as 16 * w
-          if (p.acc_out) p.acc_out[row * n + col] = a;
-          float v = (float)a;           // v_cvt_f32_i32: round to nearest even
-          v = v * s;
-          v = v * s_pts[lr];
-          v = v * s_logit[lr];
-          if (p.combine == kCombineOrdered) {
-            p.y[row * n + col] = v;
+      for (int q = 0; q < 4; ++q) {
+        const int lr0 = wm * WTM + i * 32 + q * 8 + (lane >> 5) * 4;
+        const float4 P4 = *(const float4*)(rp_pts + lr0);
+        const float4 L4 = *(const float4*)(rp_logit + lr0);
+        int4 D4 = make_int4(-1, -1, -1, -1);
+        if constexpr (COMBINE == kCombineAtomic) D4 = *(const int4*)(rp_dest + lr0);
+        const float Pv[4] = {P4.x, P4.y, P4.z, P4.w};
+        const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
+        const int Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int lr = lr0 + u;
+          if (!full && lr >= e_valid) continue;
+          float* base;
+          if constexpr (COMBINE == kCombineOrdered) {
+            base = p.y + (e_row0 + lr) * n + lane_col;
           } else {
-            const int32_t d = s_dest[lr];
-            if (d >= 0) __hip_atomic_fetch_add(p.out + (int64_t)d * n + col, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (Dv[u] < 0) continue;
+            base = p.out + (int64_t)Dv[u] * n + lane_col;
+          }
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            if (!full && !col_ok[j]) continue;
+            int32_t a = acc[i][j][q * 4 + u];
+            if constexpr (INT4) a >>= 4;  // weights were staged as 16 * w
+            if (dump) p.acc_out[(e_row0 + lr) * n + lane_col + j * 32] = a;
+            float v = (float)a;           // v_cvt_f32_i32: round to nearest even
+            v = v * scv[j];
+            v = v * Pv[u];
+            v = v * Lv[u];
+            if constexpr (COMBINE == kCombineOrdered)
+              __builtin_nontemporal_store(v, base + j * 32);
+            else
+              __hip_atomic_fetch_add(base + j * 32, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
       }
     }
-    __syncthreads();  // s_pts / s_logit / s_dest and LDS stages are reused by the next tile
+    if (!has_next) break;
+    t = t_next;
+    cur = nxt;
+    pb ^= 1;
   }
 }
 
@@ -547,21 +770,19 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p, const int32
 // ---------------------------------------------------------------------------
 TileShape tile_shape(TileId id) {
   switch (id) {
-    case kTile256x256: return {256, 256, 64};
     case kTile128x256: return {128, 256, 64};
     case kTile64x256: return {64, 256, 64};
     default: return {32, 256, 64};
   }
 }
 
-int tile_occupancy(TileId id) { return id == kTile256x256 ? 1 : 2; }
+int tile_occupancy(TileId) { return 2; }
 
 const char* tile_kernel_name(TileId id, bool int4) {
   static const char* names[kNumTiles][2] = {
-      {"gmm_kernel<256,256,64,2x2,i8>", "gmm_kernel<256,256,64,2x2,i4>"},
-      {"gmm_kernel<128,256,64,2x2,i8>", "gmm_kernel<128,256,64,2x2,i4>"},
-      {"gmm_kernel<64,256,64,1x4,i8>", "gmm_kernel<64,256,64,1x4,i4>"},
-      {"gmm_kernel<32,256,64,1x4,i8>", "gmm_kernel<32,256,64,1x4,i4>"},
+      {"gmm_kernel<128,256,64,2x2,s3,i8>", "gmm_kernel<128,256,64,2x2,s3,i4>"},
+      {"gmm_kernel<64,256,64,1x4,s3,i8>", "gmm_kernel<64,256,64,1x4,s3,i4>"},
+      {"gmm_kernel<32,256,64,1x4,s3,i8>", "gmm_kernel<32,256,64,1x4,s3,i4>"},
   };
   return names[(int)id][int4 ? 1 : 0];
 }
@@ -585,13 +806,20 @@ OrderedWorkspace ordered_workspace(int64_t m, int64_t n, int64_t output_bs) {
   return w;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int OCC>
+template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC>
 static void launch_gemm(const KParams& kp, bool int4, int grid, hipStream_t s) {
-  if (int4) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, OCC, true>), dim3(grid), dim3(kThreads), 0, s, kp);
-  else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, OCC, false>), dim3(grid), dim3(kThreads), 0, s, kp);
+  const dim3 gd(grid), bd(kThreads);
+  const size_t dyn = ((size_t)(2 * kp.e + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
+  if (kp.combine == kCombineOrdered) {
+    if (int4) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineOrdered>), gd, bd, dyn, s, kp);
+    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineOrdered>), gd, bd, dyn, s, kp);
+  } else {
+    if (int4) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineAtomic>), gd, bd, dyn, s, kp);
+    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineAtomic>), gd, bd, dyn, s, kp);
+  }
 }
 
-int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* stream) {
+int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* stream, void* const* gemm_events) {
   hipStream_t s = (hipStream_t)stream;
   const TileShape ts = tile_shape(plan.tile);
   KParams kp;
@@ -643,12 +871,13 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
     hipLaunchKernelGGL(seed_kernel, dim3(gs > 0 ? gs : 1), dim3(kThreads), 0, s, kp);
   }
   if (a.m > 0 && plan.grid > 0) {
+    if (gemm_events && gemm_events[0]) hipEventRecord((hipEvent_t)gemm_events[0], s);
     switch (plan.tile) {
-      case kTile256x256: launch_gemm<256, 256, 64, 2, 2, 1>(kp, a.int4, plan.grid, s); break;
-      case kTile128x256: launch_gemm<128, 256, 64, 2, 2, 2>(kp, a.int4, plan.grid, s); break;
-      case kTile64x256: launch_gemm<64, 256, 64, 1, 4, 2>(kp, a.int4, plan.grid, s); break;
-      default: launch_gemm<32, 256, 64, 1, 4, 2>(kp, a.int4, plan.grid, s); break;
+      case kTile128x256: launch_gemm<128, 256, 64, 2, 2, 3, 2>(kp, a.int4, plan.grid, s); break;
+      case kTile64x256: launch_gemm<64, 256, 64, 1, 4, 3, 2>(kp, a.int4, plan.grid, s); break;
+      default: launch_gemm<32, 256, 64, 1, 4, 3, 2>(kp, a.int4, plan.grid, s); break;
     }
+    if (gemm_events && gemm_events[1]) hipEventRecord((hipEvent_t)gemm_events[1], s);
   }
   if (plan.combine == kCombineOrdered) {
     const OrderedWorkspace w = ordered_workspace(a.m, a.n, a.output_bs);

@@ -93,7 +93,7 @@ def test_auto_picks_ordered_for_large_problems():
     info = B.PlanInfo()
     assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
     assert info.combine == B.COMBINE["ordered"]
-    assert info.tile_m == 256
+    assert info.tile_m == 128
 
 
 def test_plan_does_not_depend_on_data_and_follows_hint():
