@@ -871,13 +871,19 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
     hipLaunchKernelGGL(seed_kernel, dim3(gs > 0 ? gs : 1), dim3(kThreads), 0, s, kp);
   }
   if (a.m > 0 && plan.grid > 0) {
-    if (gemm_events && gemm_events[0]) hipEventRecord((hipEvent_t)gemm_events[0], s);
+    if (gemm_events && gemm_events[0]) {
+      const hipError_t er = hipEventRecord((hipEvent_t)gemm_events[0], s);
+      if (er != hipSuccess) return (int)er;
+    }
     switch (plan.tile) {
       case kTile128x256: launch_gemm<128, 256, 64, 2, 2, 3, 2>(kp, a.int4, plan.grid, s); break;
       case kTile64x256: launch_gemm<64, 256, 64, 1, 4, 3, 2>(kp, a.int4, plan.grid, s); break;
       default: launch_gemm<32, 256, 64, 1, 4, 3, 2>(kp, a.int4, plan.grid, s); break;
     }
-    if (gemm_events && gemm_events[1]) hipEventRecord((hipEvent_t)gemm_events[1], s);
+    if (gemm_events && gemm_events[1]) {
+      const hipError_t er = hipEventRecord((hipEvent_t)gemm_events[1], s);
+      if (er != hipSuccess) return (int)er;
+    }
   }
   if (plan.combine == kCombineOrdered) {
     const OrderedWorkspace w = ordered_workspace(a.m, a.n, a.output_bs);
