@@ -131,7 +131,10 @@ typedef struct {
   /* tuningConfig: host array; element 0 = expected rows per expert, used only
    * to choose tiles ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2", function
    * description: the first value is the expected token count per expert and
-   * the tiling follows it).  Results never depend on it.  May be NULL.        */
+   * the tiling follows it).  Element 1 (an extension of this library), if
+   * present and non-zero, forces the tile height: 32, 64, 128 or 256; any
+   * other value is rejected (ATTR).  Results never depend on it.  May be
+   * NULL.                                                                     */
   const int64_t* tuning_config;
   int64_t tuning_config_len;
 } gmmfr_args;
@@ -155,7 +158,10 @@ int gmm_finalize_routing_workspace(const gmmfr_args* args, size_t* workspace_byt
 
 /* Stage 2: validate again, then enqueue the computation on `stream`
  * (a hipStream_t; NULL = the null stream).  `workspace` is device memory of
- * at least the stage-1 size (may be NULL when that size is 0).
+ * at least the stage-1 size: 1 KiB of work-queue counters in every mode, plus,
+ * for the ordered combine, m*n*4 bytes of per-row contributions and
+ * (2*outputBS + outputBS+1 + m) int32 of row buckets (256-byte aligned
+ * sections).  Its contents need no initialisation and are not preserved.
  * Returns GMMFR_OK, a validation status, GMMFR_ERR_WORKSPACE, or
  * GMMFR_ERR_HIP when a launch fails. */
 int gmm_finalize_routing(const gmmfr_args* args, void* workspace, size_t workspace_bytes, void* stream);

@@ -77,6 +77,9 @@ int validate(const gmmfr_args* a, Derived* d) {
     return GMMFR_ERR_ATTR;
   if (a->deterministic == 1 && a->combine == GMMFR_COMBINE_ATOMIC) return GMMFR_ERR_ATTR;
   if (a->tuning_config_len < 0 || (a->tuning_config_len > 0 && !a->tuning_config)) return GMMFR_ERR_ATTR;
+  if (a->tuning_config_len > 1 && a->tuning_config[1] != 0 && a->tuning_config[1] != 32 &&
+      a->tuning_config[1] != 64 && a->tuning_config[1] != 128 && a->tuning_config[1] != 256)
+    return GMMFR_ERR_ATTR;
 
   // shapes
   if (a->x1.ndim != 2) return GMMFR_ERR_SHAPE;
@@ -136,8 +139,20 @@ int validate(const gmmfr_args* a, Derived* d) {
 // Tile choice from the expected rows per expert: tuningConfig[0] when given
 // (the operator's tiling hint), else m / e.  Results do not depend on it.
 TileId choose_tile(const gmmfr_args* a, const Derived& d) {
+  if (a->tuning_config_len > 1) {  // explicit tile height
+    switch (a->tuning_config[1]) {
+      case 256: return kTile256x256;
+      case 128: return kTile128x256;
+      case 64: return kTile64x256;
+      case 32: return kTile32x256;
+      default: break;
+    }
+  }
   int64_t expect = (d.m + d.e - 1) / d.e;
   if (a->tuning_config_len > 0 && a->tuning_config[0] > 0) expect = a->tuning_config[0];
+  // One 256-row tile per CU measured slower than two 128-row tiles per CU on
+  // every shape tried (one workgroup cannot hide its own epilogue), so the
+  // 256-row tile is chosen only on request.
   if (expect >= 256) return kTile128x256;
   if (expect >= 64) return kTile64x256;
   return kTile32x256;
@@ -162,7 +177,7 @@ int make_plan(const gmmfr_args* a, const Derived& d, int cu_count, Plan* plan) {
   int64_t grid = std::min(max_tiles, resident);
   if (grid > 8) grid -= grid % 8;  // whole XCD rounds: workgroups are dealt to the 8 XCDs in turn
   plan->grid = d.m > 0 ? (int32_t)grid : 0;
-  plan->workspace_bytes = plan->combine == kCombineOrdered ? ordered_workspace(d.m, d.n, d.output_bs).total : 0;
+  plan->workspace_bytes = workspace_layout(d.m, d.n, d.output_bs, plan->combine == kCombineOrdered).total;
   return GMMFR_OK;
 }
 
@@ -225,13 +240,15 @@ static int run_stage2(const gmmfr_args* args, void* workspace, size_t workspace_
   Derived d;
   int st = validate(args, &d);
   if (st != GMMFR_OK) return st;
-  const int cus = device_cu_count();
-  if (cus <= 0) return GMMFR_ERR_HIP;
   Plan plan;
-  st = make_plan(args, d, cus, &plan);
+  st = make_plan(args, d, 1, &plan);  // workspace size does not depend on the device
   if (st != GMMFR_OK) return st;
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes)) return GMMFR_ERR_WORKSPACE;
   if (plan.workspace_bytes > 0 && !aligned16(workspace)) return GMMFR_ERR_ALIGN;
+  const int cus = device_cu_count();
+  if (cus <= 0) return GMMFR_ERR_HIP;
+  st = make_plan(args, d, cus, &plan);
+  if (st != GMMFR_OK) return st;
   if (log_enabled())
     std::fprintf(stderr, "[gmmfr] m=%lld k=%lld n=%lld e=%lld combine=%s %s grid=%d ws=%zu\n", (long long)d.m,
                  (long long)d.k, (long long)d.n, (long long)d.e, plan.combine == kCombineOrdered ? "ordered" : "atomic",

@@ -12,10 +12,11 @@ enum Combine : int32_t { kCombineAtomic = 1, kCombineOrdered = 2 };
 
 // GEMM tile variants compiled into the library.
 enum TileId : int32_t {
-  kTile128x256 = 0,   // BM=128 BN=256, 2x2 waves of 64x128, 3 stages
-  kTile64x256 = 1,    // BM=64  BN=256, 1x4 waves of 64x64, 3 stages
-  kTile32x256 = 2,    // BM=32  BN=256, 1x4 waves of 32x64, 3 stages
-  kNumTiles = 3
+  kTile256x256 = 0,   // BM=256 BN=256, 2x2 waves of 128x128, 3 stages, 1 workgroup per CU
+  kTile128x256 = 1,   // BM=128 BN=256, 2x2 waves of 64x128, 3 stages
+  kTile64x256 = 2,    // BM=64  BN=256, 1x4 waves of 64x64, 3 stages
+  kTile32x256 = 3,    // BM=32  BN=256, 1x4 waves of 32x64, 3 stages
+  kNumTiles = 4
 };
 
 struct TileShape {
@@ -44,11 +45,13 @@ struct LaunchArgs {
   int64_t bsdp, shared_offset, output_bs;
 };
 
-// Workspace carve-up of the ordered combine (byte offsets, 256-aligned).
-struct OrderedWorkspace {
-  size_t y_off, counts_off, cursor_off, offsets_off, list_off, total;
+// Workspace carve-up (byte offsets, 256-aligned).  Every plan has the control
+// block (GEMM tile-queue counters); the ordered combine adds the rest.
+constexpr size_t kCtrlBytes = 1024;
+struct Workspace {
+  size_t ctrl_off, y_off, counts_off, cursor_off, offsets_off, list_off, total;
 };
-OrderedWorkspace ordered_workspace(int64_t m, int64_t n, int64_t output_bs);
+Workspace workspace_layout(int64_t m, int64_t n, int64_t output_bs, bool ordered);
 
 struct Plan {
   Combine combine;

@@ -48,7 +48,36 @@ struct KParams {
   int32_t e, group_list_type, scale_bf16, row_index_i32;
   int32_t n_tiles_n;
   int32_t combine;
+  int32_t* tile_ctr;    // per-XCD tile queues (kTileQueues counters, 64 bytes apart), zeroed before the GEMM
 };
+
+constexpr int kTileQueues = 8;       // one per XCD
+constexpr int kTileQueueStride = 16; // int32 elements between counters (one 64-byte line each)
+constexpr int kTileBlock = 64;       // consecutive raster tiles handed to one XCD at a time
+
+// XCD (XCC) the calling wave runs on.
+__device__ __forceinline__ int xcc_id() {
+  return (int)(__builtin_amdgcn_s_getreg((20) | (0 << 6) | ((16 - 1) << 11)) & (kTileQueues - 1));
+}
+
+// Tile of the j-th grab from queue q: raster blocks of kTileBlock tiles are
+// dealt to the queues in turn.  -1 once past the last tile.
+__device__ __forceinline__ int queue_tile(int q, int j, int total) {
+  const int64_t t = ((int64_t)(j / kTileBlock) * kTileQueues + q) * kTileBlock + (j % kTileBlock);
+  return t < total ? (int)t : -1;
+}
+
+// One grab from queue q, then from the other queues in turn until a tile is
+// found or all are exhausted (-1).  Stealing only happens at the very end, and
+// makes every tile processed whatever the placement of workgroups on XCDs.
+__device__ int grab_tile_from(int* ctr, int q, int total) {
+  for (int tries = 0; tries < kTileQueues; ++tries) {
+    const int qq = (q + tries) % kTileQueues;
+    const int t = queue_tile(qq, atomicAdd(ctr + qq * kTileQueueStride, 1), total);
+    if (t >= 0) return t;
+  }
+  return -1;
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
@@ -186,6 +215,20 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // not wait for copies in flight (the caller waits for those it needs).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// One accumulator element read where it is used.  With accumulators in AGPRs
+// this keeps the compiler from copying the whole accumulator array to VGPRs
+// at once after the mainloop (which would need every VGPR and spill).
+template <bool FROM_AGPR>
+__device__ __forceinline__ int32_t acc_elem(int32_t x) {
+  if constexpr (FROM_AGPR) {
+    int32_t v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(x));
+    return v;
+  } else {
+    return x;
+  }
+}
+
 // int4 word -> 8 int8 holding 16 * value, in column order (two dwords).
 __device__ __forceinline__ void unpack_int4_x16(uint32_t w, uint32_t& d0, uint32_t& d1) {
   const uint32_t lo = (w << 4) & 0xF0F0F0F0u;  // 16*t0, 16*t2, 16*t4, 16*t6
@@ -296,10 +339,18 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   const int64_t k = p.k, n = p.n;
   const int ktiles = (int)(k / BK);
 
-  // consecutive logical tiles on one XCD (workgroups are dealt round-robin to the 8 XCDs)
-  const int G = gridDim.x;
-  int t = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-  if (t >= total_tiles) return;
+  // Tiles come from per-XCD queues so that the tiles running at the same time
+  // on one XCD are consecutive in raster order and share panels in its L2.
+  __shared__ int s_tiles[2];
+  const int xcd = xcc_id();
+  if (tid == 0) {
+    s_tiles[0] = grab_tile_from(p.tile_ctr, xcd, total_tiles);
+    s_tiles[1] = s_tiles[0] >= 0 ? grab_tile_from(p.tile_ctr, xcd, total_tiles) : -1;
+  }
+  __syncthreads();
+  int t = s_tiles[0];
+  int t1 = s_tiles[1];
+  if (t < 0) return;
 
   auto coord = [&](int tt) { return tile_coord<BM, BN>(p, s_ends, s_tile_pre, tt); };
 
@@ -447,11 +498,11 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     }
   };
 
-  // Entering stage j of the current tile: its copies are complete, every wave
-  // has finished reading stage j-1 (its fragments are in registers), so stage
-  // j+STAGES-1 may overwrite stage j-1's buffer.  Stage 0 of a tile waits for
-  // everything (the previous tile's stores are counted by the same counter).
-  auto enter_stage = [&](int j) {
+  // Entering stage j of the current tile: its copies are complete, and every
+  // wave has finished reading stage j-1 (its fragments are in registers).
+  // Stage 0 of a tile waits for everything (the previous tile's stores are
+  // counted by the same counter).
+  auto sync_stage = [&](int j) {
     if (j > 0 && j + STAGES - 2 < ktiles) {
       if (a_full) wait_vmcnt<(STAGES - 2) * LOADS_FULL>();
       else wait_vmcnt<(STAGES - 2) * LOADS_SHORT>();
@@ -459,6 +510,9 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       wait_vmcnt<0>();
     }
     lds_barrier();
+  };
+  // After sync_stage(j): stage j+STAGES-1 may overwrite stage j-1's buffer.
+  auto refill = [&](int j) {
     if (j + STAGES - 1 < ktiles) issue_stage((j + STAGES - 1) % STAGES, j + STAGES - 1);
   };
 
@@ -472,10 +526,11 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   store_rows(pb);
 
   while (true) {
-    const int t_next = t + G;
-    const bool has_next = t_next < total_tiles;
+    // the tile after this one (t1) is known; the one after that is grabbed
+    // now and read at the last stage, where all copies have landed anyway
+    const bool has_next = t1 >= 0;
     TileCoord nxt = cur;
-    if (has_next) nxt = coord(t_next);
+    if (has_next) nxt = coord(t1);
 
     v16i acc[FM][FN];
 #pragma unroll
@@ -483,8 +538,11 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = v16i{0};
 
-    enter_stage(0);
-    // the next tile's row factors go to the other buffer while this one runs
+    sync_stage(0);
+    refill(0);
+    int pending = -1;
+    if (tid == 0 && has_next) pending = atomicAdd(p.tile_ctr + xcd * kTileQueueStride, 1);
+    // the next tile's row factors go to the other buffer at the last stage
     if (has_next) fetch_rows(nxt);
     v4i af[2][FM], bf[2][FN];
     load_frags(0, 0, af[0], bf[0]);
@@ -504,14 +562,27 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
             if (kt + STAGES - 1 < ktiles) store_b4(stage == 0 ? STAGES - 1 : stage - 1);
           }
           if (kt + 1 < ktiles) {
-            enter_stage(kt + 1);
+            sync_stage(kt + 1);
+            refill(kt + 1);
             load_frags(stage_next, 0, af[nxt_f], bf[nxt_f]);
-          } else if (has_next) {
-            // last stage: every wave has its fragments; start the next tile's
-            // copies now so that they land while this tile's epilogue runs
-            lds_barrier();
-            set_sources(nxt);
-            prologue();
+          } else {
+            // last stage: every copy of this tile has landed (wait_vmcnt<0>
+            // below covers the row loads and the queue grab too)
+            wait_vmcnt<0>();
+            if (has_next) store_rows(pb ^ 1);
+            if (tid == 0) {
+              int t2 = -1;
+              if (has_next) {
+                t2 = queue_tile(xcd, pending, total_tiles);
+                if (t2 < 0) t2 = grab_tile_from(p.tile_ctr, xcd, total_tiles);
+              }
+              s_tiles[pb] = t2;
+            }
+            lds_barrier();  // every wave has its fragments; the next tile's copies may start
+            if (has_next) {
+              set_sources(nxt);
+              prologue();
+            }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -524,7 +595,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       }
       stage = stage_next;
     }
-    if (has_next) store_rows(pb ^ 1);  // visible to all waves after the next tile's first barrier
+    const int t2 = s_tiles[pb];
 
     // ---- epilogue.  Lane holds column lane%32 and rows (r/4)*8 + (lane/32)*4 + r%4
     // of each 32x32 block; four consecutive registers are four consecutive rows.
@@ -578,7 +649,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
             if (!full && !col_ok[j]) continue;
-            int32_t a = acc[i][j][q * 4 + u];
+            int32_t a = acc_elem<(FM * FN * 16 > 128)>(acc[i][j][q * 4 + u]);
             if constexpr (INT4) a >>= 4;  // weights were staged as 16 * w
             if (dump) p.acc_out[(e_row0 + lr) * n + lane_col + j * 32] = a;
             float v = (float)a;           // v_cvt_f32_i32: round to nearest even
@@ -594,7 +665,8 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       }
     }
     if (!has_next) break;
-    t = t_next;
+    t = t1;
+    t1 = t2;
     cur = nxt;
     pb ^= 1;
   }
@@ -618,6 +690,7 @@ __device__ __forceinline__ float4 seed4(const KParams& p, int64_t d, int64_t j4)
 }
 
 __global__ __launch_bounds__(kThreads) void seed_kernel(KParams p) {
+  if (blockIdx.x == 0 && threadIdx.x < (int)(kCtrlBytes / 4)) p.tile_ctr[threadIdx.x] = 0;
   const int64_t n4 = p.n / 4, total = p.output_bs * n4;
   for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * kThreads) {
     const int64_t d = idx / n4, j4 = idx % n4;
@@ -650,8 +723,10 @@ __device__ int64_t block_covered_rows(const KParams& p, int64_t* s_red) {
   return c;
 }
 
-__global__ __launch_bounds__(kThreads) void fill_i32_kernel(int32_t* ptr, int64_t count, int32_t value) {
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < count; i += (int64_t)gridDim.x * kThreads) ptr[i] = value;
+// Zero the bucket counts and the GEMM's tile-queue counters.
+__global__ __launch_bounds__(kThreads) void zero_counts_kernel(int32_t* counts, int64_t count, int32_t* ctrl) {
+  if (blockIdx.x == 0 && threadIdx.x < (int)(kCtrlBytes / 4)) ctrl[threadIdx.x] = 0;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < count; i += (int64_t)gridDim.x * kThreads) counts[i] = 0;
 }
 
 __global__ __launch_bounds__(kThreads) void hist_kernel(KParams p, int32_t* counts) {
@@ -770,16 +845,18 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p, const int32
 // ---------------------------------------------------------------------------
 TileShape tile_shape(TileId id) {
   switch (id) {
+    case kTile256x256: return {256, 256, 64};
     case kTile128x256: return {128, 256, 64};
     case kTile64x256: return {64, 256, 64};
     default: return {32, 256, 64};
   }
 }
 
-int tile_occupancy(TileId) { return 2; }
+int tile_occupancy(TileId id) { return id == kTile256x256 ? 1 : 2; }
 
 const char* tile_kernel_name(TileId id, bool int4) {
   static const char* names[kNumTiles][2] = {
+      {"gmm_kernel<256,256,64,2x2,s3,i8>", "gmm_kernel<256,256,64,2x2,s3,i4>"},
       {"gmm_kernel<128,256,64,2x2,s3,i8>", "gmm_kernel<128,256,64,2x2,s3,i4>"},
       {"gmm_kernel<64,256,64,1x4,s3,i8>", "gmm_kernel<64,256,64,1x4,s3,i4>"},
       {"gmm_kernel<32,256,64,1x4,s3,i8>", "gmm_kernel<32,256,64,1x4,s3,i4>"},
@@ -789,19 +866,23 @@ const char* tile_kernel_name(TileId id, bool int4) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-OrderedWorkspace ordered_workspace(int64_t m, int64_t n, int64_t output_bs) {
-  OrderedWorkspace w;
+Workspace workspace_layout(int64_t m, int64_t n, int64_t output_bs, bool ordered) {
+  Workspace w{};
   size_t off = 0;
-  w.y_off = off;
-  off += align256((size_t)m * (size_t)n * sizeof(float));
-  w.counts_off = off;
-  off += align256((size_t)output_bs * 4);
-  w.cursor_off = off;
-  off += align256((size_t)output_bs * 4);
-  w.offsets_off = off;
-  off += align256((size_t)(output_bs + 1) * 4);
-  w.list_off = off;
-  off += align256((size_t)(m > 0 ? m : 1) * 4);
+  w.ctrl_off = off;
+  off += kCtrlBytes;
+  if (ordered) {
+    w.y_off = off;
+    off += align256((size_t)m * (size_t)n * sizeof(float));
+    w.counts_off = off;
+    off += align256((size_t)output_bs * 4);
+    w.cursor_off = off;
+    off += align256((size_t)output_bs * 4);
+    w.offsets_off = off;
+    off += align256((size_t)(output_bs + 1) * 4);
+    w.list_off = off;
+    off += align256((size_t)(m > 0 ? m : 1) * 4);
+  }
   w.total = off;
   return w;
 }
@@ -846,18 +927,19 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
   kp.row_index_i32 = a.row_index_i32;
   kp.n_tiles_n = (int32_t)((a.n + ts.bn - 1) / ts.bn);
   kp.combine = plan.combine;
+  const Workspace w = workspace_layout(a.m, a.n, a.output_bs, plan.combine == kCombineOrdered);
+  char* ws = (char*)workspace;
+  kp.tile_ctr = (int32_t*)(ws + w.ctrl_off);
 
   const int64_t n4 = a.n / 4;
   if (plan.combine == kCombineOrdered) {
-    const OrderedWorkspace w = ordered_workspace(a.m, a.n, a.output_bs);
-    char* ws = (char*)workspace;
     kp.y = (float*)(ws + w.y_off);
     int32_t* counts = (int32_t*)(ws + w.counts_off);
     int32_t* cursor = (int32_t*)(ws + w.cursor_off);
     int32_t* offsets = (int32_t*)(ws + w.offsets_off);
     int32_t* list = (int32_t*)(ws + w.list_off);
     const int gb = (int)std::min<int64_t>(1024, (a.output_bs + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(gb), dim3(kThreads), 0, s, counts, a.output_bs, 0);
+    hipLaunchKernelGGL(zero_counts_kernel, dim3(gb), dim3(kThreads), 0, s, counts, a.output_bs, kp.tile_ctr);
     if (a.m > 0) {
       const int gm = (int)std::min<int64_t>(2048, (a.m + kThreads - 1) / kThreads);
       hipLaunchKernelGGL(hist_kernel, dim3(gm), dim3(kThreads), 0, s, kp, counts);
@@ -876,6 +958,7 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
       if (er != hipSuccess) return (int)er;
     }
     switch (plan.tile) {
+      case kTile256x256: launch_gemm<256, 256, 64, 2, 2, 3, 1>(kp, a.int4, plan.grid, s); break;
       case kTile128x256: launch_gemm<128, 256, 64, 2, 2, 3, 2>(kp, a.int4, plan.grid, s); break;
       case kTile64x256: launch_gemm<64, 256, 64, 1, 4, 3, 2>(kp, a.int4, plan.grid, s); break;
       default: launch_gemm<32, 256, 64, 1, 4, 3, 2>(kp, a.int4, plan.grid, s); break;
@@ -886,8 +969,6 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
     }
   }
   if (plan.combine == kCombineOrdered) {
-    const OrderedWorkspace w = ordered_workspace(a.m, a.n, a.output_bs);
-    char* ws = (char*)workspace;
     const int gr = (int)std::min<int64_t>(65535, a.output_bs);
     hipLaunchKernelGGL(reduce_kernel, dim3(gr > 0 ? gr : 1), dim3(kThreads), 0, s, kp,
                        (const int32_t*)(ws + w.offsets_off), (const int32_t*)(ws + w.list_off));

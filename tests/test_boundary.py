@@ -71,10 +71,10 @@ def _ws(a):
     return st, n.value
 
 
-def test_valid_atomic_needs_no_workspace():
+def test_atomic_workspace_is_the_control_block():
     a = _args(m=32, k=256, n=256, e=4, obs=16)
     a.combine = B.COMBINE["atomic"]
-    assert _ws(a) == (B.OK, 0)
+    assert _ws(a) == (B.OK, 1024)
 
 
 def test_ordered_workspace_formula():
@@ -84,7 +84,7 @@ def test_ordered_workspace_formula():
 
     def al(x):
         return (x + 255) // 256 * 256
-    want = al(m * n * 4) + al(obs * 4) * 2 + al((obs + 1) * 4) + al(m * 4)
+    want = 1024 + al(m * n * 4) + al(obs * 4) * 2 + al((obs + 1) * 4) + al(m * 4)
     assert _ws(a) == (B.OK, want)
 
 
@@ -106,6 +106,15 @@ def test_plan_does_not_depend_on_data_and_follows_hint():
     a.tuning_config_len = 1
     B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info))
     assert info.tile_m == 32 and base != 32
+    for forced in (256, 128, 64, 32):
+        hint2 = (ctypes.c_int64 * 2)(0, forced)
+        a.tuning_config = ctypes.cast(hint2, ctypes.POINTER(ctypes.c_int64))
+        a.tuning_config_len = 2
+        assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
+        assert info.tile_m == forced
+    hint2 = (ctypes.c_int64 * 2)(0, 96)
+    a.tuning_config = ctypes.cast(hint2, ctypes.POINTER(ctypes.c_int64))
+    assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.ERR_ATTR
 
 
 CASES = [
@@ -172,6 +181,13 @@ def test_status_strings():
     for code in range(9):
         assert B.lib().gmmfr_status_string(code)
     assert B.lib().gmmfr_status_string(99) == b"unknown status"
+
+
+def test_stage_two_requires_the_workspace():
+    a = _args()
+    a.combine = B.COMBINE["atomic"]
+    assert B.lib().gmm_finalize_routing(ctypes.byref(a), None, 0, None) == B.ERR_WORKSPACE
+    assert B.lib().gmm_finalize_routing(ctypes.byref(a), ctypes.c_void_p(0x100000), 1023, None) == B.ERR_WORKSPACE
 
 
 def test_stage_two_rejects_before_any_launch():

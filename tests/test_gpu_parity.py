@@ -27,7 +27,7 @@ def _check_full(p, *, hints=(None,), modes=("ordered", "atomic")):
     cov = G.covered_mask(p)
     d = G.to_device(p)
     for hint in hints:
-        tc = None if hint is None else [hint]
+        tc = None if hint is None else list(hint) if isinstance(hint, tuple) else [hint]
         for mode in modes:
             det = mode == "ordered"
             out, acc = G.run_gpu(p, d, deterministic=det, combine="auto" if det else "atomic", want_acc=True,
@@ -83,7 +83,7 @@ CASES = {
 @pytest.mark.parametrize("name", list(CASES), ids=list(CASES))
 def test_random_case_all_elements(name):
     p = W.random_problem(**CASES[name])
-    _check_full(p, hints=(None, 8, 100, 300, 5000))
+    _check_full(p, hints=(None, 8, 100, 300, (0, 256)))  # every tile variant
 
 
 def test_zero_rows_gives_seed():
@@ -206,7 +206,7 @@ def test_ordered_mode_is_run_to_run_identical():
     p = W.make_config("decode", 1)
     d = G.to_device(p)
     a, _ = G.run_gpu(p, d, deterministic=True)
-    b, _ = G.run_gpu(p, d, deterministic=True, tuning_config=[5000])
+    b, _ = G.run_gpu(p, d, deterministic=True, tuning_config=[0, 256])
     c, _ = G.run_gpu(p, d, deterministic=True, tuning_config=[8])
     a = a.cpu().numpy()
     G.assert_bitexact(b.cpu().numpy(), a)
