@@ -327,6 +327,8 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   __shared__ __attribute__((aligned(16))) float s_pts[2][BM];
   __shared__ __attribute__((aligned(16))) float s_logit[2][BM];
   __shared__ __attribute__((aligned(16))) int32_t s_dest[2][BM];
+  // per-column dequantisation scale of a tile, double-buffered the same way
+  __shared__ __attribute__((aligned(16))) float s_scale[2][BN];
 
   build_group_table(p, BM, s_ends, s_tile_pre, s_scan);
   const int total_tiles = s_tile_pre[p.e];
@@ -456,11 +458,12 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     }
   };
   // per-row factors of a tile into buffer `pb`: loads first, LDS writes later
-  float fp_pts = 1.0f, fp_logit = 1.0f;
+  float fp_pts = 1.0f, fp_logit = 1.0f, fp_scale = 1.0f;
   int32_t fp_dest = -1;
   auto fetch_rows = [&](const TileCoord& c) {
     fp_pts = 1.0f;
     fp_logit = 1.0f;
+    fp_scale = 1.0f;
     fp_dest = -1;
     if (tid < BM && tid < c.valid_rows) {
       const int64_t row = c.row0 + tid;
@@ -468,6 +471,10 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       if (p.logit) fp_logit = p.logit[row];
       fp_dest = (int32_t)dest_row(p, row);
     }
+    const int64_t col = c.col0 + tid;
+    if (tid < BN && p.scale && col < n)
+      fp_scale = p.scale_bf16 ? bf16_to_f32(((const uint16_t*)p.scale)[(int64_t)c.g * n + col])
+                              : ((const float*)p.scale)[(int64_t)c.g * n + col];
   };
   auto store_rows = [&](int pb) {
     if (tid < BM) {
@@ -475,8 +482,9 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       s_logit[pb][tid] = fp_logit;
       s_dest[pb][tid] = fp_dest;
     }
+    if (tid < BN) s_scale[pb][tid] = fp_scale;
   };
-  static_assert(BM <= kThreads, "one thread per tile row");
+  static_assert(BM <= kThreads && BN <= kThreads, "one thread per tile row and per tile column");
 
   auto load_frags = [&](int sc, int kk, v4i (&af)[FM], v4i (&bf)[FN]) {
     const int8_t* As = sA + sc * A_BYTES;
@@ -603,63 +611,105 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     // epilogue address is computed (and kept live, or spilled) across the
     // mainloop.
     int64_t e_row0 = cur.row0, e_col0 = cur.col0;
-    int e_valid = cur.valid_rows, e_g = cur.g;
-    asm volatile("" : "+s"(e_row0), "+s"(e_col0), "+s"(e_valid), "+s"(e_g));
+    int e_valid = cur.valid_rows;
+    asm volatile("" : "+s"(e_row0), "+s"(e_col0), "+s"(e_valid));
     const bool dump = p.acc_out != nullptr;
-    // full tiles (all rows in the group, all columns < n) take the unguarded path
-    const bool full = e_valid == BM && e_col0 + BN <= n;
-    const int64_t lane_col = e_col0 + wn * WTN + (lane & 31);
     const float* rp_pts = s_pts[pb];
     const float* rp_logit = s_logit[pb];
     const int32_t* rp_dest = s_dest[pb];
     float scv[FN];
-    bool col_ok[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t col = lane_col + j * 32;
-      col_ok[j] = col < n;
-      scv[j] = 1.0f;
-      if (p.scale && col_ok[j])
-        scv[j] = p.scale_bf16 ? bf16_to_f32(((const uint16_t*)p.scale)[(int64_t)e_g * n + col])
-                              : ((const float*)p.scale)[(int64_t)e_g * n + col];
-    }
+    for (int j = 0; j < FN; ++j) scv[j] = s_scale[pb][wn * WTN + j * 32 + (lane & 31)];
+    // One element: int32 -> fp32 (round to nearest even), then the three
+    // factors in the oracle's order.
+    auto value = [&](int i, int j, int r, float pv, float lv) {
+      int32_t a = acc_elem<(FM * FN * 16 > 128)>(acc[i][j][r]);
+      if constexpr (INT4) a >>= 4;  // weights were staged as 16 * w
+      float v = (float)a;
+      v = v * scv[j];
+      v = v * pv;
+      v = v * lv;
+      return v;
+    };
+    if (e_valid == BM && e_col0 + BN <= n && n < (int64_t(1) << 28) && !dump) {
+      // Full tile: no per-element guards.  Ordered stores use one wave-uniform
+      // row base and one 32-bit lane offset for every store.
+      const uint32_t lane_off = (uint32_t)((lane >> 5) * 4 * n + (lane & 31));
+      float* wave_y = p.y + (e_row0 + wm * WTM) * n + e_col0 + wn * WTN;
+      float* wave_out = p.out + e_col0 + wn * WTN + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int lr0 = wm * WTM + i * 32 + q * 8 + (lane >> 5) * 4;
-        const float4 P4 = *(const float4*)(rp_pts + lr0);
-        const float4 L4 = *(const float4*)(rp_logit + lr0);
-        int4 D4 = make_int4(-1, -1, -1, -1);
-        if constexpr (COMBINE == kCombineAtomic) D4 = *(const int4*)(rp_dest + lr0);
-        const float Pv[4] = {P4.x, P4.y, P4.z, P4.w};
-        const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
-        const int Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+        for (int q = 0; q < 4; ++q) {
+          const int lr0 = wm * WTM + i * 32 + q * 8 + (lane >> 5) * 4;
+          const float4 P4 = *(const float4*)(rp_pts + lr0);
+          const float4 L4 = *(const float4*)(rp_logit + lr0);
+          int4 D4 = make_int4(-1, -1, -1, -1);
+          if constexpr (COMBINE == kCombineAtomic) D4 = *(const int4*)(rp_dest + lr0);
+          const float Pv[4] = {P4.x, P4.y, P4.z, P4.w};
+          const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
+          const int Dv[4] = {D4.x, D4.y, D4.z, D4.w};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int lr = lr0 + u;
-          if (!full && lr >= e_valid) continue;
-          float* base;
-          if constexpr (COMBINE == kCombineOrdered) {
-            base = p.y + (e_row0 + lr) * n + lane_col;
-          } else {
-            if (Dv[u] < 0) continue;
-            base = p.out + (int64_t)Dv[u] * n + lane_col;
+          for (int u = 0; u < 4; ++u) {
+            if constexpr (COMBINE == kCombineOrdered) {
+              float* rowp = wave_y + (int64_t)(i * 32 + q * 8 + u) * n;
+#pragma unroll
+              for (int j = 0; j < FN; ++j)
+                __builtin_nontemporal_store(value(i, j, q * 4 + u, Pv[u], Lv[u]), (rowp + j * 32) + lane_off);
+            } else {
+              if (Dv[u] < 0) continue;
+              float* base = wave_out + (int64_t)Dv[u] * n;
+#pragma unroll
+              for (int j = 0; j < FN; ++j)
+                __hip_atomic_fetch_add(base + j * 32, value(i, j, q * 4 + u, Pv[u], Lv[u]), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
           }
+        }
+      }
+    } else {
+      // Partial tile (group tail or n tail) or accumulator dump: guarded.
+      const int64_t lane_col = e_col0 + wn * WTN + (lane & 31);
+      bool col_ok[FN];
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            if (!full && !col_ok[j]) continue;
-            int32_t a = acc_elem<(FM * FN * 16 > 128)>(acc[i][j][q * 4 + u]);
-            if constexpr (INT4) a >>= 4;  // weights were staged as 16 * w
-            if (dump) p.acc_out[(e_row0 + lr) * n + lane_col + j * 32] = a;
-            float v = (float)a;           // v_cvt_f32_i32: round to nearest even
-            v = v * scv[j];
-            v = v * Pv[u];
-            v = v * Lv[u];
-            if constexpr (COMBINE == kCombineOrdered)
-              __builtin_nontemporal_store(v, base + j * 32);
-            else
-              __hip_atomic_fetch_add(base + j * 32, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int j = 0; j < FN; ++j) col_ok[j] = lane_col + j * 32 < n;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int lr0 = wm * WTM + i * 32 + q * 8 + (lane >> 5) * 4;
+          const float4 P4 = *(const float4*)(rp_pts + lr0);
+          const float4 L4 = *(const float4*)(rp_logit + lr0);
+          int4 D4 = make_int4(-1, -1, -1, -1);
+          if constexpr (COMBINE == kCombineAtomic) D4 = *(const int4*)(rp_dest + lr0);
+          const float Pv[4] = {P4.x, P4.y, P4.z, P4.w};
+          const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
+          const int Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int lr = lr0 + u;
+            if (lr >= e_valid) continue;
+            float* base;
+            if constexpr (COMBINE == kCombineOrdered) {
+              base = p.y + (e_row0 + lr) * n + lane_col;
+            } else {
+              if (Dv[u] < 0) continue;
+              base = p.out + (int64_t)Dv[u] * n + lane_col;
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              if (!col_ok[j]) continue;
+              if (dump) {
+                int32_t a = acc_elem<(FM * FN * 16 > 128)>(acc[i][j][q * 4 + u]);
+                if constexpr (INT4) a >>= 4;
+                p.acc_out[(e_row0 + lr) * n + lane_col + j * 32] = a;
+              }
+              const float v = value(i, j, q * 4 + u, Pv[u], Lv[u]);
+              if constexpr (COMBINE == kCombineOrdered)
+                __builtin_nontemporal_store(v, base + j * 32);
+              else
+                __hip_atomic_fetch_add(base + j * 32, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
           }
         }
       }
