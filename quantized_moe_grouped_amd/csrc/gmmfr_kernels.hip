@@ -172,13 +172,16 @@ __device__ __forceinline__ int find_group(const int32_t* s_tile_pre, int e, int 
 //   A stage: [BM][BK] bytes, k-contiguous; 16-byte chunk c of row r is stored
 //            at chunk position c ^ swz_a(r).  Read with ds_read_b128.
 //   B stage: [BK][BN] bytes, n-contiguous (the weight's own layout); chunk c
-//            of k-row r is stored at position c ^ (r & 7).  Read with the
-//            gfx950 transpose load ds_read_b64_tr_b8: within each 16-lane
+//            of k-row r is stored at position c ^ (2 * (r & 7)).  Read with
+//            the gfx950 transpose load ds_read_b64_tr_b8: within each 16-lane
 //            group, lane 16G+i receives byte (i % 8) of the eight 8-byte rows
 //            addressed by lanes 16G + 2b + i/8 (b = 0..7).  Lane s therefore
 //            supplies k-row (s%16)/2 at column 16*((s/16)%2) + 8*(s%2) and
 //            gets eight consecutive k of column s%32; two such loads give the
-//            16 k-values the i8 MFMA expects per lane.
+//            16 k-values the i8 MFMA expects per lane.  The 32 lanes of one
+//            pass touch 8 k-rows x 2 adjacent chunks; the even swizzle sends
+//            them to 16 distinct chunk positions (all 64 banks), where r & 7
+//            alone would fold the pair onto 8 positions (2-way conflicts).
 // Both stages are filled by global_load_lds_dwordx4 (HBM -> LDS without
 // VGPRs); a lane's LDS slot is fixed, so the swizzle is applied by choosing
 // which global chunk each lane fetches.
@@ -188,7 +191,7 @@ __device__ __forceinline__ int swz_a(int r) {
   if constexpr (BK == 64) return ((r >> 1) ^ (r >> 3)) & 3;
   else return (r ^ (r >> 3)) & 7;
 }
-__device__ __forceinline__ int swz_b(int r) { return r & 7; }
+__device__ __forceinline__ int swz_b(int r) { return (r & 7) << 1; }
 
 // HBM -> LDS copy of 16 bytes per lane: lane i of the wave writes LDS bytes
 // [lds_base + 16 i, lds_base + 16 i + 16).  lds_base must be wave-uniform.
@@ -213,7 +216,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // Workgroup barrier that publishes LDS written by ds_write (lgkmcnt) but does
 // not wait for copies in flight (the caller waits for those it needs).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void lds_barrier() {
+  // the compiler's own waitcnt tracking sees this lgkmcnt(0); the empty asm
+  // statements keep memory accesses from moving across the barrier
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // One accumulator element read where it is used.  With accumulators in AGPRs
 // this keeps the compiler from copying the whole accumulator array to VGPRs
@@ -309,7 +319,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   constexpr int LOADS_SHORT = A_INSTR - 1 + B_ISSUED;
   static_assert(WAVES_M * WAVES_N == NWAVES, "4 waves");
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-  static_assert(BN >= 128, "B swizzle needs 8 chunks per row");
+  static_assert(BN >= 256, "B swizzle needs 16 chunks per row");
   static_assert(A_SLOTS % 64 == 0 && B_SLOTS % 64 == 0, "whole waves per copy");
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
   static_assert((STAGES - 2) * LOADS_FULL < 64, "vmcnt range");
@@ -486,24 +496,75 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   };
   static_assert(BM <= kThreads && BN <= kThreads, "one thread per tile row and per tile column");
 
+  // Fragment reads.  Read item r of a k-substep: A fragments first, then B.
+  auto read_a = [&](int sc, int kk, int i, v4i& dst) {
+    const int r = wm * WTM + i * 32 + (lane & 31);
+    const int c = kk * 2 + (lane >> 5);
+    dst = *(const LDS_PTR(v4i))(sA + sc * A_BYTES + r * BK + ((c ^ swz_a<BK>(r)) << 4));
+  };
+  auto read_b = [&](int sc, int kk, int j, v4i& dst) {
+    const int r = kk * 32 + (lane >> 5) * 16 + ((lane & 15) >> 1);
+    const int col = wn * WTN + j * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+    const int8_t* a0 = sB + sc * B_BYTES + r * BN + (((col >> 4) ^ swz_b(r)) << 4) + (col & 15);
+    const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0));
+    const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0 + 8 * BN));  // same swizzle
+    dst = v4i{lo.x, lo.y, hi.x, hi.y};
+  };
   auto load_frags = [&](int sc, int kk, v4i (&af)[FM], v4i (&bf)[FN]) {
-    const int8_t* As = sA + sc * A_BYTES;
-    const int8_t* Bs = sB + sc * B_BYTES;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int r = wm * WTM + i * 32 + (lane & 31);
-      const int c = kk * 2 + (lane >> 5);
-      af[i] = *(const LDS_PTR(v4i))(As + r * BK + ((c ^ swz_a<BK>(r)) << 4));
-    }
+    for (int i = 0; i < FM; ++i) read_a(sc, kk, i, af[i]);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int r = kk * 32 + (lane >> 5) * 16 + ((lane & 15) >> 1);
-      const int col = wn * WTN + j * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-      const int8_t* a0 = Bs + r * BN + (((col >> 4) ^ swz_b(r)) << 4) + (col & 15);
-      const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0));
-      const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0 + 8 * BN));  // same swizzle
-      bf[j] = v4i{lo.x, lo.y, hi.x, hi.y};
+    for (int j = 0; j < FN; ++j) read_b(sc, kk, j, bf[j]);
+  };
+  // Copy items of one stage refill: the A copies, then the B copies (int8
+  // weights) -- int4 weights take one register-load item first instead.
+  constexpr int N_COPY = INT4 ? A_INSTR + 1 : A_INSTR + B_INSTR;
+  auto copy_item = [&](auto d_, int sc, int kt) {
+    constexpr int d = decltype(d_)::value;
+    if constexpr (INT4) {
+      if constexpr (d == 0) {
+        fetch_b4(kt);
+      } else {
+        constexpr int q = d - 1;
+        constexpr int slot_base = (q * NWAVES) * 64;
+        const int sb = slot_base + wave * 64;
+        if ((A_SLOTS % (NWAVES * 64)) == 0 || sb < A_SLOTS)
+          lds_dma16_sv(a_base + (int64_t)kt * BK, a_off[q],
+                       __builtin_amdgcn_readfirstlane(lds_addr(sA + sc * A_BYTES + sb * 16)));
+      }
+    } else if constexpr (d < A_INSTR) {
+      const int sb = (d * NWAVES + wave) * 64;
+      if ((A_SLOTS % (NWAVES * 64)) == 0 || sb < A_SLOTS)
+        lds_dma16_sv(a_base + (int64_t)kt * BK, a_off[d],
+                     __builtin_amdgcn_readfirstlane(lds_addr(sA + sc * A_BYTES + sb * 16)));
+    } else {
+      constexpr int q = d - A_INSTR;
+      const int sb = (q * NWAVES + wave) * 64;
+      if ((B_SLOTS % (NWAVES * 64)) == 0 || sb < B_SLOTS)
+        lds_dma16_sv(b_base + (int64_t)kt * BK * n, b_off[q],
+                     __builtin_amdgcn_readfirstlane(lds_addr(sB + sc * B_BYTES + sb * 16)));
     }
+  };
+  // The MFMAs of one k-substep with other work spread between them: after
+  // MFMA m go the copy items [ND*m/NM, ND*(m+1)/NM) and then the read items
+  // [NR*m/NM, NR*(m+1)/NM).  Scheduling barriers pin this order, so that
+  // neither copies (which stall issue while the address unit is busy) nor
+  // LDS reads bunch up in front of the matrix core.
+  auto mfma_step = [&](v4i (&af)[FM], v4i (&bf)[FN], v16i (&acc)[FM][FN], auto ND_, auto NR_, auto&& copy, auto&& read) {
+    constexpr int NM = FM * FN, ND = decltype(ND_)::value, NR = decltype(NR_)::value;
+    static_for<0, NM>([&](auto m_) {
+      constexpr int m = decltype(m_)::value;
+      acc[m / FN][m % FN] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[m / FN], bf[m % FN], acc[m / FN][m % FN], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<ND * m / NM, ND * (m + 1) / NM>([&](auto d_) {
+        copy(d_);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      static_for<NR * m / NM, NR * (m + 1) / NM>([&](auto r_) {
+        read(r_);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
   };
 
   // Entering stage j of the current tile: its copies are complete, and every
@@ -558,21 +619,28 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     int stage = 0;
     for (int kt = 0; kt < ktiles; ++kt) {
       const int stage_next = stage + 1 == STAGES ? 0 : stage + 1;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int cur_f = kk & 1, nxt_f = cur_f ^ 1;
-        if (kk + 1 < KK) {
-          load_frags(stage, kk + 1, af[nxt_f], bf[nxt_f]);
+      auto no_copy = [&](auto) {};
+      static_for<0, KK>([&](auto kk_) {
+        constexpr int kk = decltype(kk_)::value;
+        constexpr int cur_f = kk & 1, nxt_f = cur_f ^ 1;
+        if constexpr (kk + 1 < KK) {
+          // next substep of this stage, read under this substep's MFMAs
+          auto rd = [&](auto r_) {
+            constexpr int r = decltype(r_)::value;
+            if constexpr (r < FM) read_a(stage, kk + 1, r, af[nxt_f][r]);
+            else read_b(stage, kk + 1, r - FM, bf[nxt_f][r - FM]);
+          };
+          mfma_step(af[cur_f], bf[cur_f], acc, std::integral_constant<int, 0>{},
+                    std::integral_constant<int, FM + FN>{}, no_copy, rd);
         } else {
           if constexpr (INT4) {
             // int4 weights fetched on entering this stage, for the stage
             // STAGES-1 ahead, go to LDS before the next fetch reuses b4reg
             if (kt + STAGES - 1 < ktiles) store_b4(stage == 0 ? STAGES - 1 : stage - 1);
           }
-          if (kt + 1 < ktiles) {
+          const bool more = kt + 1 < ktiles;
+          if (more) {
             sync_stage(kt + 1);
-            refill(kt + 1);
-            load_frags(stage_next, 0, af[nxt_f], bf[nxt_f]);
           } else {
             // last stage: every copy of this tile has landed (wait_vmcnt<0>
             // below covers the row loads and the queue grab too)
@@ -592,15 +660,29 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
               prologue();
             }
           }
+          // Under this substep's MFMAs: the refill of the buffer just
+          // released (stage kt + STAGES) and the first substep of the next
+          // stage.  One instruction stream for every case (wave-uniform
+          // conditions inside the items), so that the accumulators stay in
+          // the same registers whatever path a k-step takes.
+          const bool fill = kt + STAGES < ktiles;
+          const int kt_fill = kt + STAGES;
+          const int sc_fill = stage;  // (kt + STAGES) % STAGES
+          auto cp = [&](auto d_) {
+            if (fill) copy_item(d_, sc_fill, kt_fill);
+          };
+          auto rd = [&](auto r_) {
+            constexpr int r = decltype(r_)::value;
+            if (more) {
+              if constexpr (r < FM) read_a(stage_next, 0, r, af[nxt_f][r]);
+              else read_b(stage_next, 0, r - FM, bf[nxt_f][r - FM]);
+            }
+          };
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_step(af[cur_f], bf[cur_f], acc, std::integral_constant<int, N_COPY>{},
+                    std::integral_constant<int, FM + FN>{}, cp, rd);
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur_f][i], bf[cur_f][j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      });
       stage = stage_next;
     }
     const int t2 = s_tiles[pb];
@@ -649,14 +731,17 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
           const float Pv[4] = {P4.x, P4.y, P4.z, P4.w};
           const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
           const int Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+          if constexpr (COMBINE == kCombineOrdered) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if constexpr (COMBINE == kCombineOrdered) {
+            for (int u = 0; u < 4; ++u) {
               float* rowp = wave_y + (int64_t)(i * 32 + q * 8 + u) * n;
 #pragma unroll
               for (int j = 0; j < FN; ++j)
                 __builtin_nontemporal_store(value(i, j, q * 4 + u, Pv[u], Lv[u]), (rowp + j * 32) + lane_off);
-            } else {
+            }
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
               if (Dv[u] < 0) continue;
               float* base = wave_out + (int64_t)Dv[u] * n;
 #pragma unroll
