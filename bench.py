@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--combine", default="auto", choices=["auto", "atomic", "ordered"])
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--tile-m", type=int, default=0, choices=[0, 32, 64, 128, 256],
+                    help="force the GEMM tile height (0 = the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="rows in the oracle sample (0 = auto)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -174,7 +176,7 @@ def main():
     cargs, keep = B.make_args(x1, x2, gl, out, scale=scale, pertoken_scale=pts, logit=logit, row_index=ri,
                               shared_input=shared, shared_input_offset=p.shared_input_offset,
                               group_list_type=p.group_list_type, deterministic=args.deterministic,
-                              combine=args.combine)
+                              combine=args.combine, tuning_config=[0, args.tile_m] if args.tile_m else None)
     plan = B.plan(cargs)
     ws_bytes = B.workspace_size(cargs)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)

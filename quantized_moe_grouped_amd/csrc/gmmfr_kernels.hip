@@ -571,10 +571,24 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   // wave has finished reading stage j-1 (its fragments are in registers).
   // Stage 0 of a tile waits for everything (the previous tile's stores are
   // counted by the same counter).
+  // Stage 0 of a tile: the previous tile's epilogue stores were issued after
+  // this tile's prologue copies, and may stay in flight.  After an ordered
+  // full-tile epilogue (FM*FN*16 separate stores, counted at half in case the
+  // compiler pairs some) the wait allows that many more; after any other
+  // epilogue only the later stages (younger than stage 0 either way).
+  constexpr int FAST_STORES = COMBINE == kCombineOrdered ? FM * FN * 8 : 0;
+  constexpr int W0_FULL = (STAGES - 2) * LOADS_FULL + FAST_STORES < 63 ? (STAGES - 2) * LOADS_FULL + FAST_STORES : 63;
+  constexpr int W0_SHORT = (STAGES - 2) * LOADS_SHORT + FAST_STORES < 63 ? (STAGES - 2) * LOADS_SHORT + FAST_STORES : 63;
+  bool stores_counted = false;  // the previous epilogue took the ordered full-tile path
   auto sync_stage = [&](int j) {
-    if (j > 0 && j + STAGES - 2 < ktiles) {
-      if (a_full) wait_vmcnt<(STAGES - 2) * LOADS_FULL>();
-      else wait_vmcnt<(STAGES - 2) * LOADS_SHORT>();
+    if (j + STAGES - 2 < ktiles) {
+      if (j == 0 && stores_counted) {
+        if (a_full) wait_vmcnt<W0_FULL>();
+        else wait_vmcnt<W0_SHORT>();
+      } else {
+        if (a_full) wait_vmcnt<(STAGES - 2) * LOADS_FULL>();
+        else wait_vmcnt<(STAGES - 2) * LOADS_SHORT>();
+      }
     } else {
       wait_vmcnt<0>();
     }
@@ -713,7 +727,9 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       v = v * lv;
       return v;
     };
-    if (e_valid == BM && e_col0 + BN <= n && n < (int64_t(1) << 28) && !dump) {
+    const bool fast_epi = e_valid == BM && e_col0 + BN <= n && n < (int64_t(1) << 28) && !dump;
+    stores_counted = fast_epi;
+    if (fast_epi) {
       // Full tile: no per-element guards.  Ordered stores use one wave-uniform
       // row base and one 32-bit lane offset for every store.
       const uint32_t lane_off = (uint32_t)((lane >> 5) * 4 * n + (lane & 31));
@@ -874,29 +890,49 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(KParams p, int32_t* coun
 }
 
 // Single workgroup of 1024 threads: exclusive scan of counts into offsets
-// (output_bs + 1 entries) and cursor := offsets.
+// (output_bs + 1 entries) and cursor := offsets.  Chunks of kScanChunk counts
+// are staged in LDS with coalesced loads, each thread scans a contiguous run
+// of the chunk, the 1024 run totals are scanned across the block, and the
+// chunk goes back out coalesced.
+constexpr int kScanChunk = 32768;  // 128 KiB of LDS
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* counts, int32_t* offsets, int32_t* cursor, int64_t nbins) {
+  __shared__ int32_t s_buf[kScanChunk];
   __shared__ int32_t s[1024];
   const int tid = threadIdx.x;
-  const int64_t per = (nbins + 1023) / 1024;
-  const int64_t b0 = tid * per, b1 = min(b0 + per, nbins);
-  int32_t local = 0;
-  for (int64_t b = b0; b < b1; ++b) local += counts[b];
-  s[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t t = tid >= off ? s[tid - off] : 0;
+  int32_t carry = 0;
+  for (int64_t base = 0; base < nbins; base += kScanChunk) {
+    const int len = (int)min((int64_t)kScanChunk, nbins - base);
+#pragma unroll 8
+    for (int i = tid; i < len; i += 1024) s_buf[i] = counts[base + i];
     __syncthreads();
-    s[tid] += t;
+    const int per = (len + 1023) / 1024;
+    const int b0 = min(tid * per, len), b1 = min(b0 + per, len);
+    int32_t local = 0;
+    for (int b = b0; b < b1; ++b) local += s_buf[b];
+    s[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int32_t t = tid >= off ? s[tid - off] : 0;
+      __syncthreads();
+      s[tid] += t;
+      __syncthreads();
+    }
+    int32_t run = carry + (tid > 0 ? s[tid - 1] : 0);
+    for (int b = b0; b < b1; ++b) {
+      const int32_t c = s_buf[b];
+      s_buf[b] = run;
+      run += c;
+    }
+    const int32_t total = s[1023];
+    __syncthreads();
+    for (int i = tid; i < len; i += 1024) {
+      offsets[base + i] = s_buf[i];
+      cursor[base + i] = s_buf[i];
+    }
+    carry += total;
     __syncthreads();
   }
-  int32_t run = tid > 0 ? s[tid - 1] : 0;
-  for (int64_t b = b0; b < b1; ++b) {
-    offsets[b] = run;
-    cursor[b] = run;
-    run += counts[b];
-  }
-  if (tid == 1023) offsets[nbins] = s[1023];
+  if (tid == 0) offsets[nbins] = carry;
 }
 
 __global__ __launch_bounds__(kThreads) void scatter_kernel(KParams p, int32_t* cursor, int32_t* list) {
@@ -934,16 +970,23 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p, const int32
         s_sorted[rank] = x;
       }
       __syncthreads();
+      // Rows in batches of kBatch: the batch's loads are issued together
+      // (independent, streamed once), then folded in ascending order.
+      constexpr int kBatch = 8;
+      typedef float v4f __attribute__((ext_vector_type(4)));
       for (int64_t j4 = tid; j4 < n4; j4 += kThreads) {
-        float4 v = seed4(p, d, j4);
-        for (int s = 0; s < len; ++s) {
-          const float4 y = *(const float4*)(p.y + (int64_t)s_sorted[s] * n + j4 * 4);
-          v.x = v.x + y.x;
-          v.y = v.y + y.y;
-          v.z = v.z + y.z;
-          v.w = v.w + y.w;
+        const float4 seed = seed4(p, d, j4);
+        v4f v = {seed.x, seed.y, seed.z, seed.w};
+        for (int s0 = 0; s0 < len; s0 += kBatch) {
+          v4f yb[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u)
+            if (s0 + u < len) yb[u] = __builtin_nontemporal_load((const v4f*)(p.y + (int64_t)s_sorted[s0 + u] * n) + j4);
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u)
+            if (s0 + u < len) v = v + yb[u];
         }
-        *(float4*)(p.out + d * n + j4 * 4) = v;
+        __builtin_nontemporal_store(v, (v4f*)(p.out + d * n) + j4);
       }
       __syncthreads();
     } else {

@@ -96,6 +96,23 @@ def test_auto_picks_ordered_for_large_problems():
     assert info.tile_m == 128
 
 
+@pytest.mark.parametrize("m,e,int4,want", [
+    (131072, 32, False, "ordered"),   # prefill-shaped: atomics would outlast the GEMM
+    (4096, 8, False, "ordered"),      # decode-shaped
+    (32768, 64, True, "atomic"),      # int4 weights: slower MFMA feed hides the atomics
+    (2048, 256, False, "atomic"),     # many experts: weight streaming dominates
+    (32, 4, False, "atomic"),
+])
+def test_auto_combine_follows_the_shape(m, e, int4, want):
+    a = _args(m=m, e=e, obs=max(m // 8, 1), int4=int4)
+    info = B.PlanInfo()
+    assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
+    assert info.combine == B.COMBINE[want]
+    a.deterministic = 1
+    assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
+    assert info.combine == B.COMBINE["ordered"]
+
+
 def test_plan_does_not_depend_on_data_and_follows_hint():
     a = _args(m=4096, n=7168, obs=512, e=8)
     info = B.PlanInfo()

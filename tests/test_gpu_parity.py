@@ -102,6 +102,13 @@ def test_long_segment_path():
     _check_full(p, hints=(None,))
 
 
+def test_many_destinations_scan_in_chunks():
+    """output_bs above the index scan's LDS chunk (32768 destinations): the
+    offsets are built over several chunks with a carry."""
+    p = W.random_problem(14, 3000, 64, 16, 3, output_bs=70001, bsdp=5000, shared_offset=60000)
+    _check_full(p, hints=(None,))
+
+
 def test_extreme_accumulators_round_like_the_oracle():
     """x1 = x2 = -128, k = 2048: acc = 2^25 (above 2^24); plus mixed
     magnitudes whose int32 -> fp32 conversion must round to nearest even."""
