@@ -260,7 +260,7 @@ static int run_stage2(const gmmfr_args* args, void* workspace, size_t workspace_
   if (log_enabled())
     std::fprintf(stderr, "[gmmfr] m=%lld k=%lld n=%lld e=%lld combine=%s %s grid=%d ws=%zu\n", (long long)d.m,
                  (long long)d.k, (long long)d.n, (long long)d.e, plan.combine == kCombineOrdered ? "ordered" : "atomic",
-                 tile_kernel_name(plan.tile, d.int4), plan.grid, plan.workspace_bytes);
+                 tile_kernel_name(plan.tile, d.int4, d.k), plan.grid, plan.workspace_bytes);
   const int err = launch_all(to_launch(args, d), plan, workspace, stream, gemm_events);
   return err == 0 ? GMMFR_OK : GMMFR_ERR_HIP;
 }
@@ -292,7 +292,7 @@ int gmm_finalize_routing_plan(const gmmfr_args* args, gmmfr_plan_info* info) {
   info->grid = plan.grid;
   info->int4_weights = d.int4 ? 1 : 0;
   info->workspace_bytes = (int64_t)plan.workspace_bytes;
-  std::snprintf(info->gemm_kernel, sizeof(info->gemm_kernel), "%s", tile_kernel_name(plan.tile, d.int4));
+  std::snprintf(info->gemm_kernel, sizeof(info->gemm_kernel), "%s", tile_kernel_name(plan.tile, d.int4, d.k));
   return GMMFR_OK;
 }
 

@@ -70,7 +70,7 @@ __device__ __forceinline__ int queue_tile(int q, int j, int total) {
 // One grab from queue q, then from the other queues in turn until a tile is
 // found or all are exhausted (-1).  Stealing only happens at the very end, and
 // makes every tile processed whatever the placement of workgroups on XCDs.
-__device__ int grab_tile_from(int* ctr, int q, int total) {
+__device__ __forceinline__ int grab_tile_from(int* ctr, int q, int total) {
   for (int tries = 0; tries < kTileQueues; ++tries) {
     const int qq = (q + tries) % kTileQueues;
     const int t = queue_tile(qq, atomicAdd(ctr + qq * kTileQueueStride, 1), total);
@@ -80,6 +80,12 @@ __device__ int grab_tile_from(int* ctr, int q, int total) {
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// A 64-bit value that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32) |
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)x));
+}
 
 // Destination row of source row i; -1 when outside [0, output_bs).
 __device__ __forceinline__ int64_t dest_row(const KParams& p, int64_t i) {
@@ -210,6 +216,12 @@ __device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, u
                : "memory");
 }
 
+// 4 bytes per lane (global_load_lds_dword), saddr form: lane i writes LDS
+// bytes [lds_base + 4 i, lds_base + 4 i + 4).  Inactive lanes write nothing.
+__device__ __forceinline__ void lds_dma4_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase) : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const LDS_PTR(void))p;
 }
@@ -298,7 +310,9 @@ __device__ __forceinline__ TileCoord tile_coord(const KParams& p, const int32_t*
   return c;
 }
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int OCC, bool INT4, int COMBINE>
+// CONT selects the continuous copy pipeline (int8 weights, k / BK >= STAGES,
+// checked by the host) over the tile-by-tile loop.
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int OCC, bool INT4, int COMBINE, bool CONT>
 __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -333,12 +347,15 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   int32_t* s_tile_pre = s_dyn + p.e;
   int64_t* s_scan = (int64_t*)sA;  // scan scratch, used before the first copy into sA
   static_assert(STAGES * A_BYTES >= kThreads * 8, "scan scratch fits in the A stages");
-  // per-row epilogue factors, double-buffered across consecutive tiles
+  // Per-row epilogue inputs of a tile (pertokenScale, logit, rowIndex) and
+  // per-column scales, as raw words of the caller's arrays, double-buffered
+  // across consecutive tiles: rowIndex takes two words per row when int64,
+  // one when int32; the scale one word per column (fp32) or per column pair
+  // (bf16).
   __shared__ __attribute__((aligned(16))) float s_pts[2][BM];
   __shared__ __attribute__((aligned(16))) float s_logit[2][BM];
-  __shared__ __attribute__((aligned(16))) int32_t s_dest[2][BM];
-  // per-column dequantisation scale of a tile, double-buffered the same way
-  __shared__ __attribute__((aligned(16))) float s_scale[2][BN];
+  __shared__ __attribute__((aligned(16))) uint32_t s_ridx[2][2 * BM];
+  __shared__ __attribute__((aligned(16))) uint32_t s_scale[2][BN];
 
   build_group_table(p, BM, s_ends, s_tile_pre, s_scan);
   const int total_tiles = s_tile_pre[p.e];
@@ -347,24 +364,23 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int lane_id = lane, wave_m = wm, wave_n = wn;
   const bool a_full = ((A_INSTR - 1) * NWAVES + wave) * 64 < A_SLOTS;  // wave-uniform
   const int64_t k = p.k, n = p.n;
   const int ktiles = (int)(k / BK);
 
-  // Tiles come from per-XCD queues so that the tiles running at the same time
-  // on one XCD are consecutive in raster order and share panels in its L2.
   __shared__ int s_tiles[2];
   const int xcd = xcc_id();
-  if (tid == 0) {
-    s_tiles[0] = grab_tile_from(p.tile_ctr, xcd, total_tiles);
-    s_tiles[1] = s_tiles[0] >= 0 ? grab_tile_from(p.tile_ctr, xcd, total_tiles) : -1;
-  }
-  __syncthreads();
-  int t = s_tiles[0];
-  int t1 = s_tiles[1];
-  if (t < 0) return;
-
-  auto coord = [&](int tt) { return tile_coord<BM, BN>(p, s_ends, s_tile_pre, tt); };
+  // Tile coordinates are the same for every lane; say so, so that they stay
+  // in scalar registers.
+  auto coord = [&](int tt) {
+    TileCoord c = tile_coord<BM, BN>(p, s_ends, s_tile_pre, __builtin_amdgcn_readfirstlane(tt));
+    c.g = __builtin_amdgcn_readfirstlane(c.g);
+    c.valid_rows = __builtin_amdgcn_readfirstlane(c.valid_rows);
+    c.row0 = uniform64(c.row0);
+    c.col0 = uniform64(c.col0);
+    return c;
+  };
 
   // ---- per-tile copy sources: wave-uniform bases plus per-lane offsets
   // (bytes, < BM*k resp. < BK*n, so they fit in 32 bits)
@@ -467,34 +483,77 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       }
     }
   };
-  // per-row factors of a tile into buffer `pb`: loads first, LDS writes later
-  float fp_pts = 1.0f, fp_logit = 1.0f, fp_scale = 1.0f;
-  int32_t fp_dest = -1;
+  // Per-row and per-column epilogue inputs of a tile into buffer `pb`, as raw
+  // words.  Rows past the group or past m and columns past n read a clamped,
+  // valid address; the epilogue never uses them.
+  const int ridx_words = p.row_index ? (p.row_index_i32 ? BM : 2 * BM) : 0;
+  const int scale_words = p.scale ? (p.scale_bf16 ? BN / 2 : BN) : 0;
+  auto row_word_src = [&](const TileCoord& c, int q, int words_per_row) -> int64_t {
+    const int64_t row = min(c.row0 + q / words_per_row, p.m - 1);
+    return row * words_per_row + q % words_per_row;  // word index into the array
+  };
+  auto scale_word_src = [&](const TileCoord& c, int q) -> int64_t {
+    // fp32: one column per word; bf16: columns 2q, 2q+1 (n is even)
+    if (p.scale_bf16) return ((int64_t)c.g * n + min(c.col0 + 2 * q, n - 2)) / 2;
+    return (int64_t)c.g * n + min(c.col0 + q, n - 1);
+  };
+  // Register path (the k-loop with a tile prologue): loads now, LDS writes later.
+  uint32_t fr_pts = 0, fr_logit = 0, fr_ridx0 = 0, fr_ridx1 = 0, fr_scale = 0;
   auto fetch_rows = [&](const TileCoord& c) {
-    fp_pts = 1.0f;
-    fp_logit = 1.0f;
-    fp_scale = 1.0f;
-    fp_dest = -1;
-    if (tid < BM && tid < c.valid_rows) {
-      const int64_t row = c.row0 + tid;
-      if (p.pertoken) fp_pts = p.pertoken[row];
-      if (p.logit) fp_logit = p.logit[row];
-      fp_dest = (int32_t)dest_row(p, row);
+    if (tid < BM) {
+      if (p.pertoken) fr_pts = ((const uint32_t*)p.pertoken)[row_word_src(c, tid, 1)];
+      if (p.logit) fr_logit = ((const uint32_t*)p.logit)[row_word_src(c, tid, 1)];
     }
-    const int64_t col = c.col0 + tid;
-    if (tid < BN && p.scale && col < n)
-      fp_scale = p.scale_bf16 ? bf16_to_f32(((const uint16_t*)p.scale)[(int64_t)c.g * n + col])
-                              : ((const float*)p.scale)[(int64_t)c.g * n + col];
+    const uint32_t* ri = (const uint32_t*)p.row_index;
+    if (tid < ridx_words) fr_ridx0 = ri[row_word_src(c, tid, ridx_words / BM)];
+    if (tid + kThreads < ridx_words) fr_ridx1 = ri[row_word_src(c, tid + kThreads, ridx_words / BM)];
+    if (tid < scale_words) fr_scale = ((const uint32_t*)p.scale)[scale_word_src(c, tid)];
   };
   auto store_rows = [&](int pb) {
     if (tid < BM) {
-      s_pts[pb][tid] = fp_pts;
-      s_logit[pb][tid] = fp_logit;
-      s_dest[pb][tid] = fp_dest;
+      s_pts[pb][tid] = __uint_as_float(fr_pts);
+      s_logit[pb][tid] = __uint_as_float(fr_logit);
     }
-    if (tid < BN) s_scale[pb][tid] = fp_scale;
+    if (tid < ridx_words) s_ridx[pb][tid] = fr_ridx0;
+    if (tid + kThreads < ridx_words) s_ridx[pb][tid + kThreads] = fr_ridx1;
+    if (tid < scale_words) s_scale[pb][tid] = fr_scale;
   };
-  static_assert(BM <= kThreads && BN <= kThreads, "one thread per tile row and per tile column");
+  // Copy path (the continuous pipeline): straight to LDS, one word per lane,
+  // from a per-tile base so that lane offsets stay small.  Issued before the
+  // k-step copies that follow, so the stage waits cover them.
+  auto dma_rows = [&](const TileCoord& c, int pb) {
+    auto words = [&](const uint32_t* base_any, uint32_t* dst, int nwords, auto&& word_off) {
+      const uint32_t* base = (const uint32_t*)uniform64((int64_t)base_any);  // the same in every lane
+      const int q = wave * 64 + lane;
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const int qq = q + pass * kThreads;
+        if (pass * kThreads + wave * 64 < nwords) {  // wave-uniform
+          if (qq < nwords)
+            lds_dma4_sv(base, (uint32_t)word_off(qq) * 4u,
+                        __builtin_amdgcn_readfirstlane(lds_addr(dst + pass * kThreads + wave * 64)));
+        }
+      }
+    };
+    auto row_off = [&](int q, int wpr) { return (int)(min(c.row0 + q / wpr, p.m - 1) - c.row0) * wpr + q % wpr; };
+    if (p.pertoken)
+      words((const uint32_t*)p.pertoken + c.row0, (uint32_t*)s_pts[pb], BM, [&](int q) { return row_off(q, 1); });
+    if (p.logit)
+      words((const uint32_t*)p.logit + c.row0, (uint32_t*)s_logit[pb], BM, [&](int q) { return row_off(q, 1); });
+    if (ridx_words) {
+      const int wpr = ridx_words / BM;
+      words((const uint32_t*)p.row_index + c.row0 * wpr, s_ridx[pb], ridx_words, [&](int q) { return row_off(q, wpr); });
+    }
+    if (scale_words) {
+      if (p.scale_bf16)
+        words((const uint32_t*)((const uint16_t*)p.scale + (int64_t)c.g * n + c.col0), s_scale[pb], scale_words,
+              [&](int q) { return (int)(min(c.col0 + 2 * q, n - 2) - c.col0) / 2; });
+      else
+        words((const uint32_t*)p.scale + (int64_t)c.g * n + c.col0, s_scale[pb], scale_words,
+              [&](int q) { return (int)(min(c.col0 + q, n - 1) - c.col0); });
+    }
+  };
+  static_assert(BM <= kThreads && BN <= kThreads && 2 * BM <= 2 * kThreads, "one pass per tile row and column");
 
   // Fragment reads.  Read item r of a k-substep: A fragments first, then B.
   auto read_a = [&](int sc, int kk, int i, v4i& dst) {
@@ -545,27 +604,34 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
                      __builtin_amdgcn_readfirstlane(lds_addr(sB + sc * B_BYTES + sb * 16)));
     }
   };
-  // The MFMAs of one k-substep with other work spread between them: after
-  // MFMA m go the copy items [ND*m/NM, ND*(m+1)/NM) and then the read items
-  // [NR*m/NM, NR*(m+1)/NM).  Scheduling barriers pin this order, so that
-  // neither copies (which stall issue while the address unit is busy) nor
-  // LDS reads bunch up in front of the matrix core.
+  // The MFMAs of one k-substep with other work spread between them: copy item
+  // x of ND goes after MFMA x*NM/ND, read item x of NR after MFMA
+  // x*(NM-2)/NR (the last two MFMAs cover the latency of the last reads).
+  // Scheduling barriers pin this order, so that neither copies (which stall
+  // issue while the address unit is busy) nor LDS reads bunch up in front of
+  // the matrix core.
   auto mfma_step = [&](v4i (&af)[FM], v4i (&bf)[FN], v16i (&acc)[FM][FN], auto ND_, auto NR_, auto&& copy, auto&& read) {
     constexpr int NM = FM * FN, ND = decltype(ND_)::value, NR = decltype(NR_)::value;
+    constexpr int RSPAN = NM > 2 ? NM - 2 : NM;
     static_for<0, NM>([&](auto m_) {
       constexpr int m = decltype(m_)::value;
       acc[m / FN][m % FN] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[m / FN], bf[m % FN], acc[m / FN][m % FN], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      static_for<ND * m / NM, ND * (m + 1) / NM>([&](auto d_) {
-        copy(d_);
-        __builtin_amdgcn_sched_barrier(0);
+      static_for<0, ND>([&](auto d_) {
+        if constexpr (decltype(d_)::value * NM / ND == m) {
+          copy(d_);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       });
-      static_for<NR * m / NM, NR * (m + 1) / NM>([&](auto r_) {
-        read(r_);
-        __builtin_amdgcn_sched_barrier(0);
+      static_for<0, NR>([&](auto r_) {
+        if constexpr (decltype(r_)::value * RSPAN / NR == m) {
+          read(r_);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       });
     });
   };
+  auto no_copy = [&](auto) {};
 
   // Entering stage j of the current tile: its copies are complete, and every
   // wave has finished reading stage j-1 (its fragments are in registers).
@@ -599,7 +665,261 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     if (j + STAGES - 1 < ktiles) issue_stage((j + STAGES - 1) % STAGES, j + STAGES - 1);
   };
 
-  // ---- first tile
+  // ---- epilogue of one tile.  Lane holds column lane%32 and rows
+  // (r/4)*8 + (lane/32)*4 + r%4 of each 32x32 block; four consecutive
+  // registers are four consecutive rows.  Returns whether the ordered
+  // full-tile path (FM*FN*16 separate stores) was taken.
+  auto epilogue = [&](const TileCoord& c, int pb, v16i (&acc)[FM][FN]) -> bool {
+    // The tile coordinates pass through an opaque point so that no epilogue
+    // address is computed (and kept live, or spilled) across the mainloop.
+    int64_t e_row0 = uniform64(c.row0), e_col0 = uniform64(c.col0);
+    int e_valid = __builtin_amdgcn_readfirstlane(c.valid_rows);
+    asm volatile("" : "+s"(e_row0), "+s"(e_col0), "+s"(e_valid));
+    // Likewise the lane and wave indices: every lane-dependent epilogue
+    // address is computed here, not hoisted out of the tile loop (where it
+    // would be kept live, or spilled, across the mainloop).
+    int lane = lane_id;
+    int wm = wave_m, wn = wave_n;
+    asm volatile("" : "+v"(lane), "+s"(wm), "+s"(wn));
+    const bool dump = p.acc_out != nullptr;
+    float scv[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int cl = wn * WTN + j * 32 + (lane & 31);
+      scv[j] = 1.0f;
+      if (p.scale) {
+        if (p.scale_bf16) {
+          const uint32_t w = s_scale[pb][cl >> 1];
+          scv[j] = __uint_as_float((cl & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        } else {
+          scv[j] = __uint_as_float(s_scale[pb][cl]);
+        }
+      }
+    }
+    const float4 ones = make_float4(1.f, 1.f, 1.f, 1.f);
+    auto factors = [&](int lr0, float (&Pv)[4], float (&Lv)[4], int (&Dv)[4]) {
+      const float4 P4 = p.pertoken ? *(const float4*)(&s_pts[pb][lr0]) : ones;
+      const float4 L4 = p.logit ? *(const float4*)(&s_logit[pb][lr0]) : ones;
+      Pv[0] = P4.x; Pv[1] = P4.y; Pv[2] = P4.z; Pv[3] = P4.w;
+      Lv[0] = L4.x; Lv[1] = L4.y; Lv[2] = L4.z; Lv[3] = L4.w;
+      if constexpr (COMBINE == kCombineAtomic) {
+        // destination of each row from the raw rowIndex words; -1 when
+        // outside [0, outputBS)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = lr0 + u;
+          int64_t d;
+          if (!p.row_index) d = e_row0 + r;
+          else if (p.row_index_i32) d = (int32_t)s_ridx[pb][r];
+          else d = (int64_t)((uint64_t)s_ridx[pb][2 * r] | ((uint64_t)s_ridx[pb][2 * r + 1] << 32));
+          Dv[u] = (d >= 0 && d < p.output_bs) ? (int)d : -1;
+        }
+      } else {
+        Dv[0] = Dv[1] = Dv[2] = Dv[3] = -1;
+      }
+    };
+    // One element: int32 -> fp32 (round to nearest even), then the three
+    // factors in the oracle's order.
+    auto value = [&](int i, int j, int r, float pv, float lv) {
+      int32_t a = acc_elem<(FM * FN * 16 > 128)>(acc[i][j][r]);
+      if constexpr (INT4) a >>= 4;  // weights were staged as 16 * w
+      float v = (float)a;
+      v = v * scv[j];
+      v = v * pv;
+      v = v * lv;
+      return v;
+    };
+    const bool fast_epi = e_valid == BM && e_col0 + BN <= n && n < (int64_t(1) << 28) && !dump;
+    if (fast_epi) {
+      // Full tile: no per-element guards.  Ordered stores use one wave-uniform
+      // row base and one 32-bit lane offset for every store.
+      const uint32_t lane_off = (uint32_t)((lane >> 5) * 4 * n + (lane & 31));
+      float* wave_y = p.y + (e_row0 + wm * WTM) * n + e_col0 + wn * WTN;
+      float* wave_out = p.out + e_col0 + wn * WTN + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int lr0 = wm * WTM + i * 32 + q * 8 + (lane >> 5) * 4;
+          float Pv[4], Lv[4];
+          int Dv[4];
+          factors(lr0, Pv, Lv, Dv);
+          if constexpr (COMBINE == kCombineOrdered) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              float* rowp = wave_y + (int64_t)(i * 32 + q * 8 + u) * n;
+#pragma unroll
+              for (int j = 0; j < FN; ++j)
+                __builtin_nontemporal_store(value(i, j, q * 4 + u, Pv[u], Lv[u]), (rowp + j * 32) + lane_off);
+            }
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              if (Dv[u] < 0) continue;
+              float* base = wave_out + (int64_t)Dv[u] * n;
+#pragma unroll
+              for (int j = 0; j < FN; ++j)
+                __hip_atomic_fetch_add(base + j * 32, value(i, j, q * 4 + u, Pv[u], Lv[u]), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        }
+      }
+    } else {
+      // Partial tile (group tail or n tail) or accumulator dump: guarded.
+      const int64_t lane_col = e_col0 + wn * WTN + (lane & 31);
+      bool col_ok[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) col_ok[j] = lane_col + j * 32 < n;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int lr0 = wm * WTM + i * 32 + q * 8 + (lane >> 5) * 4;
+          float Pv[4], Lv[4];
+          int Dv[4];
+          factors(lr0, Pv, Lv, Dv);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int lr = lr0 + u;
+            if (lr >= e_valid) continue;
+            float* base;
+            if constexpr (COMBINE == kCombineOrdered) {
+              base = p.y + (e_row0 + lr) * n + lane_col;
+            } else {
+              if (Dv[u] < 0) continue;
+              base = p.out + (int64_t)Dv[u] * n + lane_col;
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              if (!col_ok[j]) continue;
+              if (dump) {
+                int32_t a = acc_elem<(FM * FN * 16 > 128)>(acc[i][j][q * 4 + u]);
+                if constexpr (INT4) a >>= 4;
+                p.acc_out[(e_row0 + lr) * n + lane_col + j * 32] = a;
+              }
+              const float v = value(i, j, q * 4 + u, Pv[u], Lv[u]);
+              if constexpr (COMBINE == kCombineOrdered)
+                __builtin_nontemporal_store(v, base + j * 32);
+              else
+                __hip_atomic_fetch_add(base + j * 32, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        }
+      }
+    }
+    return fast_epi;
+  };
+
+  // ===== Continuous copy pipeline (int8 weights, at least STAGES k-steps).
+  // One stream of k-steps across this workgroup's tiles: the refill issued
+  // at a k-step fetches the k-slice STAGES steps ahead, which near a tile's
+  // end belongs to the next tile, so no tile starts with a prologue wait.
+  // Tile order is static: workgroup w takes the tiles of raster queue w % 8
+  // (blocks of kTileBlock consecutive tiles dealt to the 8 queues in turn,
+  // workgroups being dealt to the 8 XCDs in the same way) in turn with the
+  // other workgroups of that queue.  Every k-step has the same shape: the
+  // MFMAs of substep 0 with the reads of substep 1; the wait for the next
+  // k-step's copies and a barrier; the MFMAs of substep 1 with the refill of
+  // the buffer just released and the next k-step's substep-0 reads.
+  static_assert(!CONT || (!INT4 && KK == 2), "continuous pipeline: int8 weights, two substeps per stage");
+  if constexpr (CONT) {
+    {
+      const int G = gridDim.x;
+      const bool blocked = G % kTileQueues == 0;
+      const int vq = blockIdx.x % kTileQueues, lw = blockIdx.x / kTileQueues, per_q = G / kTileQueues;
+      auto tile_at = [&](int j) -> int {
+        if (blocked) return queue_tile(vq, j * per_q + lw, total_tiles);
+        const int64_t tt = (int64_t)j * G + blockIdx.x;
+        return tt < total_tiles ? (int)tt : -1;
+      };
+      int j = 0;
+      const int t0 = tile_at(0);
+      if (t0 < 0) return;
+      TileCoord cur = coord(t0);
+      int t_nxt = tile_at(1);
+      TileCoord nxt = cur;  // without a next tile the last refills re-copy this one
+      if (t_nxt >= 0) nxt = coord(t_nxt);
+      int pb = 0;
+      dma_rows(cur, pb);
+      set_sources(cur);
+      static_for<0, STAGES>([&](auto st_) { issue_stage(decltype(st_)::value, decltype(st_)::value); });
+      if (a_full) wait_vmcnt<(STAGES - 1) * LOADS_FULL>();
+      else wait_vmcnt<(STAGES - 1) * LOADS_SHORT>();
+      lds_barrier();
+      v4i af[2][FM], bf[2][FN];
+      load_frags(0, 0, af[0], bf[0]);
+      int stage = 0;
+      bool prev_fast = false;
+      v16i acc[FM][FN];
+      auto kstep = [&](int kt, int fill_ks) {
+        const int stage_next = stage + 1 == STAGES ? 0 : stage + 1;
+        auto rd1 = [&](auto r_) {
+          constexpr int r = decltype(r_)::value;
+          if constexpr (r < FM) read_a(stage, 1, r, af[1][r]);
+          else read_b(stage, 1, r - FM, bf[1][r - FM]);
+        };
+        mfma_step(af[0], bf[0], acc, std::integral_constant<int, 0>{}, std::integral_constant<int, FM + FN>{},
+                  no_copy, rd1);
+        // the next k-step's copies have landed and every wave holds this
+        // stage's fragments; after the first k-step of a tile the previous
+        // tile's epilogue stores may still be in flight
+        if (kt == 0 && prev_fast) {
+          if (a_full) wait_vmcnt<W0_FULL>();
+          else wait_vmcnt<W0_SHORT>();
+        } else {
+          if (a_full) wait_vmcnt<(STAGES - 2) * LOADS_FULL>();
+          else wait_vmcnt<(STAGES - 2) * LOADS_SHORT>();
+        }
+        lds_barrier();
+        auto cp = [&](auto d_) { copy_item(d_, stage, fill_ks); };
+        auto rd0 = [&](auto r_) {
+          constexpr int r = decltype(r_)::value;
+          if constexpr (r < FM) read_a(stage_next, 0, r, af[0][r]);
+          else read_b(stage_next, 0, r - FM, bf[0][r - FM]);
+        };
+        mfma_step(af[1], bf[1], acc, std::integral_constant<int, N_COPY>{}, std::integral_constant<int, FM + FN>{},
+                  cp, rd0);
+        stage = stage_next;
+      };
+      while (true) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < FN; ++jj) acc[i][jj] = v16i{0};
+#pragma unroll 1
+        for (int kt = 0; kt < ktiles - STAGES; ++kt) kstep(kt, kt + STAGES);
+        set_sources(nxt);  // the remaining refills fetch the next tile's first k-slices
+#pragma unroll 1
+        for (int kt = ktiles - STAGES; kt < ktiles; ++kt) kstep(kt, kt + STAGES - ktiles);
+        prev_fast = epilogue(cur, pb, acc);
+        if (t_nxt < 0) break;
+        ++j;
+        cur = nxt;
+        t_nxt = tile_at(j + 1);
+        if (t_nxt >= 0) nxt = coord(t_nxt);
+        pb ^= 1;
+        dma_rows(cur, pb);
+      }
+      wait_vmcnt<0>();  // no copy in flight when the workgroup ends
+      return;
+    }
+  }
+
+  if constexpr (!CONT) {
+  // ===== Tile-by-tile loop (int4 weights, or fewer than STAGES k-steps):
+  // tiles from per-XCD queues (tiles running together on one XCD are
+  // consecutive in raster order and share panels in its L2; an empty queue
+  // steals from the others), each tile starting with its own prologue.
+  if (tid == 0) {
+    s_tiles[0] = grab_tile_from(p.tile_ctr, xcd, total_tiles);
+    s_tiles[1] = s_tiles[0] >= 0 ? grab_tile_from(p.tile_ctr, xcd, total_tiles) : -1;
+  }
+  __syncthreads();
+  int t = s_tiles[0];
+  int t1 = s_tiles[1];
+  if (t < 0) return;
+
   TileCoord cur = coord(t);
   int pb = 0;
   set_sources(cur);
@@ -633,7 +953,6 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     int stage = 0;
     for (int kt = 0; kt < ktiles; ++kt) {
       const int stage_next = stage + 1 == STAGES ? 0 : stage + 1;
-      auto no_copy = [&](auto) {};
       static_for<0, KK>([&](auto kk_) {
         constexpr int kk = decltype(kk_)::value;
         constexpr int cur_f = kk & 1, nxt_f = cur_f ^ 1;
@@ -700,126 +1019,13 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       stage = stage_next;
     }
     const int t2 = s_tiles[pb];
-
-    // ---- epilogue.  Lane holds column lane%32 and rows (r/4)*8 + (lane/32)*4 + r%4
-    // of each 32x32 block; four consecutive registers are four consecutive rows.
-    // The tile coordinates pass through an opaque point here so that no
-    // epilogue address is computed (and kept live, or spilled) across the
-    // mainloop.
-    int64_t e_row0 = cur.row0, e_col0 = cur.col0;
-    int e_valid = cur.valid_rows;
-    asm volatile("" : "+s"(e_row0), "+s"(e_col0), "+s"(e_valid));
-    const bool dump = p.acc_out != nullptr;
-    const float* rp_pts = s_pts[pb];
-    const float* rp_logit = s_logit[pb];
-    const int32_t* rp_dest = s_dest[pb];
-    float scv[FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) scv[j] = s_scale[pb][wn * WTN + j * 32 + (lane & 31)];
-    // One element: int32 -> fp32 (round to nearest even), then the three
-    // factors in the oracle's order.
-    auto value = [&](int i, int j, int r, float pv, float lv) {
-      int32_t a = acc_elem<(FM * FN * 16 > 128)>(acc[i][j][r]);
-      if constexpr (INT4) a >>= 4;  // weights were staged as 16 * w
-      float v = (float)a;
-      v = v * scv[j];
-      v = v * pv;
-      v = v * lv;
-      return v;
-    };
-    const bool fast_epi = e_valid == BM && e_col0 + BN <= n && n < (int64_t(1) << 28) && !dump;
-    stores_counted = fast_epi;
-    if (fast_epi) {
-      // Full tile: no per-element guards.  Ordered stores use one wave-uniform
-      // row base and one 32-bit lane offset for every store.
-      const uint32_t lane_off = (uint32_t)((lane >> 5) * 4 * n + (lane & 31));
-      float* wave_y = p.y + (e_row0 + wm * WTM) * n + e_col0 + wn * WTN;
-      float* wave_out = p.out + e_col0 + wn * WTN + (lane & 31);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int lr0 = wm * WTM + i * 32 + q * 8 + (lane >> 5) * 4;
-          const float4 P4 = *(const float4*)(rp_pts + lr0);
-          const float4 L4 = *(const float4*)(rp_logit + lr0);
-          int4 D4 = make_int4(-1, -1, -1, -1);
-          if constexpr (COMBINE == kCombineAtomic) D4 = *(const int4*)(rp_dest + lr0);
-          const float Pv[4] = {P4.x, P4.y, P4.z, P4.w};
-          const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
-          const int Dv[4] = {D4.x, D4.y, D4.z, D4.w};
-          if constexpr (COMBINE == kCombineOrdered) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              float* rowp = wave_y + (int64_t)(i * 32 + q * 8 + u) * n;
-#pragma unroll
-              for (int j = 0; j < FN; ++j)
-                __builtin_nontemporal_store(value(i, j, q * 4 + u, Pv[u], Lv[u]), (rowp + j * 32) + lane_off);
-            }
-          } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              if (Dv[u] < 0) continue;
-              float* base = wave_out + (int64_t)Dv[u] * n;
-#pragma unroll
-              for (int j = 0; j < FN; ++j)
-                __hip_atomic_fetch_add(base + j * 32, value(i, j, q * 4 + u, Pv[u], Lv[u]), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            }
-          }
-        }
-      }
-    } else {
-      // Partial tile (group tail or n tail) or accumulator dump: guarded.
-      const int64_t lane_col = e_col0 + wn * WTN + (lane & 31);
-      bool col_ok[FN];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) col_ok[j] = lane_col + j * 32 < n;
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int lr0 = wm * WTM + i * 32 + q * 8 + (lane >> 5) * 4;
-          const float4 P4 = *(const float4*)(rp_pts + lr0);
-          const float4 L4 = *(const float4*)(rp_logit + lr0);
-          int4 D4 = make_int4(-1, -1, -1, -1);
-          if constexpr (COMBINE == kCombineAtomic) D4 = *(const int4*)(rp_dest + lr0);
-          const float Pv[4] = {P4.x, P4.y, P4.z, P4.w};
-          const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
-          const int Dv[4] = {D4.x, D4.y, D4.z, D4.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int lr = lr0 + u;
-            if (lr >= e_valid) continue;
-            float* base;
-            if constexpr (COMBINE == kCombineOrdered) {
-              base = p.y + (e_row0 + lr) * n + lane_col;
-            } else {
-              if (Dv[u] < 0) continue;
-              base = p.out + (int64_t)Dv[u] * n + lane_col;
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-              if (!col_ok[j]) continue;
-              if (dump) {
-                int32_t a = acc_elem<(FM * FN * 16 > 128)>(acc[i][j][q * 4 + u]);
-                if constexpr (INT4) a >>= 4;
-                p.acc_out[(e_row0 + lr) * n + lane_col + j * 32] = a;
-              }
-              const float v = value(i, j, q * 4 + u, Pv[u], Lv[u]);
-              if constexpr (COMBINE == kCombineOrdered)
-                __builtin_nontemporal_store(v, base + j * 32);
-              else
-                __hip_atomic_fetch_add(base + j * 32, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-          }
-        }
-      }
-    }
+    stores_counted = epilogue(cur, pb, acc);
     if (!has_next) break;
     t = t1;
     t1 = t2;
     cur = nxt;
     pb ^= 1;
+  }
   }
 }
 
@@ -1032,14 +1238,17 @@ TileShape tile_shape(TileId id) {
 
 int tile_occupancy(TileId id) { return id == kTile256x256 ? 1 : 2; }
 
-const char* tile_kernel_name(TileId id, bool int4) {
-  static const char* names[kNumTiles][2] = {
-      {"gmm_kernel<256,256,64,2x2,s3,i8>", "gmm_kernel<256,256,64,2x2,s3,i4>"},
-      {"gmm_kernel<128,256,64,2x2,s3,i8>", "gmm_kernel<128,256,64,2x2,s3,i4>"},
-      {"gmm_kernel<64,256,64,1x4,s3,i8>", "gmm_kernel<64,256,64,1x4,s3,i4>"},
-      {"gmm_kernel<32,256,64,1x4,s3,i8>", "gmm_kernel<32,256,64,1x4,s3,i4>"},
+bool uses_continuous_pipeline(bool int4, int64_t k, int bk, int stages) { return !int4 && k / bk >= stages; }
+
+const char* tile_kernel_name(TileId id, bool int4, int64_t k) {
+  static const char* names[kNumTiles][3] = {
+      {"gmm_kernel<256,256,64,2x2,s3,i8>", "gmm_kernel<256,256,64,2x2,s3,i4>", "gmm_kernel<256,256,64,2x2,s3,i8,cont>"},
+      {"gmm_kernel<128,256,64,2x2,s3,i8>", "gmm_kernel<128,256,64,2x2,s3,i4>", "gmm_kernel<128,256,64,2x2,s3,i8,cont>"},
+      {"gmm_kernel<64,256,64,1x4,s3,i8>", "gmm_kernel<64,256,64,1x4,s3,i4>", "gmm_kernel<64,256,64,1x4,s3,i8,cont>"},
+      {"gmm_kernel<32,256,64,1x4,s3,i8>", "gmm_kernel<32,256,64,1x4,s3,i4>", "gmm_kernel<32,256,64,1x4,s3,i8,cont>"},
   };
-  return names[(int)id][int4 ? 1 : 0];
+  const TileShape ts = tile_shape(id);
+  return names[(int)id][int4 ? 1 : uses_continuous_pipeline(int4, k, ts.bk, 3) ? 2 : 0];
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1069,12 +1278,15 @@ template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC>
 static void launch_gemm(const KParams& kp, bool int4, int grid, hipStream_t s) {
   const dim3 gd(grid), bd(kThreads);
   const size_t dyn = ((size_t)(2 * kp.e + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
+  const bool cont = uses_continuous_pipeline(int4, kp.k, BK, ST);
   if (kp.combine == kCombineOrdered) {
-    if (int4) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineOrdered>), gd, bd, dyn, s, kp);
-    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineOrdered>), gd, bd, dyn, s, kp);
+    if (int4) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineOrdered, false>), gd, bd, dyn, s, kp);
+    else if (cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineOrdered, true>), gd, bd, dyn, s, kp);
+    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineOrdered, false>), gd, bd, dyn, s, kp);
   } else {
-    if (int4) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineAtomic>), gd, bd, dyn, s, kp);
-    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineAtomic>), gd, bd, dyn, s, kp);
+    if (int4) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineAtomic, false>), gd, bd, dyn, s, kp);
+    else if (cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineAtomic, true>), gd, bd, dyn, s, kp);
+    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineAtomic, false>), gd, bd, dyn, s, kp);
   }
 }
 
