@@ -162,16 +162,17 @@ Combine choose_combine(const gmmfr_args* a, const Derived& d) {
   if (a->deterministic == 1 || a->combine == GMMFR_COMBINE_ORDERED) return kCombineOrdered;
   if (a->combine == GMMFR_COMBINE_ATOMIC) return kCombineAtomic;
   // fp32 atomics retire at a fixed rate (about 1.3 TB/s of payload on this
-  // part) but overlap the GEMM; the ordered path costs a y round trip plus the
-  // reduction.  Atomics win while their time stays well under the GEMM's own
-  // (the larger of its MFMA time and its weight-streaming time), estimated
-  // from the shapes alone so the plan never depends on device data.
+  // part) and slow the GEMM once they exceed about half of its own time; the
+  // ordered path costs a y round trip, the reduction and some 30 us of extra
+  // launches.  The GEMM's time is the larger of its MFMA time and its
+  // weight-streaming time, at measured rates, estimated from the shapes alone
+  // so the plan never depends on device data.
   const double contributions = (double)d.m * (double)d.n;
   const double t_atomic = contributions * 4.0 / 1.3e12;
-  const double t_mfma = 2.0 * (double)d.m * (double)d.k * (double)d.n / (d.int4 ? 1.0e15 : 1.4e15);
+  const double t_mfma = 2.0 * (double)d.m * (double)d.k * (double)d.n / (d.int4 ? 0.93e15 : 1.6e15);
   const double experts = (double)std::min<int64_t>(d.e, std::max<int64_t>(d.m, 1));
   const double t_weights = experts * (double)d.k * (double)d.n * (d.int4 ? 0.5 : 1.0) / 5.0e12;
-  return t_atomic < 0.85 * std::max(t_mfma, t_weights) ? kCombineAtomic : kCombineOrdered;
+  return t_atomic < 0.5 * std::max(t_mfma, t_weights) + 30e-6 ? kCombineAtomic : kCombineOrdered;
 }
 
 int make_plan(const gmmfr_args* a, const Derived& d, int cu_count, Plan* plan) {
