@@ -892,6 +892,9 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
         set_sources(nxt);  // the remaining refills fetch the next tile's first k-slices
 #pragma unroll 1
         for (int kt = ktiles - STAGES; kt < ktiles; ++kt) kstep(kt, kt + STAGES - ktiles);
+        // the next tile's row and column inputs go to the other buffer before
+        // this tile's stores fill the copy queue
+        if (t_nxt >= 0) dma_rows(nxt, pb ^ 1);
         prev_fast = epilogue(cur, pb, acc);
         if (t_nxt < 0) break;
         ++j;
@@ -899,7 +902,6 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
         t_nxt = tile_at(j + 1);
         if (t_nxt >= 0) nxt = coord(t_nxt);
         pb ^= 1;
-        dma_rows(cur, pb);
       }
       wait_vmcnt<0>();  // no copy in flight when the workgroup ends
       return;
