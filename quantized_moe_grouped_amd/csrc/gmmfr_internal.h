@@ -66,9 +66,10 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
 
 // Workgroups per CU the GEMM variant is compiled for.
 int tile_occupancy(TileId id);
-// Whether the GEMM runs the continuous copy pipeline (int8 weights and at
-// least `stages` k-steps per tile) rather than the tile-by-tile loop.
-bool uses_continuous_pipeline(bool int4, int64_t k, int bk, int stages);
+// Whether the GEMM runs the continuous copy pipeline (int8 weights, tiles of
+// at least 64 rows and at least `stages` k-steps per tile) rather than the
+// tile-by-tile loop.
+bool uses_continuous_pipeline(bool int4, int64_t k, int bm, int bk, int stages);
 const char* tile_kernel_name(TileId id, bool int4, int64_t k);
 
 }  // namespace gmmfr

@@ -1240,7 +1240,11 @@ TileShape tile_shape(TileId id) {
 
 int tile_occupancy(TileId id) { return id == kTile256x256 ? 1 : 2; }
 
-bool uses_continuous_pipeline(bool int4, int64_t k, int bk, int stages) { return !int4 && k / bk >= stages; }
+// The 32-row tile serves groups of a few dozen rows, where the dynamic
+// per-XCD queues of the tile-by-tile loop balance the uneven groups better.
+bool uses_continuous_pipeline(bool int4, int64_t k, int bm, int bk, int stages) {
+  return !int4 && bm >= 64 && k / bk >= stages;
+}
 
 const char* tile_kernel_name(TileId id, bool int4, int64_t k) {
   static const char* names[kNumTiles][3] = {
@@ -1250,7 +1254,7 @@ const char* tile_kernel_name(TileId id, bool int4, int64_t k) {
       {"gmm_kernel<32,256,64,1x4,s3,i8>", "gmm_kernel<32,256,64,1x4,s3,i4>", "gmm_kernel<32,256,64,1x4,s3,i8,cont>"},
   };
   const TileShape ts = tile_shape(id);
-  return names[(int)id][int4 ? 1 : uses_continuous_pipeline(int4, k, ts.bk, 3) ? 2 : 0];
+  return names[(int)id][int4 ? 1 : uses_continuous_pipeline(int4, k, ts.bm, ts.bk, 3) ? 2 : 0];
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1280,14 +1284,14 @@ template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC>
 static void launch_gemm(const KParams& kp, bool int4, int grid, hipStream_t s) {
   const dim3 gd(grid), bd(kThreads);
   const size_t dyn = ((size_t)(2 * kp.e + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
-  const bool cont = uses_continuous_pipeline(int4, kp.k, BK, ST);
+  const bool cont = uses_continuous_pipeline(int4, kp.k, BM, BK, ST);
   if (kp.combine == kCombineOrdered) {
     if (int4) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineOrdered, false>), gd, bd, dyn, s, kp);
-    else if (cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineOrdered, true>), gd, bd, dyn, s, kp);
+    else if (BM >= 64 && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineOrdered, (BM >= 64)>), gd, bd, dyn, s, kp);
     else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineOrdered, false>), gd, bd, dyn, s, kp);
   } else {
     if (int4) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineAtomic, false>), gd, bd, dyn, s, kp);
-    else if (cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineAtomic, true>), gd, bd, dyn, s, kp);
+    else if (BM >= 64 && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineAtomic, (BM >= 64)>), gd, bd, dyn, s, kp);
     else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineAtomic, false>), gd, bd, dyn, s, kp);
   }
 }

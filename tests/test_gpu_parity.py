@@ -77,6 +77,12 @@ CASES = {
     "int4_counts_many_tiles": dict(seed=7, m=1100, k=320, n=800 - 800 % 32, e=3, int4=True, group_list_type=1,
                                    output_bs=500),
     "full_int8_range": dict(seed=8, m=333, k=448, n=400, e=3, lo=-128, hi=127, output_bs=100),
+    # k >= 192: the continuous copy pipeline (tiles of 64 or more rows)
+    "long_k_no_factors": dict(seed=15, m=600, k=320, n=272, e=3, with_scale=False, with_pts=False,
+                              with_logit=False, with_row_index=False, output_bs=600),
+    "long_k_i32_index_bf16_shared": dict(seed=16, m=900, k=256, n=528, e=4, row_index_dtype=np.int32,
+                                         scale_bf16=True, output_bs=450, bsdp=100, shared_offset=350),
+    "long_k_many_empty": dict(seed=17, m=1500, k=192, n=256, e=40, empty_frac=0.7, output_bs=400, uncovered=20),
 }
 
 
