@@ -317,8 +317,13 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int KK = BK / 32;
-  constexpr int CPR_A = BK / 16, CPR_B = BN / 16;
-  constexpr int A_BYTES = BM * BK, B_BYTES = BK * BN;
+  // int4 weights in the continuous pipeline stay packed in LDS (two columns
+  // per byte); the tile-by-tile loop unpacks them on the way in.
+  constexpr bool PACKED = INT4 && CONT;
+  constexpr bool REGB4 = INT4 && !CONT;  // int4 B through registers
+  constexpr int B_ROW = PACKED ? BN / 2 : BN;  // bytes of one k-row of a B stage
+  constexpr int CPR_A = BK / 16, CPR_B = B_ROW / 16;
+  constexpr int A_BYTES = BM * BK, B_BYTES = BK * B_ROW;
   constexpr int A_SLOTS = BM * CPR_A, B_SLOTS = BK * CPR_B;
   constexpr int NWAVES = kThreads / 64;
   constexpr int A_INSTR = (A_SLOTS + kThreads - 1) / kThreads;    // per thread (whole waves may idle)
@@ -328,12 +333,12 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   // vector-memory ops one thread issues per stage (DMA and int4 register
   // loads).  When A_SLOTS is not a multiple of the block, the last A copy is
   // issued by the first waves only; those waves wait with the larger count.
-  constexpr int B_ISSUED = INT4 ? B4_PER : B_INSTR;
+  constexpr int B_ISSUED = REGB4 ? B4_PER : B_INSTR;
   constexpr int LOADS_FULL = A_INSTR + B_ISSUED;
   constexpr int LOADS_SHORT = A_INSTR - 1 + B_ISSUED;
   static_assert(WAVES_M * WAVES_N == NWAVES, "4 waves");
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-  static_assert(BN >= 256, "B swizzle needs 16 chunks per row");
+  static_assert(BN >= 256, "B swizzle needs 16 chunks per row (8 when packed)");
   static_assert(A_SLOTS % 64 == 0 && B_SLOTS % 64 == 0, "whole waves per copy");
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
   static_assert((STAGES - 2) * LOADS_FULL < 64, "vmcnt range");
@@ -365,6 +370,11 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   const int lane = tid & 63;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int lane_id = lane, wave_m = wm, wave_n = wn;
+  // B chunk swizzle.  Packed rows hold 8 chunks: a 32-lane pass of the
+  // transpose read covers 8 k-rows x 2 adjacent chunks, two rows per bank
+  // cycle; 2((r >> 1) & 3) sends the rows of one parity to 8 distinct chunk
+  // positions.
+  auto swzb = [](int r) { return PACKED ? ((r >> 1) & 3) << 1 : swz_b(r); };
   const bool a_full = ((A_INSTR - 1) * NWAVES + wave) * 64 < A_SLOTS;  // wave-uniform
   const int64_t k = p.k, n = p.n;
   const int ktiles = (int)(k / BK);
@@ -385,12 +395,12 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   // ---- per-tile copy sources: wave-uniform bases plus per-lane offsets
   // (bytes, < BM*k resp. < BK*n, so they fit in 32 bits)
   uint32_t a_off[A_INSTR];
-  uint32_t b_off[INT4 ? 1 : B_INSTR];
+  uint32_t b_off[REGB4 ? 1 : B_INSTR];
   const int8_t* a_base = p.x1;
   const int8_t* b_base = nullptr;
   const uint32_t* w4 = nullptr;
   int64_t b4_col0 = 0;
-  uint4 b4reg[INT4 ? B4_PER : 1];
+  uint4 b4reg[REGB4 ? B4_PER : 1];
   auto set_sources = [&](const TileCoord& c) {
     a_base = p.x1 + c.row0 * k;
 #pragma unroll
@@ -400,14 +410,16 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       const int64_t row = min(c.row0 + r, p.m - 1);  // rows past the group: loaded, never stored
       a_off[q] = (uint32_t)((row - c.row0) * k + ((cpos ^ swz_a<BK>(r)) * 16));
     }
-    if constexpr (!INT4) {
-      b_base = (const int8_t*)p.x2 + (int64_t)c.g * k * n + c.col0;
+    if constexpr (!REGB4) {
+      // bytes of one weight row, and the tile's first byte in it
+      const int64_t rowb = PACKED ? n / 2 : n, col0b = PACKED ? c.col0 / 2 : c.col0;
+      b_base = (const int8_t*)p.x2 + (int64_t)c.g * k * rowb + col0b;
 #pragma unroll
       for (int q = 0; q < B_INSTR; ++q) {
         const int slot = (q * NWAVES + wave) * 64 + lane;
         const int r = (slot / CPR_B) % BK, cpos = slot % CPR_B;
-        const int64_t col = min(c.col0 + ((cpos ^ swz_b(r)) * 16), n - 16);  // past n: loaded, never stored
-        b_off[q] = (uint32_t)((int64_t)r * n + (col - c.col0));
+        const int64_t colb = min(col0b + ((cpos ^ swzb(r)) * 16), rowb - 16);  // past n: loaded, never stored
+        b_off[q] = (uint32_t)((int64_t)r * rowb + (colb - col0b));
       }
     } else {
       w4 = (const uint32_t*)p.x2 + (int64_t)c.g * k * (n / 8);
@@ -425,7 +437,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     }
   };
   auto issue_b8 = [&](int sc, int kt) {
-    const int8_t* base = b_base + (int64_t)kt * BK * n;
+    const int8_t* base = b_base + (int64_t)kt * BK * (PACKED ? n / 2 : n);
 #pragma unroll
     for (int q = 0; q < B_INSTR; ++q) {
       const int slot_base = (q * NWAVES + wave) * 64;
@@ -465,7 +477,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   // stage fill: int4 issues its register loads first so that waiting for
   // them later does not also wait for the A copy issued after them
   auto issue_stage = [&](int sc, int kt) {
-    if constexpr (INT4) {
+    if constexpr (REGB4) {
       fetch_b4(kt);
       issue_a(sc, kt);
     } else {
@@ -479,7 +491,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     for (int st = 0; st < STAGES - 1; ++st) {
       if (st < ktiles) {
         issue_stage(st, st);
-        if constexpr (INT4) store_b4(st);
+        if constexpr (REGB4) store_b4(st);
       }
     }
   };
@@ -564,23 +576,44 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   auto read_b = [&](int sc, int kk, int j, v4i& dst) {
     const int r = kk * 32 + (lane >> 5) * 16 + ((lane & 15) >> 1);
     const int col = wn * WTN + j * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-    const int8_t* a0 = sB + sc * B_BYTES + r * BN + (((col >> 4) ^ swz_b(r)) << 4) + (col & 15);
+    const int8_t* a0 = sB + sc * B_BYTES + r * B_ROW + (((col >> 4) ^ swzb(r)) << 4) + (col & 15);
     const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0));
-    const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0 + 8 * BN));  // same swizzle
+    const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0 + 8 * B_ROW));  // same swizzle
     dst = v4i{lo.x, lo.y, hi.x, hi.y};
   };
-  auto load_frags = [&](int sc, int kk, v4i (&af)[FM], v4i (&bf)[FN]) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) read_a(sc, kk, i, af[i]);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) read_b(sc, kk, j, bf[j]);
+  // Packed int4: one transpose read of byte column b gives, per k, the
+  // nibbles of columns 2b (low) and 2b+1 (high); masking each byte yields
+  // the two int8 fragments of 16 * w (exact, the accumulator is shifted back
+  // at the end).  Pair g covers tile columns 64 g .. 64 g + 63 of the wave:
+  // fragment 2g holds the even ones, 2g+1 the odd ones (MFMA column l of
+  // either is tile column 64 g + 2 l + parity).
+  auto read_b4pair = [&](int sc, int kk, int g, v4i& even, v4i& odd) {
+    const int r = kk * 32 + (lane >> 5) * 16 + ((lane & 15) >> 1);
+    const int colb = wn * (WTN / 2) + g * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+    const int8_t* a0 = sB + sc * B_BYTES + r * B_ROW + (((colb >> 4) ^ swzb(r)) << 4) + (colb & 15);
+    const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0));
+    const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0 + 8 * B_ROW));
+    const v4i w = {lo.x, lo.y, hi.x, hi.y};
+    even = (w << 4) & (int)0xF0F0F0F0;
+    odd = w & (int)0xF0F0F0F0;
   };
-  // Copy items of one stage refill: the A copies, then the B copies (int8
-  // weights) -- int4 weights take one register-load item first instead.
-  constexpr int N_COPY = INT4 ? A_INSTR + 1 : A_INSTR + B_INSTR;
+  // read item r of a substep into fragment set (af, bf): A first, then B
+  constexpr int NREAD = FM + (PACKED ? FN / 2 : FN);
+  auto read_item = [&](auto r_, int sc, int kk, v4i (&af)[FM], v4i (&bf)[FN]) {
+    constexpr int r = decltype(r_)::value;
+    if constexpr (r < FM) read_a(sc, kk, r, af[r]);
+    else if constexpr (PACKED) read_b4pair(sc, kk, r - FM, bf[2 * (r - FM)], bf[2 * (r - FM) + 1]);
+    else read_b(sc, kk, r - FM, bf[r - FM]);
+  };
+  auto load_frags = [&](int sc, int kk, v4i (&af)[FM], v4i (&bf)[FN]) {
+    static_for<0, NREAD>([&](auto r_) { read_item(r_, sc, kk, af, bf); });
+  };
+  // Copy items of one stage refill: the A copies, then the B copies --
+  // int4 weights through registers take one register-load item first instead.
+  constexpr int N_COPY = REGB4 ? A_INSTR + 1 : A_INSTR + B_INSTR;
   auto copy_item = [&](auto d_, int sc, int kt) {
     constexpr int d = decltype(d_)::value;
-    if constexpr (INT4) {
+    if constexpr (REGB4) {
       if constexpr (d == 0) {
         fetch_b4(kt);
       } else {
@@ -600,7 +633,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       constexpr int q = d - A_INSTR;
       const int sb = (q * NWAVES + wave) * 64;
       if ((B_SLOTS % (NWAVES * 64)) == 0 || sb < B_SLOTS)
-        lds_dma16_sv(b_base + (int64_t)kt * BK * n, b_off[q],
+        lds_dma16_sv(b_base + (int64_t)kt * BK * (PACKED ? n / 2 : n), b_off[q],
                      __builtin_amdgcn_readfirstlane(lds_addr(sB + sc * B_BYTES + sb * 16)));
     }
   };
@@ -642,7 +675,8 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   // full-tile epilogue (FM*FN*16 separate stores, counted at half in case the
   // compiler pairs some) the wait allows that many more; after any other
   // epilogue only the later stages (younger than stage 0 either way).
-  constexpr int FAST_STORES = COMBINE == kCombineOrdered ? FM * FN * 8 : 0;
+  // separate stores of the ordered full-tile epilogue, counted at half
+  constexpr int FAST_STORES = COMBINE == kCombineOrdered ? FM * FN * (PACKED ? 4 : 8) : 0;
   constexpr int W0_FULL = (STAGES - 2) * LOADS_FULL + FAST_STORES < 63 ? (STAGES - 2) * LOADS_FULL + FAST_STORES : 63;
   constexpr int W0_SHORT = (STAGES - 2) * LOADS_SHORT + FAST_STORES < 63 ? (STAGES - 2) * LOADS_SHORT + FAST_STORES : 63;
   bool stores_counted = false;  // the previous epilogue took the ordered full-tile path
@@ -682,10 +716,15 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     int wm = wave_m, wn = wave_n;
     asm volatile("" : "+v"(lane), "+s"(wm), "+s"(wn));
     const bool dump = p.acc_out != nullptr;
+    // Tile-local column of this lane in MFMA block j (packed int4: block 2g
+    // holds the even columns of pair g, block 2g+1 the odd ones).
+    auto col_of = [&](int j) {
+      return PACKED ? wn * WTN + (j >> 1) * 64 + 2 * (lane & 31) + (j & 1) : wn * WTN + j * 32 + (lane & 31);
+    };
     float scv[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int cl = wn * WTN + j * 32 + (lane & 31);
+      const int cl = col_of(j);
       scv[j] = 1.0f;
       if (p.scale) {
         if (p.scale_bf16) {
@@ -732,10 +771,11 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     const bool fast_epi = e_valid == BM && e_col0 + BN <= n && n < (int64_t(1) << 28) && !dump;
     if (fast_epi) {
       // Full tile: no per-element guards.  Ordered stores use one wave-uniform
-      // row base and one 32-bit lane offset for every store.
-      const uint32_t lane_off = (uint32_t)((lane >> 5) * 4 * n + (lane & 31));
+      // row base and one 32-bit lane offset for every store (packed int4: the
+      // even and odd blocks of a pair go out together, 8 bytes per lane).
+      const uint32_t lane_off = (uint32_t)((lane >> 5) * 4 * n + (PACKED ? 2 : 1) * (lane & 31));
       float* wave_y = p.y + (e_row0 + wm * WTM) * n + e_col0 + wn * WTN;
-      float* wave_out = p.out + e_col0 + wn * WTN + (lane & 31);
+      float* wave_out = p.out + e_col0 + wn * WTN + (PACKED ? 2 : 1) * (lane & 31);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -748,9 +788,18 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               float* rowp = wave_y + (int64_t)(i * 32 + q * 8 + u) * n;
+              if constexpr (PACKED) {
+                typedef float v2f __attribute__((ext_vector_type(2)));
 #pragma unroll
-              for (int j = 0; j < FN; ++j)
-                __builtin_nontemporal_store(value(i, j, q * 4 + u, Pv[u], Lv[u]), (rowp + j * 32) + lane_off);
+                for (int g = 0; g < FN / 2; ++g)
+                  __builtin_nontemporal_store(
+                      v2f{value(i, 2 * g, q * 4 + u, Pv[u], Lv[u]), value(i, 2 * g + 1, q * 4 + u, Pv[u], Lv[u])},
+                      (v2f*)((rowp + g * 64) + lane_off));
+              } else {
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                  __builtin_nontemporal_store(value(i, j, q * 4 + u, Pv[u], Lv[u]), (rowp + j * 32) + lane_off);
+              }
             }
           } else {
 #pragma unroll
@@ -759,7 +808,8 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
               float* base = wave_out + (int64_t)Dv[u] * n;
 #pragma unroll
               for (int j = 0; j < FN; ++j)
-                __hip_atomic_fetch_add(base + j * 32, value(i, j, q * 4 + u, Pv[u], Lv[u]), __ATOMIC_RELAXED,
+                __hip_atomic_fetch_add(base + (PACKED ? (j >> 1) * 64 + (j & 1) : j * 32),
+                                       value(i, j, q * 4 + u, Pv[u], Lv[u]), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
             }
           }
@@ -767,10 +817,13 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       }
     } else {
       // Partial tile (group tail or n tail) or accumulator dump: guarded.
-      const int64_t lane_col = e_col0 + wn * WTN + (lane & 31);
+      int64_t colj[FN];
       bool col_ok[FN];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) col_ok[j] = lane_col + j * 32 < n;
+      for (int j = 0; j < FN; ++j) {
+        colj[j] = e_col0 + col_of(j);
+        col_ok[j] = colj[j] < n;
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -785,10 +838,10 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
             if (lr >= e_valid) continue;
             float* base;
             if constexpr (COMBINE == kCombineOrdered) {
-              base = p.y + (e_row0 + lr) * n + lane_col;
+              base = p.y + (e_row0 + lr) * n;
             } else {
               if (Dv[u] < 0) continue;
-              base = p.out + (int64_t)Dv[u] * n + lane_col;
+              base = p.out + (int64_t)Dv[u] * n;
             }
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
@@ -796,13 +849,13 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
               if (dump) {
                 int32_t a = acc_elem<(FM * FN * 16 > 128)>(acc[i][j][q * 4 + u]);
                 if constexpr (INT4) a >>= 4;
-                p.acc_out[(e_row0 + lr) * n + lane_col + j * 32] = a;
+                p.acc_out[(e_row0 + lr) * n + colj[j]] = a;
               }
               const float v = value(i, j, q * 4 + u, Pv[u], Lv[u]);
               if constexpr (COMBINE == kCombineOrdered)
-                __builtin_nontemporal_store(v, base + j * 32);
+                __builtin_nontemporal_store(v, base + colj[j]);
               else
-                __hip_atomic_fetch_add(base + j * 32, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(base + colj[j], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
           }
         }
@@ -822,7 +875,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   // MFMAs of substep 0 with the reads of substep 1; the wait for the next
   // k-step's copies and a barrier; the MFMAs of substep 1 with the refill of
   // the buffer just released and the next k-step's substep-0 reads.
-  static_assert(!CONT || (!INT4 && KK == 2), "continuous pipeline: int8 weights, two substeps per stage");
+  static_assert(!CONT || KK == 2, "continuous pipeline: two substeps per stage");
   if constexpr (CONT) {
     {
       const int G = gridDim.x;
@@ -854,12 +907,8 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       v16i acc[FM][FN];
       auto kstep = [&](int kt, int fill_ks) {
         const int stage_next = stage + 1 == STAGES ? 0 : stage + 1;
-        auto rd1 = [&](auto r_) {
-          constexpr int r = decltype(r_)::value;
-          if constexpr (r < FM) read_a(stage, 1, r, af[1][r]);
-          else read_b(stage, 1, r - FM, bf[1][r - FM]);
-        };
-        mfma_step(af[0], bf[0], acc, std::integral_constant<int, 0>{}, std::integral_constant<int, FM + FN>{},
+        auto rd1 = [&](auto r_) { read_item(r_, stage, 1, af[1], bf[1]); };
+        mfma_step(af[0], bf[0], acc, std::integral_constant<int, 0>{}, std::integral_constant<int, NREAD>{},
                   no_copy, rd1);
         // the next k-step's copies have landed and every wave holds this
         // stage's fragments; after the first k-step of a tile the previous
@@ -873,12 +922,8 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
         }
         lds_barrier();
         auto cp = [&](auto d_) { copy_item(d_, stage, fill_ks); };
-        auto rd0 = [&](auto r_) {
-          constexpr int r = decltype(r_)::value;
-          if constexpr (r < FM) read_a(stage_next, 0, r, af[0][r]);
-          else read_b(stage_next, 0, r - FM, bf[0][r - FM]);
-        };
-        mfma_step(af[1], bf[1], acc, std::integral_constant<int, N_COPY>{}, std::integral_constant<int, FM + FN>{},
+        auto rd0 = [&](auto r_) { read_item(r_, stage_next, 0, af[0], bf[0]); };
+        mfma_step(af[1], bf[1], acc, std::integral_constant<int, N_COPY>{}, std::integral_constant<int, NREAD>{},
                   cp, rd0);
         stage = stage_next;
       };
@@ -1243,18 +1288,24 @@ int tile_occupancy(TileId id) { return id == kTile256x256 ? 1 : 2; }
 // The 32-row tile serves groups of a few dozen rows, where the dynamic
 // per-XCD queues of the tile-by-tile loop balance the uneven groups better.
 bool uses_continuous_pipeline(bool int4, int64_t k, int bm, int bk, int stages) {
-  return !int4 && bm >= 64 && k / bk >= stages;
+  (void)int4;
+  return bm >= 64 && k / bk >= stages;
 }
 
 const char* tile_kernel_name(TileId id, bool int4, int64_t k) {
-  static const char* names[kNumTiles][3] = {
-      {"gmm_kernel<256,256,64,2x2,s3,i8>", "gmm_kernel<256,256,64,2x2,s3,i4>", "gmm_kernel<256,256,64,2x2,s3,i8,cont>"},
-      {"gmm_kernel<128,256,64,2x2,s3,i8>", "gmm_kernel<128,256,64,2x2,s3,i4>", "gmm_kernel<128,256,64,2x2,s3,i8,cont>"},
-      {"gmm_kernel<64,256,64,1x4,s3,i8>", "gmm_kernel<64,256,64,1x4,s3,i4>", "gmm_kernel<64,256,64,1x4,s3,i8,cont>"},
-      {"gmm_kernel<32,256,64,1x4,s3,i8>", "gmm_kernel<32,256,64,1x4,s3,i4>", "gmm_kernel<32,256,64,1x4,s3,i8,cont>"},
+  static const char* names[kNumTiles][4] = {
+      {"gmm_kernel<256,256,64,2x2,s3,i8>", "gmm_kernel<256,256,64,2x2,s3,i4>", "gmm_kernel<256,256,64,2x2,s3,i8,cont>",
+       "gmm_kernel<256,256,64,2x2,s3,i4,cont>"},
+      {"gmm_kernel<128,256,64,2x2,s3,i8>", "gmm_kernel<128,256,64,2x2,s3,i4>", "gmm_kernel<128,256,64,2x2,s3,i8,cont>",
+       "gmm_kernel<128,256,64,2x2,s3,i4,cont>"},
+      {"gmm_kernel<64,256,64,1x4,s3,i8>", "gmm_kernel<64,256,64,1x4,s3,i4>", "gmm_kernel<64,256,64,1x4,s3,i8,cont>",
+       "gmm_kernel<64,256,64,1x4,s3,i4,cont>"},
+      {"gmm_kernel<32,256,64,1x4,s3,i8>", "gmm_kernel<32,256,64,1x4,s3,i4>", "gmm_kernel<32,256,64,1x4,s3,i8,cont>",
+       "gmm_kernel<32,256,64,1x4,s3,i4,cont>"},
   };
   const TileShape ts = tile_shape(id);
-  return names[(int)id][int4 ? 1 : uses_continuous_pipeline(int4, k, ts.bm, ts.bk, 3) ? 2 : 0];
+  const bool cont = uses_continuous_pipeline(int4, k, ts.bm, ts.bk, 3);
+  return names[(int)id][(int4 ? 1 : 0) + (cont ? 2 : 0)];
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1286,11 +1337,13 @@ static void launch_gemm(const KParams& kp, bool int4, int grid, hipStream_t s) {
   const size_t dyn = ((size_t)(2 * kp.e + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
   const bool cont = uses_continuous_pipeline(int4, kp.k, BM, BK, ST);
   if (kp.combine == kCombineOrdered) {
-    if (int4) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineOrdered, false>), gd, bd, dyn, s, kp);
+    if (int4 && BM >= 64 && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineOrdered, (BM >= 64)>), gd, bd, dyn, s, kp);
+    else if (int4) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineOrdered, false>), gd, bd, dyn, s, kp);
     else if (BM >= 64 && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineOrdered, (BM >= 64)>), gd, bd, dyn, s, kp);
     else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineOrdered, false>), gd, bd, dyn, s, kp);
   } else {
-    if (int4) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineAtomic, false>), gd, bd, dyn, s, kp);
+    if (int4 && BM >= 64 && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineAtomic, (BM >= 64)>), gd, bd, dyn, s, kp);
+    else if (int4) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineAtomic, false>), gd, bd, dyn, s, kp);
     else if (BM >= 64 && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineAtomic, (BM >= 64)>), gd, bd, dyn, s, kp);
     else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineAtomic, false>), gd, bd, dyn, s, kp);
   }
