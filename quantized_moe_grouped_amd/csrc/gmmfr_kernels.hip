@@ -362,6 +362,13 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t s_ridx[2][2 * BM];
   __shared__ __attribute__((aligned(16))) uint32_t s_scale[2][BN];
 
+  // An absent pertokenScale or logit reads as 1.0 from LDS (the copies below
+  // skip it), so the epilogue reads row factors without branching; the
+  // barriers of the table build publish the fill.
+  if (!p.pertoken)
+    for (int i = threadIdx.x; i < 2 * BM; i += kThreads) (&s_pts[0][0])[i] = 1.0f;
+  if (!p.logit)
+    for (int i = threadIdx.x; i < 2 * BM; i += kThreads) (&s_logit[0][0])[i] = 1.0f;
   build_group_table(p, BM, s_ends, s_tile_pre, s_scan);
   const int total_tiles = s_tile_pre[p.e];
 
@@ -510,7 +517,8 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     return (int64_t)c.g * n + min(c.col0 + q, n - 1);
   };
   // Register path (the k-loop with a tile prologue): loads now, LDS writes later.
-  uint32_t fr_pts = 0, fr_logit = 0, fr_ridx0 = 0, fr_ridx1 = 0, fr_scale = 0;
+  // (an absent pertokenScale or logit stays 1.0)
+  uint32_t fr_pts = 0x3F800000u, fr_logit = 0x3F800000u, fr_ridx0 = 0, fr_ridx1 = 0, fr_scale = 0;
   auto fetch_rows = [&](const TileCoord& c) {
     if (tid < BM) {
       if (p.pertoken) fr_pts = ((const uint32_t*)p.pertoken)[row_word_src(c, tid, 1)];
@@ -675,7 +683,6 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   // full-tile epilogue (FM*FN*16 separate stores, counted at half in case the
   // compiler pairs some) the wait allows that many more; after any other
   // epilogue only the later stages (younger than stage 0 either way).
-  // separate stores of the ordered full-tile epilogue, counted at half
   constexpr int FAST_STORES = COMBINE == kCombineOrdered ? FM * FN * (PACKED ? 4 : 8) : 0;
   constexpr int W0_FULL = (STAGES - 2) * LOADS_FULL + FAST_STORES < 63 ? (STAGES - 2) * LOADS_FULL + FAST_STORES : 63;
   constexpr int W0_SHORT = (STAGES - 2) * LOADS_SHORT + FAST_STORES < 63 ? (STAGES - 2) * LOADS_SHORT + FAST_STORES : 63;
@@ -735,12 +742,14 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
         }
       }
     }
-    const float4 ones = make_float4(1.f, 1.f, 1.f, 1.f);
-    auto factors = [&](int lr0, float (&Pv)[4], float (&Lv)[4], int (&Dv)[4]) {
-      const float4 P4 = p.pertoken ? *(const float4*)(&s_pts[pb][lr0]) : ones;
-      const float4 L4 = p.logit ? *(const float4*)(&s_logit[pb][lr0]) : ones;
-      Pv[0] = P4.x; Pv[1] = P4.y; Pv[2] = P4.z; Pv[3] = P4.w;
-      Lv[0] = L4.x; Lv[1] = L4.y; Lv[2] = L4.z; Lv[3] = L4.w;
+    // Rows lr0 .. lr0+3 of the tile: their pertokenScale and logit (1.0
+    // where absent, filled at the start), and in atomic mode their
+    // destinations.
+    auto row_factors = [&](int lr0, float4& P4, float4& L4) {
+      P4 = *(const float4*)(&s_pts[pb][lr0]);
+      L4 = *(const float4*)(&s_logit[pb][lr0]);
+    };
+    auto dests = [&](int lr0, int (&Dv)[4]) {
       if constexpr (COMBINE == kCombineAtomic) {
         // destination of each row from the raw rowIndex words; -1 when
         // outside [0, outputBS)
@@ -757,6 +766,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
         Dv[0] = Dv[1] = Dv[2] = Dv[3] = -1;
       }
     };
+    auto first_row = [&](int i, int q) { return wm * WTM + i * 32 + q * 8 + (lane >> 5) * 4; };
     // One element: int32 -> fp32 (round to nearest even), then the three
     // factors in the oracle's order.
     auto value = [&](int i, int j, int r, float pv, float lv) {
@@ -776,14 +786,20 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       const uint32_t lane_off = (uint32_t)((lane >> 5) * 4 * n + (PACKED ? 2 : 1) * (lane & 31));
       float* wave_y = p.y + (e_row0 + wm * WTM) * n + e_col0 + wn * WTN;
       float* wave_out = p.out + e_col0 + wn * WTN + (PACKED ? 2 : 1) * (lane & 31);
+      // the row factors of the next group of four rows are read one group
+      // ahead, so no LDS wait sits between the stores
+      float4 P_next, L_next;
+      row_factors(first_row(0, 0), P_next, L_next);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int lr0 = wm * WTM + i * 32 + q * 8 + (lane >> 5) * 4;
-          float Pv[4], Lv[4];
+          const int lr0 = first_row(i, q);
+          const float4 P4 = P_next, L4 = L_next;
+          if (i * 4 + q + 1 < FM * 4) row_factors(first_row((i * 4 + q + 1) / 4, (i * 4 + q + 1) % 4), P_next, L_next);
+          const float Pv[4] = {P4.x, P4.y, P4.z, P4.w}, Lv[4] = {L4.x, L4.y, L4.z, L4.w};
           int Dv[4];
-          factors(lr0, Pv, Lv, Dv);
+          dests(lr0, Dv);
           if constexpr (COMBINE == kCombineOrdered) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -828,10 +844,12 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int lr0 = wm * WTM + i * 32 + q * 8 + (lane >> 5) * 4;
-          float Pv[4], Lv[4];
+          const int lr0 = first_row(i, q);
+          float4 P4, L4;
+          row_factors(lr0, P4, L4);
+          const float Pv[4] = {P4.x, P4.y, P4.z, P4.w}, Lv[4] = {L4.x, L4.y, L4.z, L4.w};
           int Dv[4];
-          factors(lr0, Pv, Lv, Dv);
+          dests(lr0, Dv);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int lr = lr0 + u;
