@@ -118,7 +118,10 @@ def make_args(x1, x2, group_list, out, *, scale=None, pertoken_scale=None, logit
               tuning_config: Optional[Sequence[int]] = None, bias=None, offset=None,
               antiquant_scale=None, antiquant_offset=None, transpose_x1: bool = False,
               transpose_x2: bool = False):
-    """Build the C argument struct.  Returns (args, keepalive)."""
+    """Build the C argument struct.  Returns (args, keepalive): the struct holds
+    raw device pointers, so keep `keepalive` (which references every tensor
+    passed, and the host tuning array) alive until the call has been enqueued
+    and the stream has reached it."""
     a = Args()
     a.x1 = _desc(x1)
     a.x2 = _desc(x2)
@@ -141,11 +144,13 @@ def make_args(x1, x2, group_list, out, *, scale=None, pertoken_scale=None, logit
     a.transpose_x2 = int(bool(transpose_x2))
     a.deterministic = int(bool(deterministic))
     a.combine = COMBINE[combine]
-    keep = None
+    tuning = None
     if tuning_config:
-        keep = (ctypes.c_int64 * len(tuning_config))(*[int(v) for v in tuning_config])
-        a.tuning_config = ctypes.cast(keep, ctypes.POINTER(ctypes.c_int64))
+        tuning = (ctypes.c_int64 * len(tuning_config))(*[int(v) for v in tuning_config])
+        a.tuning_config = ctypes.cast(tuning, ctypes.POINTER(ctypes.c_int64))
         a.tuning_config_len = len(tuning_config)
+    keep = (x1, x2, group_list, out, scale, pertoken_scale, logit, row_index, shared_input, acc_out, bias, offset,
+            antiquant_scale, antiquant_offset, tuning)
     return a, keep
 
 

@@ -919,6 +919,16 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       else wait_vmcnt<(STAGES - 1) * LOADS_SHORT>();
       lds_barrier();
       v4i af[2][FM], bf[2][FN];
+      // The k-steps run at a raised wave priority and the epilogue at the
+      // base one: where the two workgroups of a CU share a SIMD, the one in
+      // its k-loop issues its MFMAs and copies ahead of the other's epilogue.
+      // Not for a workgroup's last two tiles, whose epilogues end the launch
+      // (there the fair order finishes first).
+      auto raise_priority = [&](int jj) {
+        if (tile_at(jj + 2) >= 0) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      };
+      raise_priority(0);
       load_frags(0, 0, af[0], bf[0]);
       int stage = 0;
       bool prev_fast = false;
@@ -958,9 +968,11 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
         // the next tile's row and column inputs go to the other buffer before
         // this tile's stores fill the copy queue
         if (t_nxt >= 0) dma_rows(nxt, pb ^ 1);
+        __builtin_amdgcn_s_setprio(0);
         prev_fast = epilogue(cur, pb, acc);
         if (t_nxt < 0) break;
         ++j;
+        raise_priority(j);
         cur = nxt;
         t_nxt = tile_at(j + 1);
         if (t_nxt >= 0) nxt = coord(t_nxt);

@@ -214,3 +214,27 @@ def test_stage_two_rejects_before_any_launch():
     a.group_list_type = 5
     st = B.lib().gmm_finalize_routing(ctypes.byref(a), None, 0, None)
     assert st == B.ERR_ATTR
+
+
+def test_make_args_keepalive_holds_every_tensor():
+    """The argument struct holds raw pointers; the keepalive it comes with must
+    keep each tensor passed alive (temporaries included)."""
+    import gc
+    import weakref
+    import torch
+    tmp = torch.zeros(16, dtype=torch.int64)
+    ref = weakref.ref(tmp)
+    x1 = torch.zeros((4, 64), dtype=torch.int8)
+    x2 = torch.zeros((1, 64, 16), dtype=torch.int8)
+    out = torch.zeros((4, 16), dtype=torch.float32)
+    a, keep = B.make_args(x1, x2, torch.tensor([4], dtype=torch.int64), out, row_index=tmp,
+                          logit=torch.ones(4, dtype=torch.float32), tuning_config=[0, 64])
+    del tmp
+    gc.collect()
+    assert ref() is not None, "a tensor passed to make_args was freed while its keepalive lives"
+    assert a.row_index.data == ref().data_ptr()
+    assert any(t is not None and getattr(t, "data_ptr", None) and t.data_ptr() == a.logit.data for t in keep)
+    assert a.tuning_config_len == 2 and a.tuning_config[1] == 64
+    del keep
+    gc.collect()
+    assert ref() is None
