@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--tile-m", type=int, default=0, choices=[0, 32, 64, 128, 256],
                     help="force the GEMM tile height (0 = the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--transpose-x2", action="store_true",
+                    help="int8 weights given transposed, (e,n,k) (the operator's transposed-x2 form)")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="rows in the oracle sample (0 = auto)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (torch copy_) 5 times: the reference kernel whose "
@@ -102,7 +104,7 @@ def cpu_baseline(p, rows_wanted: int):
                   p.scale_bf16, None if p.pertoken_scale is None else p.pertoken_scale[idx],
                   None if p.logit is None else p.logit[idx], np.cumsum(take).astype(np.int64), 0,
                   None if p.row_index is None else p.row_index[idx], p.shared_input, p.shared_input_offset,
-                  p.output_bs, p.seed, take)
+                  p.output_bs, p.seed, take, getattr(p, "x2_transposed", False))
     oracle.load()
     t0 = time.perf_counter()
     oracle.run(q, want_acc=False)
@@ -160,6 +162,8 @@ def main():
         return
     print(f"[bench] generating {args.config} seed {args.seed}", file=sys.stderr, flush=True)
     p = W.make_config(args.config, args.seed)
+    if args.transpose_x2:
+        p = W.with_transposed_weights(p)
     dev = "cuda"
 
     def T(a):
@@ -176,7 +180,8 @@ def main():
     cargs, keep = B.make_args(x1, x2, gl, out, scale=scale, pertoken_scale=pts, logit=logit, row_index=ri,
                               shared_input=shared, shared_input_offset=p.shared_input_offset,
                               group_list_type=p.group_list_type, deterministic=args.deterministic,
-                              combine=args.combine, tuning_config=[0, args.tile_m] if args.tile_m else None)
+                              combine=args.combine, tuning_config=[0, args.tile_m] if args.tile_m else None,
+                              transpose_x2=args.transpose_x2)
     plan = B.plan(cargs)
     ws_bytes = B.workspace_size(cargs)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -226,6 +231,7 @@ def main():
         "data": "synthetic (seeded generator; random int8 weights/activations, routing and scales of the stated shapes)",
         "config": {"workload": p.name, "tokens": p.output_bs, "top_k": p.m // max(p.output_bs, 1), "m": p.m,
                    "e": p.e, "k": p.k, "n": p.n, "weights": "int4" if p.x2_int4 else "int8",
+                   "weights_layout": "(e,n,k)" if p.x2_transposed else "(e,k,n)",
                    "output_bs": p.output_bs, "shared_rows": p.bsdp, "combine": plan["combine"],
                    "deterministic": bool(args.deterministic), "seed": args.seed,
                    "ops_per_step": ops, "algorithmic_bytes_per_step": abytes,

@@ -93,7 +93,9 @@ typedef struct {
   /* x1: INT8 (m,k), rows sorted by expert.                              required */
   gmmfr_tensor x1;
   /* x2: INT8 (e,k,n); or INT32 (e,k,n/8) holding eight int4 per word, column
-   * 8w+t in bits [4t,4t+4); or INT4 (e,k,n), the same bytes.          required */
+   * 8w+t in bits [4t,4t+4); or INT4 (e,k,n), the same bytes.  With
+   * transpose_x2 = 1: INT8 (e,n,k), weight column j of expert g at
+   * x2[g][j][:] (parameter notes: (e,n,k) when transposed).          required */
   gmmfr_tensor x2;
   /* scale: FLOAT32 or BFLOAT16 (e,1,n) per-channel dequant scale.      optional
    * (INT64 scale is listed by the operator without an encoding: UNSUPPORTED) */
@@ -122,7 +124,8 @@ typedef struct {
   int64_t shared_input_offset;  /* >= 0, offset + bsdp <= outputBS               */
   int64_t output_bs;            /* rows of out                                   */
   int32_t transpose_x1;         /* must be 0                                     */
-  int32_t transpose_x2;         /* must be 0                                     */
+  int32_t transpose_x2;         /* 0: x2 is (e,k,n); 1: INT8 x2 is (e,n,k) (int4
+                                   weights transposed: UNSUPPORTED)              */
   int32_t deterministic;        /* 0: order of additions unspecified (default);
                                    1: bit-reproducible, rows folded in ascending
                                    source order onto the seed                    */

@@ -7,6 +7,11 @@ and the pure-Python brute force (brute.py) is a second, independent reading.
 
 Entry points take any object with the fields of
 ``quantized_moe_grouped_amd.workloads.Problem`` (duck-typed, nothing imported).
+
+Transposed weights ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2", parameter
+notes: x2 is (e,k,n), or (e,n,k) when transposed): int8 x2 given as (e,n,k)
+means W_g = x2[g] transposed; the wrapper transposes it back with numpy and the
+C oracle computes from W as for untransposed weights.
 """
 from __future__ import annotations
 
@@ -78,7 +83,12 @@ def _c_problem(p, keep):
         return a
 
     x1 = arr(p.x1, np.int8)
-    x2 = arr(p.x2, np.int32 if p.x2_int4 else np.int8)
+    if getattr(p, "x2_transposed", False):
+        if p.x2_int4:
+            raise OracleError(2)
+        x2 = arr(np.transpose(np.asarray(p.x2), (0, 2, 1)), np.int8)  # (e,n,k) -> W (e,k,n)
+    else:
+        x2 = arr(p.x2, np.int32 if p.x2_int4 else np.int8)
     scale = None
     if p.scale is not None:
         scale = arr(p.scale, np.uint16 if p.scale_bf16 else np.float32)

@@ -19,6 +19,8 @@ def _bf16(bits: int) -> np.float32:
 
 
 def _weight(p, g: int, kk: int, j: int) -> int:
+    if getattr(p, "x2_transposed", False):  # int8 (e,n,k): column j holds k contiguous values
+        return int(p.x2[g, j, kk])
     if not p.x2_int4:
         return int(p.x2[g, kk, j])
     word = int(p.x2[g, kk, j // 8]) & 0xFFFFFFFF

@@ -21,6 +21,7 @@ using namespace gmmfr;
 struct Derived {
   int64_t m, k, n, e, bsdp, output_bs;
   bool int4;
+  bool trans_b;  // int8 weights given transposed, (e,n,k)
   bool scale_bf16;
   bool row_index_i32;
 };
@@ -71,7 +72,12 @@ int validate(const gmmfr_args* a, Derived* d) {
 
   // attributes
   if (a->group_list_type != 0 && a->group_list_type != 1) return GMMFR_ERR_ATTR;
-  if (a->transpose_x1 != 0 || a->transpose_x2 != 0) return GMMFR_ERR_ATTR;
+  if (a->transpose_x1 != 0) return GMMFR_ERR_ATTR;
+  if (a->transpose_x2 != 0 && a->transpose_x2 != 1) return GMMFR_ERR_ATTR;
+  // transposed weights: (e,n,k) int8 (parameter notes: x2 (e,k,n), or (e,n,k)
+  // when transposed); the int4 form is only given untransposed here
+  const bool trans_b = a->transpose_x2 == 1;
+  if (trans_b && a->x2.dtype != GMMFR_DT_INT8) return GMMFR_ERR_UNSUPPORTED;
   if (a->deterministic != 0 && a->deterministic != 1) return GMMFR_ERR_ATTR;
   if (a->combine != GMMFR_COMBINE_AUTO && a->combine != GMMFR_COMBINE_ATOMIC && a->combine != GMMFR_COMBINE_ORDERED)
     return GMMFR_ERR_ATTR;
@@ -87,10 +93,11 @@ int validate(const gmmfr_args* a, Derived* d) {
   if (a->x2.ndim != 3) return GMMFR_ERR_SHAPE;
   const int64_t e = a->x2.dims[0];
   int64_t n;
-  if (a->x2.dtype == GMMFR_DT_INT32) n = a->x2.dims[2] * 8;
+  if (trans_b) n = a->x2.dims[1];
+  else if (a->x2.dtype == GMMFR_DT_INT32) n = a->x2.dims[2] * 8;
   else n = a->x2.dims[2];
   const bool int4 = a->x2.dtype != GMMFR_DT_INT8;
-  if (a->x2.dims[1] != k) return GMMFR_ERR_SHAPE;
+  if (a->x2.dims[trans_b ? 2 : 1] != k) return GMMFR_ERR_SHAPE;
   if (m < 0 || m >= (int64_t(1) << 31)) return GMMFR_ERR_SHAPE;
   if (e < 1 || e > kMaxExperts) return GMMFR_ERR_SHAPE;
   if (k < 64 || k > 65536 || k % 64 != 0) return GMMFR_ERR_SHAPE;
@@ -130,6 +137,7 @@ int validate(const gmmfr_args* a, Derived* d) {
     d->bsdp = bsdp;
     d->output_bs = obs;
     d->int4 = int4;
+    d->trans_b = trans_b;
     d->scale_bf16 = present(a->scale) && a->scale.dtype == GMMFR_DT_BFLOAT16;
     d->row_index_i32 = present(a->row_index) && a->row_index.dtype == GMMFR_DT_INT32;
   }
@@ -210,6 +218,7 @@ LaunchArgs to_launch(const gmmfr_args* a, const Derived& d) {
   l.scale_bf16 = d.scale_bf16;
   l.row_index_i32 = d.row_index_i32;
   l.int4 = d.int4;
+  l.trans_b = d.trans_b;
   l.bsdp = d.bsdp;
   l.shared_offset = present(a->shared_input) ? a->shared_input_offset : 0;
   l.output_bs = d.output_bs;
@@ -261,7 +270,7 @@ static int run_stage2(const gmmfr_args* args, void* workspace, size_t workspace_
   if (log_enabled())
     std::fprintf(stderr, "[gmmfr] m=%lld k=%lld n=%lld e=%lld combine=%s %s grid=%d ws=%zu\n", (long long)d.m,
                  (long long)d.k, (long long)d.n, (long long)d.e, plan.combine == kCombineOrdered ? "ordered" : "atomic",
-                 tile_kernel_name(plan.tile, d.int4, d.k), plan.grid, plan.workspace_bytes);
+                 tile_kernel_name(plan.tile, d.int4, d.k, d.trans_b), plan.grid, plan.workspace_bytes);
   const int err = launch_all(to_launch(args, d), plan, workspace, stream, gemm_events);
   return err == 0 ? GMMFR_OK : GMMFR_ERR_HIP;
 }
@@ -293,7 +302,7 @@ int gmm_finalize_routing_plan(const gmmfr_args* args, gmmfr_plan_info* info) {
   info->grid = plan.grid;
   info->int4_weights = d.int4 ? 1 : 0;
   info->workspace_bytes = (int64_t)plan.workspace_bytes;
-  std::snprintf(info->gemm_kernel, sizeof(info->gemm_kernel), "%s", tile_kernel_name(plan.tile, d.int4, d.k));
+  std::snprintf(info->gemm_kernel, sizeof(info->gemm_kernel), "%s", tile_kernel_name(plan.tile, d.int4, d.k, d.trans_b));
   return GMMFR_OK;
 }
 

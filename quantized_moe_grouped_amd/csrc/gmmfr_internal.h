@@ -27,7 +27,7 @@ TileShape tile_shape(TileId id);
 // Everything a launch needs; pointers are device addresses.
 struct LaunchArgs {
   const int8_t* x1;
-  const void* x2;            // int8 (e,k,n) or packed int4 (e,k,n/8) words
+  const void* x2;            // int8 (e,k,n), int8 (e,n,k) when trans_b, or packed int4 (e,k,n/8) words
   const void* scale;         // f32 / bf16 (e,1,n) or nullptr
   const float* pertoken;     // (m) or nullptr
   const float* logit;        // (m) or nullptr
@@ -42,6 +42,7 @@ struct LaunchArgs {
   int32_t scale_bf16;
   int32_t row_index_i32;
   int32_t int4;
+  int32_t trans_b;           // int8 weights given as (e,n,k)
   int64_t bsdp, shared_offset, output_bs;
 };
 
@@ -70,6 +71,6 @@ int tile_occupancy(TileId id);
 // at least 64 rows and at least `stages` k-steps per tile) rather than the
 // tile-by-tile loop.
 bool uses_continuous_pipeline(bool int4, int64_t k, int bm, int bk, int stages);
-const char* tile_kernel_name(TileId id, bool int4, int64_t k);
+const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b);
 
 }  // namespace gmmfr

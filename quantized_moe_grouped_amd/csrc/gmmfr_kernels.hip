@@ -311,8 +311,10 @@ __device__ __forceinline__ TileCoord tile_coord(const KParams& p, const int32_t*
 }
 
 // CONT selects the continuous copy pipeline (int8 weights, k / BK >= STAGES,
-// checked by the host) over the tile-by-tile loop.
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int OCC, bool INT4, int COMBINE, bool CONT>
+// checked by the host) over the tile-by-tile loop.  TRANSB: int8 weights
+// given transposed, (e,n,k) with k contiguous.
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int OCC, bool INT4, int COMBINE, bool CONT,
+          bool TRANSB>
 __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -321,10 +323,15 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   // per byte); the tile-by-tile loop unpacks them on the way in.
   constexpr bool PACKED = INT4 && CONT;
   constexpr bool REGB4 = INT4 && !CONT;  // int4 B through registers
-  constexpr int B_ROW = PACKED ? BN / 2 : BN;  // bytes of one k-row of a B stage
+  // Transposed int8 weights: a B stage is laid out like an A stage, one LDS
+  // row of BK bytes per weight column, and read like it.
+  constexpr bool TB = TRANSB;
+  static_assert(!(TRANSB && INT4), "transposed weights are int8");
+  constexpr int B_ROW = TB ? BK : (PACKED ? BN / 2 : BN);  // bytes of one LDS row of a B stage
+  constexpr int B_LROWS = TB ? BN : BK;                    // LDS rows of a B stage
   constexpr int CPR_A = BK / 16, CPR_B = B_ROW / 16;
-  constexpr int A_BYTES = BM * BK, B_BYTES = BK * B_ROW;
-  constexpr int A_SLOTS = BM * CPR_A, B_SLOTS = BK * CPR_B;
+  constexpr int A_BYTES = BM * BK, B_BYTES = B_LROWS * B_ROW;
+  constexpr int A_SLOTS = BM * CPR_A, B_SLOTS = B_LROWS * CPR_B;
   constexpr int NWAVES = kThreads / 64;
   constexpr int A_INSTR = (A_SLOTS + kThreads - 1) / kThreads;    // per thread (whole waves may idle)
   constexpr int B_INSTR = (B_SLOTS + kThreads - 1) / kThreads;
@@ -417,7 +424,17 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       const int64_t row = min(c.row0 + r, p.m - 1);  // rows past the group: loaded, never stored
       a_off[q] = (uint32_t)((row - c.row0) * k + ((cpos ^ swz_a<BK>(r)) * 16));
     }
-    if constexpr (!REGB4) {
+    if constexpr (TB) {
+      // weight column col is k contiguous bytes; columns past n: loaded, never stored
+      b_base = (const int8_t*)p.x2 + ((int64_t)c.g * n + c.col0) * k;
+#pragma unroll
+      for (int q = 0; q < B_INSTR; ++q) {
+        const int slot = (q * NWAVES + wave) * 64 + lane;
+        const int r = (slot / CPR_B) % BN, cpos = slot % CPR_B;
+        const int64_t col = min(c.col0 + r, n - 1);
+        b_off[q] = (uint32_t)((col - c.col0) * k + ((cpos ^ swz_a<BK>(r)) * 16));
+      }
+    } else if constexpr (!REGB4) {
       // bytes of one weight row, and the tile's first byte in it
       const int64_t rowb = PACKED ? n / 2 : n, col0b = PACKED ? c.col0 / 2 : c.col0;
       b_base = (const int8_t*)p.x2 + (int64_t)c.g * k * rowb + col0b;
@@ -444,7 +461,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     }
   };
   auto issue_b8 = [&](int sc, int kt) {
-    const int8_t* base = b_base + (int64_t)kt * BK * (PACKED ? n / 2 : n);
+    const int8_t* base = b_base + (int64_t)kt * BK * (TB ? 1 : (PACKED ? n / 2 : n));
 #pragma unroll
     for (int q = 0; q < B_INSTR; ++q) {
       const int slot_base = (q * NWAVES + wave) * 64;
@@ -582,12 +599,19 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     dst = *(const LDS_PTR(v4i))(sA + sc * A_BYTES + r * BK + ((c ^ swz_a<BK>(r)) << 4));
   };
   auto read_b = [&](int sc, int kk, int j, v4i& dst) {
-    const int r = kk * 32 + (lane >> 5) * 16 + ((lane & 15) >> 1);
-    const int col = wn * WTN + j * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-    const int8_t* a0 = sB + sc * B_BYTES + r * B_ROW + (((col >> 4) ^ swzb(r)) << 4) + (col & 15);
-    const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0));
-    const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0 + 8 * B_ROW));  // same swizzle
-    dst = v4i{lo.x, lo.y, hi.x, hi.y};
+    if constexpr (TB) {
+      // column-major stage: the same lane layout as the A fragment
+      const int rc = wn * WTN + j * 32 + (lane & 31);
+      const int cc = kk * 2 + (lane >> 5);
+      dst = *(const LDS_PTR(v4i))(sB + sc * B_BYTES + rc * BK + ((cc ^ swz_a<BK>(rc)) << 4));
+    } else {
+      const int r = kk * 32 + (lane >> 5) * 16 + ((lane & 15) >> 1);
+      const int col = wn * WTN + j * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+      const int8_t* a0 = sB + sc * B_BYTES + r * B_ROW + (((col >> 4) ^ swzb(r)) << 4) + (col & 15);
+      const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0));
+      const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0 + 8 * B_ROW));  // same swizzle
+      dst = v4i{lo.x, lo.y, hi.x, hi.y};
+    }
   };
   // Packed int4: one transpose read of byte column b gives, per k, the
   // nibbles of columns 2b (low) and 2b+1 (high); masking each byte yields
@@ -641,7 +665,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       constexpr int q = d - A_INSTR;
       const int sb = (q * NWAVES + wave) * 64;
       if ((B_SLOTS % (NWAVES * 64)) == 0 || sb < B_SLOTS)
-        lds_dma16_sv(b_base + (int64_t)kt * BK * (PACKED ? n / 2 : n), b_off[q],
+        lds_dma16_sv(b_base + (int64_t)kt * BK * (TB ? 1 : (PACKED ? n / 2 : n)), b_off[q],
                      __builtin_amdgcn_readfirstlane(lds_addr(sB + sc * B_BYTES + sb * 16)));
     }
   };
@@ -1322,19 +1346,25 @@ bool uses_continuous_pipeline(bool int4, int64_t k, int bm, int bk, int stages) 
   return bm >= 64 && k / bk >= stages;
 }
 
-const char* tile_kernel_name(TileId id, bool int4, int64_t k) {
-  static const char* names[kNumTiles][4] = {
+const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b) {
+  // per tile: i8, i4, i8 cont, i4 cont, i8 transposed weights, i8 cont transposed weights
+  static const char* names[kNumTiles][6] = {
       {"gmm_kernel<256,256,64,2x2,s3,i8>", "gmm_kernel<256,256,64,2x2,s3,i4>", "gmm_kernel<256,256,64,2x2,s3,i8,cont>",
-       "gmm_kernel<256,256,64,2x2,s3,i4,cont>"},
+       "gmm_kernel<256,256,64,2x2,s3,i4,cont>", "gmm_kernel<256,256,64,2x2,s3,i8,tb>",
+       "gmm_kernel<256,256,64,2x2,s3,i8,cont,tb>"},
       {"gmm_kernel<128,256,64,2x2,s3,i8>", "gmm_kernel<128,256,64,2x2,s3,i4>", "gmm_kernel<128,256,64,2x2,s3,i8,cont>",
-       "gmm_kernel<128,256,64,2x2,s3,i4,cont>"},
+       "gmm_kernel<128,256,64,2x2,s3,i4,cont>", "gmm_kernel<128,256,64,2x2,s3,i8,tb>",
+       "gmm_kernel<128,256,64,2x2,s3,i8,cont,tb>"},
       {"gmm_kernel<64,256,64,1x4,s3,i8>", "gmm_kernel<64,256,64,1x4,s3,i4>", "gmm_kernel<64,256,64,1x4,s3,i8,cont>",
-       "gmm_kernel<64,256,64,1x4,s3,i4,cont>"},
+       "gmm_kernel<64,256,64,1x4,s3,i4,cont>", "gmm_kernel<64,256,64,1x4,s3,i8,tb>",
+       "gmm_kernel<64,256,64,1x4,s3,i8,cont,tb>"},
       {"gmm_kernel<32,256,64,1x4,s3,i8>", "gmm_kernel<32,256,64,1x4,s3,i4>", "gmm_kernel<32,256,64,1x4,s3,i8,cont>",
-       "gmm_kernel<32,256,64,1x4,s3,i4,cont>"},
+       "gmm_kernel<32,256,64,1x4,s3,i4,cont>", "gmm_kernel<32,256,64,1x4,s3,i8,tb>",
+       "gmm_kernel<32,256,64,1x4,s3,i8,cont,tb>"},
   };
   const TileShape ts = tile_shape(id);
   const bool cont = uses_continuous_pipeline(int4, k, ts.bm, ts.bk, 3);
+  if (trans_b && !int4) return names[(int)id][cont ? 5 : 4];
   return names[(int)id][(int4 ? 1 : 0) + (cont ? 2 : 0)];
 }
 
@@ -1361,22 +1391,32 @@ Workspace workspace_layout(int64_t m, int64_t n, int64_t output_bs, bool ordered
   return w;
 }
 
+// The continuous pipeline exists for tiles of at least 64 rows.
+template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC, int COMB>
+static void launch_gemm_mode(const KParams& kp, bool int4, bool trans_b, bool cont, dim3 gd, dim3 bd, size_t dyn,
+                             hipStream_t s) {
+  constexpr bool C = BM >= 64;
+  if (int4) {
+    if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, COMB, C, false>), gd, bd, dyn, s, kp);
+    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, COMB, false, false>), gd, bd, dyn, s, kp);
+  } else if (trans_b) {
+    if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, C, true>), gd, bd, dyn, s, kp);
+    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, false, true>), gd, bd, dyn, s, kp);
+  } else {
+    if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, C, false>), gd, bd, dyn, s, kp);
+    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, false, false>), gd, bd, dyn, s, kp);
+  }
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC>
-static void launch_gemm(const KParams& kp, bool int4, int grid, hipStream_t s) {
+static void launch_gemm(const KParams& kp, bool int4, bool trans_b, int grid, hipStream_t s) {
   const dim3 gd(grid), bd(kThreads);
   const size_t dyn = ((size_t)(2 * kp.e + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
   const bool cont = uses_continuous_pipeline(int4, kp.k, BM, BK, ST);
-  if (kp.combine == kCombineOrdered) {
-    if (int4 && BM >= 64 && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineOrdered, (BM >= 64)>), gd, bd, dyn, s, kp);
-    else if (int4) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineOrdered, false>), gd, bd, dyn, s, kp);
-    else if (BM >= 64 && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineOrdered, (BM >= 64)>), gd, bd, dyn, s, kp);
-    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineOrdered, false>), gd, bd, dyn, s, kp);
-  } else {
-    if (int4 && BM >= 64 && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineAtomic, (BM >= 64)>), gd, bd, dyn, s, kp);
-    else if (int4) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineAtomic, false>), gd, bd, dyn, s, kp);
-    else if (BM >= 64 && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineAtomic, (BM >= 64)>), gd, bd, dyn, s, kp);
-    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineAtomic, false>), gd, bd, dyn, s, kp);
-  }
+  if (kp.combine == kCombineOrdered)
+    launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineOrdered>(kp, int4, trans_b, cont, gd, bd, dyn, s);
+  else
+    launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineAtomic>(kp, int4, trans_b, cont, gd, bd, dyn, s);
 }
 
 int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* stream, void* const* gemm_events) {
@@ -1437,10 +1477,10 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
       if (er != hipSuccess) return (int)er;
     }
     switch (plan.tile) {
-      case kTile256x256: launch_gemm<256, 256, 64, 2, 2, 3, 1>(kp, a.int4, plan.grid, s); break;
-      case kTile128x256: launch_gemm<128, 256, 64, 2, 2, 3, 2>(kp, a.int4, plan.grid, s); break;
-      case kTile64x256: launch_gemm<64, 256, 64, 1, 4, 3, 2>(kp, a.int4, plan.grid, s); break;
-      default: launch_gemm<32, 256, 64, 1, 4, 3, 2>(kp, a.int4, plan.grid, s); break;
+      case kTile256x256: launch_gemm<256, 256, 64, 2, 2, 3, 1>(kp, a.int4, a.trans_b, plan.grid, s); break;
+      case kTile128x256: launch_gemm<128, 256, 64, 2, 2, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;
+      case kTile64x256: launch_gemm<64, 256, 64, 1, 4, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;
+      default: launch_gemm<32, 256, 64, 1, 4, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;
     }
     if (gemm_events && gemm_events[1]) {
       const hipError_t er = hipEventRecord((hipEvent_t)gemm_events[1], s);

@@ -86,6 +86,7 @@ class Problem:
     output_bs: int
     seed: int = 0
     counts: Optional[np.ndarray] = None  # rows per expert (for statistics)
+    x2_transposed: bool = False          # True -> int8 x2 is given as (e,n,k)
 
     @property
     def bsdp(self) -> int:
@@ -273,3 +274,11 @@ def random_problem(seed: int, m: int, k: int, n: int, e: int, *,
     return Problem(f"random{seed}", m, k, n, e, x1, x2, int4, scale, scale_bf16 and with_scale,
                    pts, logit, _group_list(counts, group_list_type), group_list_type, ri,
                    shared, shared_offset, output_bs, seed, counts)
+
+
+def with_transposed_weights(p: Problem) -> Problem:
+    """The same problem with its int8 weights given transposed, (e,n,k)."""
+    if p.x2_int4 or p.x2_transposed:
+        raise ValueError("transposed weights are taken from an untransposed int8 problem")
+    return dataclasses.replace(p, x2=np.ascontiguousarray(np.transpose(p.x2, (0, 2, 1))), x2_transposed=True,
+                               name=p.name + "-tb")

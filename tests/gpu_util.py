@@ -33,7 +33,7 @@ def call(p, d, out, *, deterministic=False, combine="auto", acc=None, tuning_con
         scale=d["scale"], pertoken_scale=d["pertoken_scale"], logit=d["logit"], row_index=d["row_index"],
         shared_input=d["shared_input"], shared_input_offset=p.shared_input_offset if p.shared_input is not None else 0,
         group_list_type=p.group_list_type, deterministic=deterministic, combine=combine, acc_out=acc,
-        tuning_config=tuning_config, workspace=workspace)
+        tuning_config=tuning_config, workspace=workspace, transpose_x2=getattr(p, "x2_transposed", False))
 
 
 def run_gpu(p, d=None, *, deterministic=False, combine="auto", want_acc=False, tuning_config=None,

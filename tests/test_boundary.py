@@ -149,7 +149,10 @@ CASES = [
     ("shared_dtype", dict(shared_input=_fake(B.DT_FLOAT32, 128, 7168)), B.ERR_DTYPE),
     ("out_dtype", dict(out=_fake(B.DT_BFLOAT16, 256, 7168)), B.ERR_DTYPE),
     ("group_list_type", dict(group_list_type=2), B.ERR_ATTR),
-    ("transpose_x2", dict(transpose_x2=1), B.ERR_ATTR),
+    ("transpose_x2_value", dict(transpose_x2=2), B.ERR_ATTR),
+    ("transpose_x2_int4", dict(transpose_x2=1, x2=_fake(B.DT_INT32, 8, 7168, 256)), B.ERR_UNSUPPORTED),
+    ("transpose_x2_k_mismatch", dict(transpose_x2=1, x2=_fake(B.DT_INT8, 8, 7168, 1024)), B.ERR_SHAPE),
+    ("transpose_x2_untransposed_dims", dict(transpose_x2=1), B.ERR_SHAPE),
     ("transpose_x1", dict(transpose_x1=1), B.ERR_ATTR),
     ("det_with_atomic", dict(deterministic=1, combine=1), B.ERR_ATTR),
     ("k_mismatch", dict(x2=_fake(B.DT_INT8, 8, 1024, 7168)), B.ERR_SHAPE),
@@ -177,6 +180,17 @@ def test_stage_one_rejects(name, over, code):
     st, ws = _ws(a)
     assert st == code, (B.STATUS_NAMES.get(st), B.STATUS_NAMES.get(code))
     assert ws == 12345  # untouched on error
+
+
+def test_transposed_weights_accepted():
+    """x2 (e,n,k) with transpose_x2 = 1 (parameter notes: transposed x2)."""
+    a = _args()
+    a.transpose_x2 = 1
+    a.x2 = _fake(B.DT_INT8, 8, 7168, 2048)
+    assert _ws(a)[0] == B.OK
+    info = B.PlanInfo()
+    assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
+    assert info.gemm_kernel.decode().endswith(",tb>")
 
 
 def test_int4_shapes_accepted_and_checked():

@@ -92,6 +92,17 @@ def test_random_case_all_elements(name):
     _check_full(p, hints=(None, 8, 100, 300, (0, 256)))  # every tile variant
 
 
+# int8 weights given transposed, (e,n,k) (parameter notes: transposed x2)
+TB_CASES = ["ragged_n_shared", "counts_i32_bf16_uncovered", "many_empty_experts", "single_row", "full_int8_range",
+            "long_k_no_factors", "long_k_i32_index_bf16_shared", "long_k_many_empty"]
+
+
+@pytest.mark.parametrize("name", TB_CASES, ids=TB_CASES)
+def test_random_case_transposed_weights(name):
+    p = W.with_transposed_weights(W.random_problem(**CASES[name]))
+    _check_full(p, hints=(None, 8, 100, 300, (0, 256)))
+
+
 def test_zero_rows_gives_seed():
     p = W.random_problem(9, 0, 64, 64, 2, output_bs=20, bsdp=6, shared_offset=3)
     ref, _ = oracle.run(p)
@@ -189,8 +200,16 @@ def _sample_src(p, rng, count=48):
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "skewed", "int4", "prefill"])
 def test_named_workload(name):
+    _check_named(W.make_config(name, 0), name)
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_named_workload_transposed_weights(name):
+    _check_named(W.with_transposed_weights(W.make_config(name, 0)), name)
+
+
+def _check_named(p, name):
     import torch
-    p = W.make_config(name, 0)
     rng = np.random.default_rng(100)
     d = G.to_device(p)
     if name == "tiny":

@@ -238,6 +238,28 @@ def test_int4_equals_int8_with_small_values():
     assert (a == qa).all() and np.array_equal(o, qo)
 
 
+def test_transposed_weights_equal_untransposed():
+    """Weights given as (e,n,k) (parameter notes: transposed x2) compute the
+    same result as the (e,k,n) form; the brute force indexes the transposed
+    array directly, the C oracle receives it transposed back."""
+    p = W.random_problem(12, 70, 96, 48, 3, bsdp=8, output_bs=30)
+    q = W.with_transposed_weights(p)
+    assert q.x2.shape == (p.e, p.n, p.k) and q.x2_transposed
+    o, a = oracle.run(p)
+    qo, qa = oracle.run(q)
+    assert (a == qa).all() and np.array_equal(o, qo)
+    small = W.random_problem(13, 9, 32, 8, 2, bsdp=2, output_bs=6)
+    ts = W.with_transposed_weights(small)
+    bo, ba = brute.brute(ts)
+    so, sa = oracle.run(small)
+    assert (sa.astype(np.int64) == ba).all() and np.array_equal(so, bo)
+    # reading the (e,n,k) bytes as (e,k,n), i.e. dropping the transpose, changes the result
+    wrong = copy.deepcopy(q)
+    wrong.x2_transposed = False
+    wo, _ = oracle.run(wrong)
+    assert not np.array_equal(wo, o)
+
+
 def test_missing_factors_equal_unit_factors():
     p = _base()
     q = copy.deepcopy(p)
