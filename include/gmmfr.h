@@ -14,6 +14,13 @@
  *   (the order (acc * deqScale) * perTokenScale is the one spelled out by
  *   the worked example of "matmul支持pertoken量化模式", ATB per-token quant
  *   linear; the routing weight is applied last).
+ *   MxA8W4 mode ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2", Atlas 350
+ *   notes on MxA8W4 quantisation): x1 FP8 E4M3, x2 FP4 E2M1 given as (e,n,k),
+ *   and one E8M0 block scale per 32 k for each row of x1 (pertokenScale) and
+ *   each weight column (scale):
+ *       acc[i][j] = sum_b 2^(pts[i][b]-127) * 2^(scale[g][j][b]-127) * sum_{kk in b} x1[i][kk] * x2[g][j][kk]
+ *   accumulated in fp32 by the matrix core (order unspecified), then
+ *       y[i][j] = acc[i][j] * logit[i].
  *   The output out (outputBS,n) fp32 starts at +0.0 with rows
  *   [sharedInputOffset, sharedInputOffset + bsdp) set to the widened bf16
  *   sharedInput, and every covered row i is added into out[rowIndex[i]].
@@ -67,7 +74,10 @@ typedef enum {
   GMMFR_DT_INT32 = 3,
   GMMFR_DT_INT64 = 4,
   GMMFR_DT_FLOAT32 = 5,
-  GMMFR_DT_BFLOAT16 = 6
+  GMMFR_DT_BFLOAT16 = 6,
+  GMMFR_DT_FLOAT8_E4M3FN = 7,  /* 1 sign, 4 exponent (bias 7), 3 mantissa; no inf; 0x7F/0xFF NaN */
+  GMMFR_DT_FLOAT4_E2M1X2 = 8,  /* two FP4 E2M1 per byte, low nibble first (values 0,.5,1,1.5,2,3,4,6 and negatives) */
+  GMMFR_DT_FLOAT8_E8M0 = 9     /* power-of-two scale 2^(b-127) per byte; 255 NaN */
 } gmmfr_dtype;
 
 /* A dense, row-major, contiguous device tensor.  data == NULL means "absent",
@@ -90,20 +100,27 @@ typedef enum {
 
 /* Arguments.  Names follow the operator's parameter list. */
 typedef struct {
-  /* x1: INT8 (m,k), rows sorted by expert.                              required */
+  /* x1: INT8 (m,k), rows sorted by expert; FLOAT8_E4M3FN (m,k) selects the
+   * MxA8W4 mode (Atlas 350 notes), with the other inputs as marked MX.  required */
   gmmfr_tensor x1;
   /* x2: INT8 (e,k,n); or INT32 (e,k,n/8) holding eight int4 per word, column
    * 8w+t in bits [4t,4t+4); or INT4 (e,k,n), the same bytes.  With
    * transpose_x2 = 1: INT8 (e,n,k), weight column j of expert g at
-   * x2[g][j][:] (parameter notes: (e,n,k) when transposed).          required */
+   * x2[g][j][:] (parameter notes: (e,n,k) when transposed).
+   * MX: FLOAT4_E2M1X2 (e,n,k/2), i.e. (e,n,k) two per byte along k, with
+   * transpose_x2 = 1.                                                  required */
   gmmfr_tensor x2;
   /* scale: FLOAT32 or BFLOAT16 (e,1,n) per-channel dequant scale.      optional
-   * (INT64 scale is listed by the operator without an encoding: UNSUPPORTED) */
+   * (INT64 scale is listed by the operator without an encoding: UNSUPPORTED)
+   * MX: FLOAT8_E8M0 (e,n,k/64,2), the block scale of x2 for each 32 k of each
+   * weight column.                                                     required */
   gmmfr_tensor scale;
   /* bias, offset, antiquantScale, antiquantOffset: reserved by the operator
    * ("pass a null pointer"); must be absent, else UNSUPPORTED.                 */
   gmmfr_tensor bias, offset, antiquant_scale, antiquant_offset;
-  /* pertokenScale: FLOAT32 (m).                                        optional */
+  /* pertokenScale: FLOAT32 (m).                                        optional
+   * MX: FLOAT8_E8M0 (m,k/64,2), the block scale of x1 for each 32 k of each
+   * row.                                                                required */
   gmmfr_tensor pertoken_scale;
   /* groupList: INT64 (e); type 0 cumulative ends, type 1 counts.       required */
   gmmfr_tensor group_list;
@@ -112,12 +129,12 @@ typedef struct {
   /* logit: FLOAT32 (m) routing weight of each row.                     optional */
   gmmfr_tensor logit;
   /* rowIndex: INT64 or INT32 (m), destination row of each source row;
-   * absent means the identity.                                         optional */
+   * absent means the identity.  MX: INT64 only.                        optional */
   gmmfr_tensor row_index;
   /* out: FLOAT32 (outputBS,n); every element is written.               required */
   gmmfr_tensor out;
   /* acc_out: INT32 (m,n) copy of the int32 accumulators of covered rows
-   * (other rows untouched).  A diagnostic for tests.                   optional */
+   * (other rows untouched).  A diagnostic for tests.  MX: UNSUPPORTED. optional */
   gmmfr_tensor acc_out;
 
   int64_t group_list_type;      /* 0 or 1                                        */

@@ -19,6 +19,7 @@ STATUS_NAMES = {0: "OK", 1: "NULLPTR", 2: "DTYPE", 3: "SHAPE", 4: "ATTR", 5: "UN
                 7: "WORKSPACE", 8: "HIP"}
 # element types (gmmfr_dtype)
 DT_NONE, DT_INT8, DT_INT4, DT_INT32, DT_INT64, DT_FLOAT32, DT_BFLOAT16 = range(7)
+DT_FLOAT8_E4M3FN, DT_FLOAT4_E2M1X2, DT_FLOAT8_E8M0 = 7, 8, 9
 COMBINE = {"auto": 0, "atomic": 1, "ordered": 2}
 
 EXPORTED = ("gmm_finalize_routing_workspace", "gmm_finalize_routing", "gmm_finalize_routing_profiled",
@@ -93,6 +94,12 @@ def _dtype_code(t, int4_packed: bool = False) -> int:
         return DT_FLOAT32
     if t.dtype == torch.bfloat16:
         return DT_BFLOAT16
+    if t.dtype == torch.float8_e4m3fn:
+        return DT_FLOAT8_E4M3FN
+    if t.dtype == torch.float4_e2m1fn_x2:
+        return DT_FLOAT4_E2M1X2
+    if t.dtype == torch.float8_e8m0fnu:
+        return DT_FLOAT8_E8M0
     raise TypeError(f"unsupported tensor dtype {t.dtype}")
 
 

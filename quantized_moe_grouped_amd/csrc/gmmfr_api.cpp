@@ -22,6 +22,7 @@ struct Derived {
   int64_t m, k, n, e, bsdp, output_bs;
   bool int4;
   bool trans_b;  // int8 weights given transposed, (e,n,k)
+  bool mx;       // MxA8W4: FP8 x1, FP4 x2 (e,n,k), E8M0 block scales
   bool scale_bf16;
   bool row_index_i32;
 };
@@ -37,12 +38,102 @@ bool present(const gmmfr_tensor& t) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-bool dims_are(const gmmfr_tensor& t, int nd, int64_t d0, int64_t d1 = -1, int64_t d2 = -1) {
+bool dims_are(const gmmfr_tensor& t, int nd, int64_t d0, int64_t d1 = -1, int64_t d2 = -1, int64_t d3 = -1) {
   if (t.ndim != nd) return false;
-  const int64_t want[3] = {d0, d1, d2};
+  const int64_t want[4] = {d0, d1, d2, d3};
   for (int i = 0; i < nd; ++i)
     if (t.dims[i] != want[i]) return false;
   return true;
+}
+
+// Attribute rules common to both data paths.
+int check_attributes(const gmmfr_args* a) {
+  if (a->group_list_type != 0 && a->group_list_type != 1) return GMMFR_ERR_ATTR;
+  if (a->deterministic != 0 && a->deterministic != 1) return GMMFR_ERR_ATTR;
+  if (a->combine != GMMFR_COMBINE_AUTO && a->combine != GMMFR_COMBINE_ATOMIC && a->combine != GMMFR_COMBINE_ORDERED)
+    return GMMFR_ERR_ATTR;
+  if (a->deterministic == 1 && a->combine == GMMFR_COMBINE_ATOMIC) return GMMFR_ERR_ATTR;
+  if (a->tuning_config_len < 0 || (a->tuning_config_len > 0 && !a->tuning_config)) return GMMFR_ERR_ATTR;
+  if (a->tuning_config_len > 1 && a->tuning_config[1] != 0 && a->tuning_config[1] != 32 &&
+      a->tuning_config[1] != 64 && a->tuning_config[1] != 128 && a->tuning_config[1] != 256)
+    return GMMFR_ERR_ATTR;
+  return GMMFR_OK;
+}
+
+// out (outputBS,n), sharedInput placement and the alignment of every present
+// base pointer, common to both data paths.
+int check_output_and_alignment(const gmmfr_args* a, int64_t n, int64_t* bsdp) {
+  const int64_t obs = a->output_bs;
+  if (obs < 1 || obs >= (int64_t(1) << 31)) return GMMFR_ERR_SHAPE;
+  if (!dims_are(a->out, 2, obs, n)) return GMMFR_ERR_SHAPE;
+  *bsdp = 0;
+  if (present(a->shared_input)) {
+    if (a->shared_input.ndim != 2 || a->shared_input.dims[1] != n) return GMMFR_ERR_SHAPE;
+    *bsdp = a->shared_input.dims[0];
+    // bsdp <= outputBS and sharedInputOffset + bsdp <= outputBS (Atlas 350 common constraints)
+    if (*bsdp < 0 || *bsdp > obs) return GMMFR_ERR_ATTR;
+    if (a->shared_input_offset < 0 || a->shared_input_offset + *bsdp > obs) return GMMFR_ERR_ATTR;
+  } else if (a->shared_input_offset < 0) {
+    return GMMFR_ERR_ATTR;
+  }
+  const gmmfr_tensor* all[] = {&a->x1, &a->x2, &a->scale, &a->pertoken_scale, &a->group_list, &a->shared_input,
+                               &a->logit, &a->row_index, &a->out, &a->acc_out};
+  for (const gmmfr_tensor* t : all)
+    if (present(*t) && !aligned16(t->data)) return GMMFR_ERR_ALIGN;
+  return GMMFR_OK;
+}
+
+// MxA8W4 ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2", Atlas 350 notes on
+// the MxA8W4 quantisation: x2 (e,n,k) with transposeX2 fixed true,
+// pertokenScale required with shape (m, ceil(k/64), 2), scale shape
+// (e, n, ceil(k/64), 2), k % 32 == 0, n % 32 == 0; rowIndex INT64 only).
+// Reading of the lost dtype table: x1 FLOAT8_E4M3FN, x2 FLOAT4_E2M1 two per
+// byte along k, both scales FLOAT8_E8M0 (one per 32 k).  Ours: k % 128 == 0.
+int validate_mx(const gmmfr_args* a, Derived* d) {
+  if (!present(a->pertoken_scale) || !present(a->scale)) return GMMFR_ERR_NULLPTR;
+  if (a->x2.dtype != GMMFR_DT_FLOAT4_E2M1X2) return GMMFR_ERR_DTYPE;
+  if (a->pertoken_scale.dtype != GMMFR_DT_FLOAT8_E8M0 || a->scale.dtype != GMMFR_DT_FLOAT8_E8M0)
+    return GMMFR_ERR_DTYPE;
+  if (a->group_list.dtype != GMMFR_DT_INT64) return GMMFR_ERR_DTYPE;
+  if (present(a->shared_input) && a->shared_input.dtype != GMMFR_DT_BFLOAT16) return GMMFR_ERR_DTYPE;
+  if (present(a->logit) && a->logit.dtype != GMMFR_DT_FLOAT32) return GMMFR_ERR_DTYPE;
+  if (present(a->row_index) && a->row_index.dtype != GMMFR_DT_INT64) return GMMFR_ERR_DTYPE;
+  if (a->out.dtype != GMMFR_DT_FLOAT32) return GMMFR_ERR_DTYPE;
+  if (present(a->acc_out)) return GMMFR_ERR_UNSUPPORTED;  // no integer accumulator on this path
+
+  if (const int st = check_attributes(a)) return st;
+  if (a->transpose_x1 != 0 || a->transpose_x2 != 1) return GMMFR_ERR_ATTR;
+
+  if (a->x1.ndim != 2 || a->x2.ndim != 3) return GMMFR_ERR_SHAPE;
+  const int64_t m = a->x1.dims[0], k = a->x1.dims[1];
+  const int64_t e = a->x2.dims[0], n = a->x2.dims[1];
+  if (a->x2.dims[2] * 2 != k) return GMMFR_ERR_SHAPE;
+  if (m < 0 || m >= (int64_t(1) << 31)) return GMMFR_ERR_SHAPE;
+  if (e < 1 || e > kMaxExperts) return GMMFR_ERR_SHAPE;
+  if (k < 128 || k > 65536 || k % 128 != 0) return GMMFR_ERR_SHAPE;
+  if (n < 32 || n % 32 != 0) return GMMFR_ERR_SHAPE;
+  if (n > (int64_t(1) << 24) || m * n >= (int64_t(1) << 40)) return GMMFR_ERR_SHAPE;
+  if (!dims_are(a->pertoken_scale, 3, m, k / 64, 2)) return GMMFR_ERR_SHAPE;
+  if (!dims_are(a->scale, 4, e, n, k / 64, 2)) return GMMFR_ERR_SHAPE;
+  if (!dims_are(a->group_list, 1, e)) return GMMFR_ERR_SHAPE;
+  if (present(a->logit) && !dims_are(a->logit, 1, m)) return GMMFR_ERR_SHAPE;
+  if (present(a->row_index) && !dims_are(a->row_index, 1, m)) return GMMFR_ERR_SHAPE;
+  int64_t bsdp = 0;
+  if (const int st = check_output_and_alignment(a, n, &bsdp)) return st;
+  if (d) {
+    d->m = m;
+    d->k = k;
+    d->n = n;
+    d->e = e;
+    d->bsdp = bsdp;
+    d->output_bs = a->output_bs;
+    d->int4 = false;
+    d->trans_b = true;
+    d->mx = true;
+    d->scale_bf16 = false;
+    d->row_index_i32 = false;
+  }
+  return GMMFR_OK;
 }
 
 // Rules, in the order they are checked.  Operator rules cite
@@ -56,6 +147,7 @@ int validate(const gmmfr_args* a, Derived* d) {
   if (present(a->bias) || present(a->offset) || present(a->antiquant_scale) || present(a->antiquant_offset))
     return GMMFR_ERR_UNSUPPORTED;
   if (present(a->scale) && a->scale.dtype == GMMFR_DT_INT64) return GMMFR_ERR_UNSUPPORTED;
+  if (a->x1.dtype == GMMFR_DT_FLOAT8_E4M3FN) return validate_mx(a, d);
 
   // element types
   if (a->x1.dtype != GMMFR_DT_INT8) return GMMFR_ERR_DTYPE;
@@ -71,21 +163,13 @@ int validate(const gmmfr_args* a, Derived* d) {
   if (present(a->acc_out) && a->acc_out.dtype != GMMFR_DT_INT32) return GMMFR_ERR_DTYPE;
 
   // attributes
-  if (a->group_list_type != 0 && a->group_list_type != 1) return GMMFR_ERR_ATTR;
+  if (const int st = check_attributes(a)) return st;
   if (a->transpose_x1 != 0) return GMMFR_ERR_ATTR;
   if (a->transpose_x2 != 0 && a->transpose_x2 != 1) return GMMFR_ERR_ATTR;
   // transposed weights: (e,n,k) int8 (parameter notes: x2 (e,k,n), or (e,n,k)
   // when transposed); the int4 form is only given untransposed here
   const bool trans_b = a->transpose_x2 == 1;
   if (trans_b && a->x2.dtype != GMMFR_DT_INT8) return GMMFR_ERR_UNSUPPORTED;
-  if (a->deterministic != 0 && a->deterministic != 1) return GMMFR_ERR_ATTR;
-  if (a->combine != GMMFR_COMBINE_AUTO && a->combine != GMMFR_COMBINE_ATOMIC && a->combine != GMMFR_COMBINE_ORDERED)
-    return GMMFR_ERR_ATTR;
-  if (a->deterministic == 1 && a->combine == GMMFR_COMBINE_ATOMIC) return GMMFR_ERR_ATTR;
-  if (a->tuning_config_len < 0 || (a->tuning_config_len > 0 && !a->tuning_config)) return GMMFR_ERR_ATTR;
-  if (a->tuning_config_len > 1 && a->tuning_config[1] != 0 && a->tuning_config[1] != 32 &&
-      a->tuning_config[1] != 64 && a->tuning_config[1] != 128 && a->tuning_config[1] != 256)
-    return GMMFR_ERR_ATTR;
 
   // shapes
   if (a->x1.ndim != 2) return GMMFR_ERR_SHAPE;
@@ -108,26 +192,10 @@ int validate(const gmmfr_args* a, Derived* d) {
   if (!dims_are(a->group_list, 1, e)) return GMMFR_ERR_SHAPE;
   if (present(a->logit) && !dims_are(a->logit, 1, m)) return GMMFR_ERR_SHAPE;
   if (present(a->row_index) && !dims_are(a->row_index, 1, m)) return GMMFR_ERR_SHAPE;
-  const int64_t obs = a->output_bs;
-  if (obs < 1 || obs >= (int64_t(1) << 31)) return GMMFR_ERR_SHAPE;
-  if (!dims_are(a->out, 2, obs, n)) return GMMFR_ERR_SHAPE;
   if (present(a->acc_out) && !dims_are(a->acc_out, 2, m, n)) return GMMFR_ERR_SHAPE;
   int64_t bsdp = 0;
-  if (present(a->shared_input)) {
-    if (a->shared_input.ndim != 2 || a->shared_input.dims[1] != n) return GMMFR_ERR_SHAPE;
-    bsdp = a->shared_input.dims[0];
-    // bsdp <= outputBS and sharedInputOffset + bsdp <= outputBS (Atlas 350 common constraints)
-    if (bsdp < 0 || bsdp > obs) return GMMFR_ERR_ATTR;
-    if (a->shared_input_offset < 0 || a->shared_input_offset + bsdp > obs) return GMMFR_ERR_ATTR;
-  } else if (a->shared_input_offset < 0) {
-    return GMMFR_ERR_ATTR;
-  }
-
-  // alignment of every present base pointer
-  const gmmfr_tensor* all[] = {&a->x1, &a->x2, &a->scale, &a->pertoken_scale, &a->group_list, &a->shared_input,
-                               &a->logit, &a->row_index, &a->out, &a->acc_out};
-  for (const gmmfr_tensor* t : all)
-    if (present(*t) && !aligned16(t->data)) return GMMFR_ERR_ALIGN;
+  if (const int st = check_output_and_alignment(a, n, &bsdp)) return st;
+  const int64_t obs = a->output_bs;
 
   if (d) {
     d->m = m;
@@ -138,6 +206,7 @@ int validate(const gmmfr_args* a, Derived* d) {
     d->output_bs = obs;
     d->int4 = int4;
     d->trans_b = trans_b;
+    d->mx = false;
     d->scale_bf16 = present(a->scale) && a->scale.dtype == GMMFR_DT_BFLOAT16;
     d->row_index_i32 = present(a->row_index) && a->row_index.dtype == GMMFR_DT_INT32;
   }
@@ -147,6 +216,7 @@ int validate(const gmmfr_args* a, Derived* d) {
 // Tile choice from the expected rows per expert: tuningConfig[0] when given
 // (the operator's tiling hint), else m / e.  Results do not depend on it.
 TileId choose_tile(const gmmfr_args* a, const Derived& d) {
+  if (d.mx) return kTile128x256;   // the MxA8W4 GEMM has one tile shape
   if (a->tuning_config_len > 1) {  // explicit tile height
     switch (a->tuning_config[1]) {
       case 256: return kTile256x256;
@@ -219,6 +289,7 @@ LaunchArgs to_launch(const gmmfr_args* a, const Derived& d) {
   l.row_index_i32 = d.row_index_i32;
   l.int4 = d.int4;
   l.trans_b = d.trans_b;
+  l.mx = d.mx;
   l.bsdp = d.bsdp;
   l.shared_offset = present(a->shared_input) ? a->shared_input_offset : 0;
   l.output_bs = d.output_bs;
@@ -270,7 +341,7 @@ static int run_stage2(const gmmfr_args* args, void* workspace, size_t workspace_
   if (log_enabled())
     std::fprintf(stderr, "[gmmfr] m=%lld k=%lld n=%lld e=%lld combine=%s %s grid=%d ws=%zu\n", (long long)d.m,
                  (long long)d.k, (long long)d.n, (long long)d.e, plan.combine == kCombineOrdered ? "ordered" : "atomic",
-                 tile_kernel_name(plan.tile, d.int4, d.k, d.trans_b), plan.grid, plan.workspace_bytes);
+                 tile_kernel_name(plan.tile, d.int4, d.k, d.trans_b, d.mx), plan.grid, plan.workspace_bytes);
   const int err = launch_all(to_launch(args, d), plan, workspace, stream, gemm_events);
   return err == 0 ? GMMFR_OK : GMMFR_ERR_HIP;
 }
@@ -302,7 +373,7 @@ int gmm_finalize_routing_plan(const gmmfr_args* args, gmmfr_plan_info* info) {
   info->grid = plan.grid;
   info->int4_weights = d.int4 ? 1 : 0;
   info->workspace_bytes = (int64_t)plan.workspace_bytes;
-  std::snprintf(info->gemm_kernel, sizeof(info->gemm_kernel), "%s", tile_kernel_name(plan.tile, d.int4, d.k, d.trans_b));
+  std::snprintf(info->gemm_kernel, sizeof(info->gemm_kernel), "%s", tile_kernel_name(plan.tile, d.int4, d.k, d.trans_b, d.mx));
   return GMMFR_OK;
 }
 

@@ -1131,6 +1131,205 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// MxA8W4 GEMM ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2", Atlas 350 notes
+// on the MxA8W4 quantisation): x1 FP8 E4M3 (m,k); x2 FP4 E2M1 given
+// transposed, (e,n,k) two per byte along k (low nibble = even k); E8M0 block
+// scales, one per 32 k: pertokenScale (m, k/64, 2) for x1, scale
+// (e, n, k/64, 2) for x2.  For row i of expert g:
+//   acc[i][j] = sum_b 2^(sA[i][b]-127) * 2^(sB[g][j][b]-127) * sum_{k in b} x1[i][k] * w[k][j]
+// accumulated in fp32 by v_mfma_scale_f32_32x32x64_f8f6f4, then
+// y = acc * logit[i] and the same combine as the int8 path.
+//
+// Lane layout of that instruction (measured on the device): A lane l holds
+// row l%32 with bytes 0-15 = k 16h..16h+15 and bytes 16-31 = k 32+16h..
+// 32+16h+15 of the 64-k step (h = l/32); B lane l holds column l%32 with
+// nibbles 0-31 = k 32h..32h+31; the scale operand of lane l is the block-h
+// scale of its row (A) or column (B); the accumulator layout is that of the
+// integer instruction (column l%32, rows (r/4)*8 + h*4 + r%4).
+// ---------------------------------------------------------------------------
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+template <int COMBINE>
+__global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
+  constexpr int BM = 128, BN = 256, BK = 64, STAGES = 4;
+  constexpr int WAVES_N = 2, WTM = 64, WTN = 128, FM = 2, FN = 4;
+  constexpr int A_BYTES = BM * BK;    // fp8: one byte per k
+  constexpr int B_COLB = BK / 2;      // fp4: 32 bytes per column and k-step
+  constexpr int B_BYTES = BN * B_COLB;
+  constexpr int A_INSTR = A_BYTES / 16 / kThreads, B_INSTR = B_BYTES / 16 / kThreads;
+  static_assert(A_INSTR == 2 && B_INSTR == 2 && BN == kThreads && BM == kThreads / 2, "copy split");
+  // copies per thread and stage: A, B and one B-scale dword; waves 0-1 add an A-scale dword
+  constexpr int LOADS_LO = A_INSTR + B_INSTR + 2, LOADS_HI = A_INSTR + B_INSTR + 1;
+
+  __shared__ __attribute__((aligned(16))) int8_t sA[STAGES * A_BYTES];
+  __shared__ __attribute__((aligned(16))) int8_t sB[STAGES * B_BYTES];
+  __shared__ __attribute__((aligned(16))) uint32_t sSA[STAGES][BM];  // the scale dword of each row
+  __shared__ __attribute__((aligned(16))) uint32_t sSB[STAGES][BN];  // and of each column
+  extern __shared__ __attribute__((aligned(16))) int32_t s_dyn[];
+  int32_t* s_ends = s_dyn;
+  int32_t* s_tile_pre = s_dyn + p.e;
+  int64_t* s_scan = (int64_t*)sA;
+  static_assert(STAGES * A_BYTES >= kThreads * 8, "scan scratch fits in the A stages");
+
+  build_group_table(p, BM, s_ends, s_tile_pre, s_scan);
+  const int total_tiles = s_tile_pre[p.e];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, h = lane >> 5;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int64_t k = p.k, n = p.n;
+  const int ktiles = (int)(k / BK);
+  const int64_t kdw = k / 128;         // scale dwords per row or column (k % 128 == 0)
+  const bool lo_wave = wave < 2;       // waves that copy the A-scale dwords (rows 0..127)
+  const uint32_t* sa_words = (const uint32_t*)p.pertoken;
+  const uint32_t* sb_words = (const uint32_t*)p.scale;
+
+  // copy sources of the current tile: wave-uniform bases, per-lane offsets (bytes)
+  const int8_t* a_base = p.x1;
+  const int8_t* b_base = (const int8_t*)p.x2;
+  const uint32_t* sa_base = sa_words;
+  const uint32_t* sb_base = sb_words;
+  uint32_t a_off[A_INSTR], b_off[B_INSTR], sa_off = 0, sb_off = 0;
+  auto set_sources = [&](const TileCoord& c) {
+    a_base = (const int8_t*)uniform64((int64_t)(p.x1 + c.row0 * k));
+#pragma unroll
+    for (int q = 0; q < A_INSTR; ++q) {
+      const int slot = (q * 4 + wave) * 64 + lane;
+      const int r = slot / 4, cpos = slot % 4;
+      const int64_t row = min(c.row0 + r, p.m - 1);  // rows past the group: loaded, never stored
+      a_off[q] = (uint32_t)((row - c.row0) * k + ((cpos ^ swz_a<BK>(r)) * 16));
+    }
+    b_base = (const int8_t*)uniform64((int64_t)((const int8_t*)p.x2 + ((int64_t)c.g * n + c.col0) * (k / 2)));
+#pragma unroll
+    for (int q = 0; q < B_INSTR; ++q) {
+      const int slot = (q * 4 + wave) * 64 + lane;
+      const int r = slot / 2, cpos = slot % 2;
+      const int64_t col = min(c.col0 + r, n - 1);    // columns past n: loaded, never stored
+      b_off[q] = (uint32_t)((col - c.col0) * (k / 2) + cpos * 16);
+    }
+    sa_base = (const uint32_t*)uniform64((int64_t)(sa_words + c.row0 * kdw));
+    sa_off = (uint32_t)((min(c.row0 + tid, p.m - 1) - c.row0) * kdw * 4);
+    sb_base = (const uint32_t*)uniform64((int64_t)(sb_words + ((int64_t)c.g * n + c.col0) * kdw));
+    sb_off = (uint32_t)((min(c.col0 + tid, n - 1) - c.col0) * kdw * 4);
+  };
+  auto issue_stage = [&](int st, int kt) {
+#pragma unroll
+    for (int q = 0; q < A_INSTR; ++q)
+      lds_dma16_sv(a_base + (int64_t)kt * BK, a_off[q],
+                   __builtin_amdgcn_readfirstlane(lds_addr(sA + st * A_BYTES + (q * 4 + wave) * 64 * 16)));
+#pragma unroll
+    for (int q = 0; q < B_INSTR; ++q)
+      lds_dma16_sv(b_base + (int64_t)kt * B_COLB, b_off[q],
+                   __builtin_amdgcn_readfirstlane(lds_addr(sB + st * B_BYTES + (q * 4 + wave) * 64 * 16)));
+    // the dword holding the two block scales of k-step kt (and of its neighbour)
+    lds_dma4_sv(sb_base + kt / 2, sb_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSB[st][wave * 64])));
+    if (lo_wave) lds_dma4_sv(sa_base + kt / 2, sa_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSA[st][wave * 64])));
+  };
+
+  auto coord = [&](int tt) {
+    TileCoord c = tile_coord<BM, BN>(p, s_ends, s_tile_pre, __builtin_amdgcn_readfirstlane(tt));
+    c.g = __builtin_amdgcn_readfirstlane(c.g);
+    c.valid_rows = __builtin_amdgcn_readfirstlane(c.valid_rows);
+    c.row0 = uniform64(c.row0);
+    c.col0 = uniform64(c.col0);
+    return c;
+  };
+
+  const int G = gridDim.x;
+  const bool blocked = G % kTileQueues == 0;
+  const int vq = blockIdx.x % kTileQueues, lw = blockIdx.x / kTileQueues, per_q = G / kTileQueues;
+  for (int j = 0;; ++j) {
+    int t;
+    if (blocked) {
+      t = queue_tile(vq, j * per_q + lw, total_tiles);
+    } else {
+      const int64_t tt = (int64_t)j * G + blockIdx.x;
+      t = tt < total_tiles ? (int)tt : -1;
+    }
+    if (t < 0) break;
+    const TileCoord c = coord(t);
+    __syncthreads();  // every wave is done with the previous tile's stages
+    set_sources(c);
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+      if (st < ktiles) issue_stage(st, st);
+    v16f acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < FN; ++jj) acc[i][jj] = v16f{0};
+#pragma unroll 1
+    for (int kt = 0; kt < ktiles; ++kt) {
+      // stage kt complete; the stages issued after it may still be in flight
+      if (kt + STAGES - 2 < ktiles) {
+        if (lo_wave) wait_vmcnt<(STAGES - 2) * LOADS_LO>();
+        else wait_vmcnt<(STAGES - 2) * LOADS_HI>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      lds_barrier();
+      if (kt + STAGES - 1 < ktiles) issue_stage((kt + STAGES - 1) % STAGES, kt + STAGES - 1);
+      const int st = kt % STAGES;
+      const int8_t* a_st = sA + st * A_BYTES;
+      const int8_t* b_st = sB + st * B_BYTES;
+      const int sel = 8 * (2 * (kt & 1) + h);  // byte of this lane's block in the scale dword
+      v8i af[FM];
+      int sa[FM], sb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WTM + i * 32 + (lane & 31);
+        const v4i lo = *(const LDS_PTR(v4i))(a_st + r * BK + ((h ^ swz_a<BK>(r)) << 4));
+        const v4i hi = *(const LDS_PTR(v4i))(a_st + r * BK + (((2 + h) ^ swz_a<BK>(r)) << 4));
+        af[i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        sa[i] = (int)(sSA[st][r] >> sel);
+      }
+      v8i bf[FN];
+#pragma unroll
+      for (int jj = 0; jj < FN; ++jj) {
+        const int cl = wn * WTN + jj * 32 + (lane & 31);
+        const v4i w = *(const LDS_PTR(v4i))(b_st + cl * B_COLB + h * 16);
+        bf[jj] = v8i{w.x, w.y, w.z, w.w, 0, 0, 0, 0};
+        sb[jj] = (int)(sSB[st][cl] >> sel);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[jj], acc[i][jj], 0, 4, 0, sa[i], 0,
+                                                                        sb[jj]);
+    }
+    // epilogue: y = acc * logit, guarded by the tile's valid rows and n
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm * WTM + i * 32 + (r / 4) * 8 + h * 4 + (r % 4);
+        if (lr >= c.valid_rows) continue;
+        const int64_t row = c.row0 + lr;
+        const float lg = p.logit ? p.logit[row] : 1.0f;
+        int64_t d = row;
+        if constexpr (COMBINE == kCombineAtomic) {
+          d = dest_row(p, row);
+          if (d < 0) continue;
+        }
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj) {
+          const int64_t col = c.col0 + wn * WTN + jj * 32 + (lane & 31);
+          if (col >= n) continue;
+          const float v = acc[i][jj][r] * lg;
+          if constexpr (COMBINE == kCombineOrdered)
+            __builtin_nontemporal_store(v, p.y + row * n + col);
+          else
+            __hip_atomic_fetch_add(p.out + d * n + col, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();  // no copy in flight when the workgroup ends
+}
+
+// ---------------------------------------------------------------------------
 // out := seed.  Rows [off, off+bsdp) take the widened bf16 sharedInput, the
 // rest +0.0 ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2", Atlas 350 common
 // constraints on sharedInput / sharedInputOffset / outputBS).
@@ -1346,7 +1545,8 @@ bool uses_continuous_pipeline(bool int4, int64_t k, int bm, int bk, int stages) 
   return bm >= 64 && k / bk >= stages;
 }
 
-const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b) {
+const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool mx) {
+  if (mx) return "mx_gemm_kernel<128,256,64,2x2,s4,fp8xfp4>";
   // per tile: i8, i4, i8 cont, i4 cont, i8 transposed weights, i8 cont transposed weights
   static const char* names[kNumTiles][6] = {
       {"gmm_kernel<256,256,64,2x2,s3,i8>", "gmm_kernel<256,256,64,2x2,s3,i4>", "gmm_kernel<256,256,64,2x2,s3,i8,cont>",
@@ -1476,7 +1676,13 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
       const hipError_t er = hipEventRecord((hipEvent_t)gemm_events[0], s);
       if (er != hipSuccess) return (int)er;
     }
-    switch (plan.tile) {
+    const size_t dyn = ((size_t)(2 * kp.e + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
+    if (a.mx) {
+      if (kp.combine == kCombineOrdered)
+        hipLaunchKernelGGL(mx_gemm_kernel<kCombineOrdered>, dim3(plan.grid), dim3(kThreads), dyn, s, kp);
+      else
+        hipLaunchKernelGGL(mx_gemm_kernel<kCombineAtomic>, dim3(plan.grid), dim3(kThreads), dyn, s, kp);
+    } else switch (plan.tile) {
       case kTile256x256: launch_gemm<256, 256, 64, 2, 2, 3, 1>(kp, a.int4, a.trans_b, plan.grid, s); break;
       case kTile128x256: launch_gemm<128, 256, 64, 2, 2, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;
       case kTile64x256: launch_gemm<64, 256, 64, 1, 4, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;

@@ -87,6 +87,9 @@ class Problem:
     seed: int = 0
     counts: Optional[np.ndarray] = None  # rows per expert (for statistics)
     x2_transposed: bool = False          # True -> int8 x2 is given as (e,n,k)
+    mx: bool = False                     # MxA8W4: x1 uint8 FP8-E4M3 codes (m,k); x2 uint8 (e,n,k/2)
+                                         # FP4-E2M1 pairs (low nibble = even k); pertoken_scale uint8
+                                         # E8M0 (m,k/64,2); scale uint8 E8M0 (e,n,k/64,2)
 
     @property
     def bsdp(self) -> int:
@@ -282,3 +285,77 @@ def with_transposed_weights(p: Problem) -> Problem:
         raise ValueError("transposed weights are taken from an untransposed int8 problem")
     return dataclasses.replace(p, x2=np.ascontiguousarray(np.transpose(p.x2, (0, 2, 1))), x2_transposed=True,
                                name=p.name + "-tb")
+
+
+# ---------------------------------------------------------------- MxA8W4 inputs
+
+
+def _fp8_codes(rng, shape) -> np.ndarray:
+    """FP8 E4M3 codes: random sign, exponent field 3..11 (|v| in [2^-4, 2^4 * 1.875]),
+    random mantissa, about 1 in 16 set to zero; never the NaN codes 0x7F/0xFF."""
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint8) << 7
+    ex = rng.integers(3, 12, size=shape, dtype=np.uint8) << 3
+    man = rng.integers(0, 8, size=shape, dtype=np.uint8)
+    codes = (sign | ex | man).astype(np.uint8)
+    codes[rng.uniform(size=shape) < 1.0 / 16] = 0
+    return codes
+
+
+def _fp4_pairs(rng, shape_pairs) -> np.ndarray:
+    """Random FP4 E2M1 codes, two per byte (every code is a number)."""
+    return rng.integers(0, 256, size=shape_pairs, dtype=np.int64).astype(np.uint8)
+
+
+def _e8m0(rng, shape, lo=120, hi=134) -> np.ndarray:
+    return rng.integers(lo, hi + 1, size=shape, dtype=np.int64).astype(np.uint8)
+
+
+def mx_problem(seed: int, m: int, k: int, n: int, e: int, *, group_list_type: int = 0,
+               with_logit: bool = True, with_row_index: bool = True, bsdp: int = 0, shared_offset: int = 0,
+               output_bs: Optional[int] = None, empty_frac: float = 0.25, uncovered: int = 0) -> Problem:
+    """A random MxA8W4 problem (FP8 activations, FP4 weights given (e,n,k), E8M0
+    block scales per 32 k) for parity and invariant tests."""
+    if k % 64:
+        raise ValueError("k must be a multiple of 64")
+    rng = np.random.default_rng(seed)
+    covered = m - uncovered
+    w = rng.uniform(0.2, 1.0, size=e) * (rng.uniform(size=e) >= empty_frac)
+    if w.sum() == 0:
+        w[rng.integers(e)] = 1.0
+    counts = _largest_remainder(w, covered) if covered > 0 else np.zeros(e, dtype=np.int64)
+    if output_bs is None:
+        output_bs = max(1, m // 2)
+    ri = rng.integers(0, output_bs, size=m).astype(np.int64) if with_row_index else None
+    logit = rng.uniform(0.0, 1.0, size=m).astype(np.float32) if with_logit else None
+    x1 = _fp8_codes(rng, (m, k))
+    x2 = _fp4_pairs(rng, (e, n, k // 2))
+    pts = _e8m0(rng, (m, k // 64, 2))
+    scale = _e8m0(rng, (e, n, k // 64, 2))
+    shared = None
+    if bsdp > 0:
+        shared = f32_to_bf16_bits(rng.standard_normal((bsdp, n)).astype(np.float32) * 64.0)
+    return Problem(f"mx{seed}", m, k, n, e, x1, x2, False, scale, False, pts, logit,
+                   _group_list(counts, group_list_type), group_list_type, ri, shared, shared_offset, output_bs,
+                   seed, counts, True, True)
+
+
+def make_mx_config(name: str = "mxa8w4", seed: int = 0) -> Problem:
+    """MxA8W4 at the prefill shape: 16384 tokens, top-8, 32 experts, k = 2048,
+    n = 7168, routing, logit and sharedInput drawn as for the prefill workload;
+    FP8 activations, FP4 weights (e,n,k) and E8M0 block scales drawn uniformly."""
+    if name != "mxa8w4":
+        raise ValueError(name)
+    rng = np.random.default_rng(seed)
+    T, K, e, k, n, obs = 16384, 8, 32, 2048, 7168, 16384
+    m = T * K
+    u = rng.uniform(-0.2, 0.2, size=e)
+    counts = _largest_remainder(4096.0 * (1.0 + u), m)
+    ri = _row_index(rng, T, K, np.int64)
+    logit = _topk_softmax_logit(rng, T, K, ri)
+    x1 = _fp8_codes(rng, (m, k))
+    x2 = _fp4_pairs(rng, (e, n, k // 2))
+    pts = _e8m0(rng, (m, k // 64, 2))
+    scale = _e8m0(rng, (e, n, k // 64, 2))
+    shared = f32_to_bf16_bits(rng.standard_normal((8192, n)).astype(np.float32))
+    return Problem(name, m, k, n, e, x1, x2, False, scale, False, pts, logit,
+                   _group_list(counts, 0), 0, ri, shared, 4096, obs, seed, counts, True, True)

@@ -15,6 +15,17 @@ def to_device(p, dev="cuda"):
     def bf16(a):
         return None if a is None else T(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
 
+    if getattr(p, "mx", False):
+        return {
+            "x1": T(p.x1).view(torch.float8_e4m3fn),
+            "x2": T(p.x2).view(torch.float4_e2m1fn_x2),
+            "scale": T(p.scale).view(torch.float8_e8m0fnu),
+            "pertoken_scale": T(p.pertoken_scale).view(torch.float8_e8m0fnu),
+            "logit": T(p.logit),
+            "group_list": T(p.group_list),
+            "row_index": T(p.row_index),
+            "shared_input": bf16(p.shared_input),
+        }
     return {
         "x1": T(p.x1),
         "x2": T(p.x2),

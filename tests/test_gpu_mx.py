@@ -1,0 +1,68 @@
+"""GPU parity of the MxA8W4 mode (FP8 activations, FP4 weights given (e,n,k),
+E8M0 block scales) against the float64 oracle, through the C ABI.
+
+The matrix core accumulates in fp32 in an order of its own, so each output
+element is checked against the oracle's error bound for any fp32 evaluation
+order (oracle/mx.py); the ordered combine must also be run-to-run identical.
+"""
+import numpy as np
+import pytest
+
+from oracle import mx as MX
+from quantized_moe_grouped_amd import workloads as W
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "ragged_shared": dict(seed=1, m=300, k=256, n=288, e=3, output_bs=200, bsdp=40, shared_offset=7),
+    "counts_uncovered": dict(seed=2, m=700, k=384, n=544, e=5, group_list_type=1, uncovered=13, output_bs=333),
+    "no_logit_identity": dict(seed=3, m=257, k=128, n=64, e=2, with_logit=False, with_row_index=False,
+                              output_bs=257),
+    "many_empty": dict(seed=4, m=900, k=256, n=256, e=40, empty_frac=0.7, output_bs=300),
+    "single_row": dict(seed=5, m=1, k=128, n=32, e=1, output_bs=1),
+    "long_k": dict(seed=6, m=400, k=2048, n=320, e=2, output_bs=150, bsdp=20, shared_offset=100),
+}
+
+
+def _check(p, got, ref, bound):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref)
+    bad = err > bound
+    assert not bad.any(), (f"{int(bad.sum())} elements outside the bound; worst excess "
+                           f"{float((err - bound).max())} at {np.argwhere(bad)[0].tolist()}")
+    # the bound is a worst case; typical errors sit far inside it (a wrong
+    # block scale or k pairing would not)
+    assert float(np.median(err / np.maximum(bound, 1e-300))) < 0.02
+
+
+@pytest.mark.parametrize("name", list(CASES), ids=list(CASES))
+def test_mx_random_case_all_elements(name):
+    p = W.mx_problem(**CASES[name])
+    ref, bound, _ = MX.run(p)
+    d = G.to_device(p)
+    for det, combine in ((True, "auto"), (False, "atomic"), (False, "auto")):
+        out, _ = G.run_gpu(p, d, deterministic=det, combine=combine)
+        _check(p, out.cpu().numpy(), ref, bound)
+
+
+def test_mx_ordered_is_run_to_run_identical():
+    p = W.mx_problem(**CASES["ragged_shared"])
+    d = G.to_device(p)
+    a, _ = G.run_gpu(p, d, deterministic=True)
+    b, _ = G.run_gpu(p, d, deterministic=True)
+    G.assert_bitexact(b.cpu().numpy(), a.cpu().numpy())
+
+
+def test_mx_workload_sampled_rows():
+    p = W.make_mx_config("mxa8w4", 0)
+    rng = np.random.default_rng(100)
+    dsel = np.array(sorted(set(rng.choice(p.output_bs, size=24, replace=False).tolist())
+                           | {0, p.output_bs - 1, 4095, 4096, 12287, 12288}), dtype=np.int64)
+    ref, bound = MX.out_rows(p, dsel)
+    d = G.to_device(p)
+    out, _ = G.run_gpu(p, d, deterministic=True)
+    _check(p, out.cpu().numpy()[dsel], ref, bound)
+    out2, _ = G.run_gpu(p, d, deterministic=False, combine="atomic")
+    _check(p, out2.cpu().numpy()[dsel], ref, bound)
