@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="prefill", choices=["tiny", "decode", "skewed", "prefill", "int4", "mxa8w4"])
+    ap.add_argument("--config", default="prefill", choices=["tiny", "decode", "skewed", "prefill", "int4", "mxa8w4", "fp8"])
     ap.add_argument("--combine", default="auto", choices=["auto", "atomic", "ordered"])
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
@@ -82,6 +82,9 @@ class Hip:
 
 def algorithmic_bytes(p):
     """Each input read once, the output written once (no atomics, no y)."""
+    if getattr(p, "fp8", False):  # fp8 x1 and weights, per-channel scale (bf16 here) and per-token scale
+        return (p.covered_rows * p.k + p.nonempty_experts * p.n * (p.k + 2) + p.m * (4 + 4 + 8) + p.e * 8
+                + p.bsdp * p.n * 2 + p.output_bs * p.n * 4)
     if getattr(p, "mx", False):  # fp8 x1, fp4 weights, one E8M0 per 32 k of each row and column
         return (p.covered_rows * (p.k + p.k // 32) + p.nonempty_experts * p.n * (p.k // 2 + p.k // 32)
                 + p.m * (4 + 8) + p.e * 8 + p.bsdp * p.n * 2 + p.output_bs * p.n * 4)
@@ -107,8 +110,9 @@ def cpu_baseline(p, rows_wanted: int):
                   p.scale_bf16, None if p.pertoken_scale is None else p.pertoken_scale[idx],
                   None if p.logit is None else p.logit[idx], np.cumsum(take).astype(np.int64), 0,
                   None if p.row_index is None else p.row_index[idx], p.shared_input, p.shared_input_offset,
-                  p.output_bs, p.seed, take, getattr(p, "x2_transposed", False), getattr(p, "mx", False))
-    if q.mx:
+                  p.output_bs, p.seed, take, x2_transposed=getattr(p, "x2_transposed", False),
+                  fp8=getattr(p, "fp8", False), mx=getattr(p, "mx", False))
+    if q.mx or q.fp8:
         from oracle import mx as omx
         t0 = time.perf_counter()
         omx.run(q)
@@ -170,7 +174,12 @@ def main():
                           "copy_GBps_read_plus_write": round(2 * (1 << 30) / dt / 1e9, 1)}), flush=True)
         return
     print(f"[bench] generating {args.config} seed {args.seed}", file=sys.stderr, flush=True)
-    p = W.make_mx_config(args.config, args.seed) if args.config == "mxa8w4" else W.make_config(args.config, args.seed)
+    if args.config == "mxa8w4":
+        p = W.make_mx_config(args.config, args.seed)
+    elif args.config == "fp8":
+        p = W.make_fp8_config(args.config, args.seed)
+    else:
+        p = W.make_config(args.config, args.seed)
     if args.transpose_x2:
         p = W.with_transposed_weights(p)
     dev = "cuda"
@@ -184,6 +193,10 @@ def main():
     if p.mx:
         x1, x2 = T(p.x1).view(torch.float8_e4m3fn), T(p.x2).view(torch.float4_e2m1fn_x2)
         scale, pts = T(p.scale).view(torch.float8_e8m0fnu), T(p.pertoken_scale).view(torch.float8_e8m0fnu)
+    elif p.fp8:
+        x1, x2 = T(p.x1).view(torch.float8_e4m3fn), T(p.x2).view(torch.float8_e4m3fn)
+        scale = None if p.scale is None else (bf16(p.scale) if p.scale_bf16 else T(p.scale))
+        pts = T(p.pertoken_scale)
     else:
         x1, x2 = T(p.x1), T(p.x2)
         scale = None if p.scale is None else (bf16(p.scale) if p.scale_bf16 else T(p.scale))
@@ -241,11 +254,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8xfp4" if p.mx else "int8",
+        "dtype": "fp8xfp4" if p.mx else ("fp8" if p.fp8 else "int8"),
         "data": "synthetic (seeded generator; random int8 weights/activations, routing and scales of the stated shapes)",
         "config": {"workload": p.name, "tokens": p.output_bs, "top_k": p.m // max(p.output_bs, 1), "m": p.m,
                    "e": p.e, "k": p.k, "n": p.n,
-                   "weights": "fp4 e2m1, e8m0 per 32 k" if p.mx else ("int4" if p.x2_int4 else "int8"),
+                   "weights": "fp4 e2m1, e8m0 per 32 k" if p.mx else
+                   ("fp8 e4m3" if p.fp8 else ("int4" if p.x2_int4 else "int8")),
                    "weights_layout": "(e,n,k)" if p.x2_transposed else "(e,k,n)",
                    "output_bs": p.output_bs, "shared_rows": p.bsdp, "combine": plan["combine"],
                    "deterministic": bool(args.deterministic), "seed": args.seed,

@@ -1,4 +1,4 @@
-"""CPU oracle for the MxA8W4 mode.  TEST INFRASTRUCTURE ONLY: the tests, the
+"""CPU oracle for the MxA8W4 and FP8 modes.  TEST INFRASTRUCTURE ONLY: the tests, the
 smoke check and the CPU-baseline leg of the benchmark may use it; the GPU
 library never does, and the two share no code.
 
@@ -26,6 +26,14 @@ accumulator with round-to-nearest-even.  Taken with one bit of margin, a block
 contributes at most 32 * 2^(e - 12) <= 2^-7 * max|product| of error (e the
 exponent of its largest product), bounded above by 2^-7 * max|x1 block| *
 max|w block|; the k/32 block sums and the accumulator then add like fp32.
+
+FP8 mode (x1 and x2 FLOAT8_E4M3FN, "aclnnGroupedMatmulFinalizeRoutingWeightNzV2"
+parameter notes: rowIndex INT64 only for FLOAT8_E4M3FN inputs; Atlas 350
+pertoken-perchannel quantisation): x2 given as (e,n,k) here, no block scales,
+and the int8 mode's dequantisation after the sum:
+
+    acc[i][j] = sum_kk x1[i][kk] * w[g][j][kk]
+    y[i][j]   = ((acc[i][j] * scale[g][0][j]) * pertokenScale[i]) * logit[i]
 
 Element formats (OCP Microscaling formats, v1.0, element data types):
     FP8 E4M3: sign, 4-bit exponent (bias 7), 3-bit mantissa; exponent 0 is
@@ -93,15 +101,23 @@ def group_ranges(p):
     return starts, ends.astype(np.int64)
 
 
+def _is_fp8(p) -> bool:
+    return bool(getattr(p, "fp8", False))
+
+
 def _scaled_rows(p, rows):
-    """x1 rows with their block scales applied, float64 (len(rows), k)."""
+    """x1 rows with their block scales applied (MX) or as decoded (FP8), float64 (len(rows), k)."""
     x = FP8_TABLE[np.asarray(p.x1)[rows]]
+    if _is_fp8(p):
+        return x
     s = E8M0_TABLE[np.asarray(p.pertoken_scale)[rows]].reshape(len(rows), -1)  # (rows, k/32)
     return x * np.repeat(s, 32, axis=1)
 
 
 def _scaled_weights(p, g):
-    """Expert g's weights with their block scales applied, float64 (n, k)."""
+    """Expert g's weights with their block scales applied (MX) or as decoded (FP8), float64 (n, k)."""
+    if _is_fp8(p):
+        return FP8_TABLE[np.asarray(p.x2)[g]]
     w = FP4_TABLE[unpack_fp4(np.asarray(p.x2)[g])]
     s = E8M0_TABLE[np.asarray(p.scale)[g]].reshape(p.n, -1)  # (n, k/32)
     return w * np.repeat(s, 32, axis=1)
@@ -120,6 +136,24 @@ def rows_acc(p, rows, g):
     amax = np.abs(a).reshape(a.shape[0], -1, 32).max(axis=2)
     wmax = np.abs(w).reshape(w.shape[0], -1, 32).max(axis=2)
     return a @ w.T, (np.abs(a) @ np.abs(w).T, amax @ wmax.T)
+
+
+def _post(p, rows, g):
+    """The factors applied after the sum, as one float64 multiplier per element,
+    and the number of rounded fp32 products that apply them: MX logit only;
+    FP8 ((acc * scale) * pertokenScale) * logit."""
+    rows = np.asarray(rows)
+    L = np.ones(len(rows)) if p.logit is None else np.asarray(p.logit, dtype=np.float64)[rows]
+    if not _is_fp8(p):
+        return np.repeat(L[:, None], p.n, axis=1), 1
+    P = np.ones(len(rows)) if p.pertoken_scale is None else np.asarray(p.pertoken_scale, dtype=np.float64)[rows]
+    if p.scale is None:
+        S = np.ones(p.n)
+    elif p.scale_bf16:
+        S = (np.asarray(p.scale)[g, 0].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    else:
+        S = np.asarray(p.scale, dtype=np.float64)[g, 0]
+    return S[None, :] * P[:, None] * L[:, None], 3
 
 
 def _seed_row(p, d):
@@ -145,9 +179,14 @@ def run(p):
     covered = np.zeros(p.m, dtype=bool)
     for a, b in zip(starts, ends):
         covered[a:b] = True
-    logit = np.ones(p.m) if p.logit is None else np.asarray(p.logit, dtype=np.float64)
-    y = acc * logit[:, None]
-    ey = _row_error(acc, mag, bmax, logit, p.k)
+    y = np.zeros_like(acc)
+    ey = np.zeros_like(acc)
+    for g in range(p.e):
+        if ends[g] > starts[g]:
+            rows = np.arange(starts[g], ends[g])
+            mult, nmul = _post(p, rows, g)
+            y[rows] = acc[rows] * mult
+            ey[rows] = _row_error(acc[rows], mag[rows], bmax[rows], mult, nmul, p.k)
     ri = np.arange(p.m) if p.row_index is None else np.asarray(p.row_index, dtype=np.int64)
     out = np.stack([_seed_row(p, d) for d in range(p.output_bs)]) if p.output_bs else np.zeros((0, p.n))
     err = np.zeros_like(out)
@@ -167,14 +206,14 @@ def run(p):
     return out, bound, acc
 
 
-def _row_error(acc, mag, bmax, logit, k):
-    """|y_gpu - acc*logit| <= |logit| (E + u (|acc| + E)) with
+def _row_error(acc, mag, bmax, mult, nmul, k):
+    """|y_gpu - acc*mult| <= |mult| (E + gamma_nmul (|acc| + E)) with
     E = 2^-7 bmax + gamma_(k/32+1) (mag + 2^-7 bmax): the in-block alignment
-    of the matrix core, the fp32 additions of the block sums, then one
-    rounded product."""
+    of the matrix core, the fp32 additions of the block sums, then nmul
+    rounded products."""
     e_blk = 2.0 ** -7 * bmax
     e_acc = e_blk + _gamma(k // 32 + 1) * (mag + e_blk)
-    return np.abs(logit)[:, None] * (e_acc + U32 * (np.abs(acc) + e_acc))
+    return np.abs(mult) * (e_acc + _gamma(nmul) * (np.abs(acc) + e_acc))
 
 
 def out_rows(p, d_list):
@@ -186,7 +225,6 @@ def out_rows(p, d_list):
     for g in range(p.e):
         group_of[starts[g]:ends[g]] = g
     ri = np.arange(p.m) if p.row_index is None else np.asarray(p.row_index, dtype=np.int64)
-    logit = np.ones(p.m) if p.logit is None else np.asarray(p.logit, dtype=np.float64)
     d_list = [int(d) for d in d_list]
     rows_of = {d: np.nonzero((ri == d) & (group_of >= 0))[0] for d in d_list}  # ascending
     need = np.unique(np.concatenate([rows_of[d] for d in d_list] + [np.zeros(0, dtype=np.int64)]))
@@ -194,8 +232,9 @@ def out_rows(p, d_list):
     for g in np.unique(group_of[need]):
         rows = need[group_of[need] == g]
         a, (m_, b_) = rows_acc(p, rows, int(g))
-        yr = a * logit[rows, None]
-        er = _row_error(a, m_, b_, logit[rows], p.k)
+        mult, nmul = _post(p, rows, int(g))
+        yr = a * mult
+        er = _row_error(a, m_, b_, mult, nmul, p.k)
         for t, i in enumerate(rows):
             y[int(i)], ey[int(i)] = yr[t], er[t]
     outs, bounds = [], []
@@ -226,6 +265,9 @@ def brute(p):
             for j in range(p.n):
                 total = 0.0
                 for kk in range(p.k):
+                    if _is_fp8(p):  # both operands FP8, no block scales
+                        total += fp8_e4m3_value(int(x1[i, kk])) * fp8_e4m3_value(int(x2[g, j, kk]))
+                        continue
                     byte = int(x2[g, j, kk // 2])
                     wcode = byte & 0xF if kk % 2 == 0 else byte >> 4
                     blk = kk // 32

@@ -23,6 +23,7 @@ struct Derived {
   bool int4;
   bool trans_b;  // int8 weights given transposed, (e,n,k)
   bool mx;       // MxA8W4: FP8 x1, FP4 x2 (e,n,k), E8M0 block scales
+  bool fp8;      // FP8 x1 and x2 (e,n,k), per-channel scale, per-token pertokenScale
   bool scale_bf16;
   bool row_index_i32;
 };
@@ -130,7 +131,62 @@ int validate_mx(const gmmfr_args* a, Derived* d) {
     d->int4 = false;
     d->trans_b = true;
     d->mx = true;
+    d->fp8 = false;
     d->scale_bf16 = false;
+    d->row_index_i32 = false;
+  }
+  return GMMFR_OK;
+}
+
+// FP8 E4M3 x1 and x2 ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2", parameter
+// notes: rowIndex INT64 only when x1 and x2 are FLOAT8_E4M3FN; Atlas 350
+// pertoken-perchannel quantisation): scale FLOAT32/BFLOAT16 (e,1,n) and
+// pertokenScale FLOAT32 (m) as in the int8 mode.  Ours: x2 given transposed,
+// (e,n,k), the matrix core's layout (transpose_x2 = 1); k % 64 == 0.
+int validate_fp8(const gmmfr_args* a, Derived* d) {
+  if (a->x2.dtype != GMMFR_DT_FLOAT8_E4M3FN) return GMMFR_ERR_DTYPE;
+  if (present(a->scale) && a->scale.dtype != GMMFR_DT_FLOAT32 && a->scale.dtype != GMMFR_DT_BFLOAT16)
+    return GMMFR_ERR_DTYPE;
+  if (present(a->pertoken_scale) && a->pertoken_scale.dtype != GMMFR_DT_FLOAT32) return GMMFR_ERR_DTYPE;
+  if (a->group_list.dtype != GMMFR_DT_INT64) return GMMFR_ERR_DTYPE;
+  if (present(a->shared_input) && a->shared_input.dtype != GMMFR_DT_BFLOAT16) return GMMFR_ERR_DTYPE;
+  if (present(a->logit) && a->logit.dtype != GMMFR_DT_FLOAT32) return GMMFR_ERR_DTYPE;
+  if (present(a->row_index) && a->row_index.dtype != GMMFR_DT_INT64) return GMMFR_ERR_DTYPE;
+  if (a->out.dtype != GMMFR_DT_FLOAT32) return GMMFR_ERR_DTYPE;
+  if (present(a->acc_out)) return GMMFR_ERR_UNSUPPORTED;  // no integer accumulator on this path
+
+  if (const int st = check_attributes(a)) return st;
+  if (a->transpose_x1 != 0) return GMMFR_ERR_ATTR;
+  if (a->transpose_x2 != 1) return GMMFR_ERR_UNSUPPORTED;  // (e,k,n) FP8 weights: not built
+
+  if (a->x1.ndim != 2 || a->x2.ndim != 3) return GMMFR_ERR_SHAPE;
+  const int64_t m = a->x1.dims[0], k = a->x1.dims[1];
+  const int64_t e = a->x2.dims[0], n = a->x2.dims[1];
+  if (a->x2.dims[2] != k) return GMMFR_ERR_SHAPE;
+  if (m < 0 || m >= (int64_t(1) << 31)) return GMMFR_ERR_SHAPE;
+  if (e < 1 || e > kMaxExperts) return GMMFR_ERR_SHAPE;
+  if (k < 64 || k > 65536 || k % 64 != 0) return GMMFR_ERR_SHAPE;
+  if (n < 16 || n % 16 != 0) return GMMFR_ERR_SHAPE;
+  if (n > (int64_t(1) << 24) || m * n >= (int64_t(1) << 40)) return GMMFR_ERR_SHAPE;
+  if (present(a->scale) && !dims_are(a->scale, 3, e, 1, n)) return GMMFR_ERR_SHAPE;
+  if (present(a->pertoken_scale) && !dims_are(a->pertoken_scale, 1, m)) return GMMFR_ERR_SHAPE;
+  if (!dims_are(a->group_list, 1, e)) return GMMFR_ERR_SHAPE;
+  if (present(a->logit) && !dims_are(a->logit, 1, m)) return GMMFR_ERR_SHAPE;
+  if (present(a->row_index) && !dims_are(a->row_index, 1, m)) return GMMFR_ERR_SHAPE;
+  int64_t bsdp = 0;
+  if (const int st = check_output_and_alignment(a, n, &bsdp)) return st;
+  if (d) {
+    d->m = m;
+    d->k = k;
+    d->n = n;
+    d->e = e;
+    d->bsdp = bsdp;
+    d->output_bs = a->output_bs;
+    d->int4 = false;
+    d->trans_b = true;
+    d->mx = false;
+    d->fp8 = true;
+    d->scale_bf16 = present(a->scale) && a->scale.dtype == GMMFR_DT_BFLOAT16;
     d->row_index_i32 = false;
   }
   return GMMFR_OK;
@@ -147,7 +203,8 @@ int validate(const gmmfr_args* a, Derived* d) {
   if (present(a->bias) || present(a->offset) || present(a->antiquant_scale) || present(a->antiquant_offset))
     return GMMFR_ERR_UNSUPPORTED;
   if (present(a->scale) && a->scale.dtype == GMMFR_DT_INT64) return GMMFR_ERR_UNSUPPORTED;
-  if (a->x1.dtype == GMMFR_DT_FLOAT8_E4M3FN) return validate_mx(a, d);
+  if (a->x1.dtype == GMMFR_DT_FLOAT8_E4M3FN)
+    return a->x2.dtype == GMMFR_DT_FLOAT8_E4M3FN ? validate_fp8(a, d) : validate_mx(a, d);
 
   // element types
   if (a->x1.dtype != GMMFR_DT_INT8) return GMMFR_ERR_DTYPE;
@@ -207,6 +264,7 @@ int validate(const gmmfr_args* a, Derived* d) {
     d->int4 = int4;
     d->trans_b = trans_b;
     d->mx = false;
+    d->fp8 = false;
     d->scale_bf16 = present(a->scale) && a->scale.dtype == GMMFR_DT_BFLOAT16;
     d->row_index_i32 = present(a->row_index) && a->row_index.dtype == GMMFR_DT_INT32;
   }
@@ -216,7 +274,7 @@ int validate(const gmmfr_args* a, Derived* d) {
 // Tile choice from the expected rows per expert: tuningConfig[0] when given
 // (the operator's tiling hint), else m / e.  Results do not depend on it.
 TileId choose_tile(const gmmfr_args* a, const Derived& d) {
-  if (d.mx) return kTile128x256;   // the MxA8W4 GEMM has one tile shape
+  if (d.mx || d.fp8) return kTile128x256;   // the FP8 GEMMs have one tile shape
   if (a->tuning_config_len > 1) {  // explicit tile height
     switch (a->tuning_config[1]) {
       case 256: return kTile256x256;
@@ -290,6 +348,7 @@ LaunchArgs to_launch(const gmmfr_args* a, const Derived& d) {
   l.int4 = d.int4;
   l.trans_b = d.trans_b;
   l.mx = d.mx;
+  l.fp8 = d.fp8;
   l.bsdp = d.bsdp;
   l.shared_offset = present(a->shared_input) ? a->shared_input_offset : 0;
   l.output_bs = d.output_bs;
@@ -341,7 +400,7 @@ static int run_stage2(const gmmfr_args* args, void* workspace, size_t workspace_
   if (log_enabled())
     std::fprintf(stderr, "[gmmfr] m=%lld k=%lld n=%lld e=%lld combine=%s %s grid=%d ws=%zu\n", (long long)d.m,
                  (long long)d.k, (long long)d.n, (long long)d.e, plan.combine == kCombineOrdered ? "ordered" : "atomic",
-                 tile_kernel_name(plan.tile, d.int4, d.k, d.trans_b, d.mx), plan.grid, plan.workspace_bytes);
+                 tile_kernel_name(plan.tile, d.int4, d.k, d.trans_b, d.mx, d.fp8), plan.grid, plan.workspace_bytes);
   const int err = launch_all(to_launch(args, d), plan, workspace, stream, gemm_events);
   return err == 0 ? GMMFR_OK : GMMFR_ERR_HIP;
 }
@@ -373,7 +432,7 @@ int gmm_finalize_routing_plan(const gmmfr_args* args, gmmfr_plan_info* info) {
   info->grid = plan.grid;
   info->int4_weights = d.int4 ? 1 : 0;
   info->workspace_bytes = (int64_t)plan.workspace_bytes;
-  std::snprintf(info->gemm_kernel, sizeof(info->gemm_kernel), "%s", tile_kernel_name(plan.tile, d.int4, d.k, d.trans_b, d.mx));
+  std::snprintf(info->gemm_kernel, sizeof(info->gemm_kernel), "%s", tile_kernel_name(plan.tile, d.int4, d.k, d.trans_b, d.mx, d.fp8));
   return GMMFR_OK;
 }
 

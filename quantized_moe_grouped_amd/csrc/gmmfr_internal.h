@@ -44,6 +44,7 @@ struct LaunchArgs {
   int32_t int4;
   int32_t trans_b;           // int8 weights given as (e,n,k)
   int32_t mx;                // MxA8W4: x1 fp8 e4m3, x2 fp4 e2m1 (e,n,k/2 bytes), scale/pertoken E8M0 block scales
+  int32_t fp8;               // x1 fp8 e4m3, x2 fp8 e4m3 (e,n,k), scale fp32/bf16 (e,1,n), pertoken fp32 (m)
   int64_t bsdp, shared_offset, output_bs;
 };
 
@@ -72,6 +73,6 @@ int tile_occupancy(TileId id);
 // at least 64 rows and at least `stages` k-steps per tile) rather than the
 // tile-by-tile loop.
 bool uses_continuous_pipeline(bool int4, int64_t k, int bm, int bk, int stages);
-const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool mx);
+const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool mx, bool fp8);
 
 }  // namespace gmmfr

@@ -1150,22 +1150,28 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-template <int COMBINE>
+// FP8 (B8 = true): the same kernel for FP8 E4M3 weights given (e,n,k) with
+// per-channel scale and per-token pertokenScale as in the int8 mode (no block
+// scales; the instruction's scale operands are 1.0): acc is the fp32 sum and
+// y = ((acc * scale) * pertokenScale) * logit.  Measured on the device: with
+// both operands FP8, B lane l holds column l%32 with the byte layout of A.
+template <int COMBINE, bool B8>
 __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
-  constexpr int BM = 128, BN = 256, BK = 64, STAGES = 4;
+  constexpr int BM = 128, BN = 256, BK = 64, STAGES = B8 ? 3 : 4;
   constexpr int WAVES_N = 2, WTM = 64, WTN = 128, FM = 2, FN = 4;
-  constexpr int A_BYTES = BM * BK;    // fp8: one byte per k
-  constexpr int B_COLB = BK / 2;      // fp4: 32 bytes per column and k-step
+  constexpr int A_BYTES = BM * BK;         // fp8: one byte per k
+  constexpr int B_COLB = B8 ? BK : BK / 2;  // fp8: 64 bytes per column and k-step; fp4: 32
   constexpr int B_BYTES = BN * B_COLB;
   constexpr int A_INSTR = A_BYTES / 16 / kThreads, B_INSTR = B_BYTES / 16 / kThreads;
-  static_assert(A_INSTR == 2 && B_INSTR == 2 && BN == kThreads && BM == kThreads / 2, "copy split");
-  // copies per thread and stage: A, B and one B-scale dword; waves 0-1 add an A-scale dword
-  constexpr int LOADS_LO = A_INSTR + B_INSTR + 2, LOADS_HI = A_INSTR + B_INSTR + 1;
+  static_assert(A_INSTR == 2 && B_INSTR == (B8 ? 4 : 2) && BN == kThreads && BM == kThreads / 2, "copy split");
+  // copies per thread and stage: A, B and (MX) one B-scale dword; waves 0-1 add an A-scale dword
+  constexpr int LOADS_LO = A_INSTR + B_INSTR + (B8 ? 0 : 2), LOADS_HI = A_INSTR + B_INSTR + (B8 ? 0 : 1);
+  constexpr int SC_STAGES = B8 ? 1 : STAGES;  // block-scale staging (MX only)
 
   __shared__ __attribute__((aligned(16))) int8_t sA[STAGES * A_BYTES];
   __shared__ __attribute__((aligned(16))) int8_t sB[STAGES * B_BYTES];
-  __shared__ __attribute__((aligned(16))) uint32_t sSA[STAGES][BM];  // the scale dword of each row
-  __shared__ __attribute__((aligned(16))) uint32_t sSB[STAGES][BN];  // and of each column
+  __shared__ __attribute__((aligned(16))) uint32_t sSA[SC_STAGES][BM];  // the scale dword of each row
+  __shared__ __attribute__((aligned(16))) uint32_t sSB[SC_STAGES][BN];  // and of each column
   extern __shared__ __attribute__((aligned(16))) int32_t s_dyn[];
   int32_t* s_ends = s_dyn;
   int32_t* s_tile_pre = s_dyn + p.e;
@@ -1180,7 +1186,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int64_t k = p.k, n = p.n;
   const int ktiles = (int)(k / BK);
-  const int64_t kdw = k / 128;         // scale dwords per row or column (k % 128 == 0)
+  const int64_t kdw = k / 128;         // MX: scale dwords per row or column (k % 128 == 0)
   const bool lo_wave = wave < 2;       // waves that copy the A-scale dwords (rows 0..127)
   const uint32_t* sa_words = (const uint32_t*)p.pertoken;
   const uint32_t* sb_words = (const uint32_t*)p.scale;
@@ -1200,13 +1206,16 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       const int64_t row = min(c.row0 + r, p.m - 1);  // rows past the group: loaded, never stored
       a_off[q] = (uint32_t)((row - c.row0) * k + ((cpos ^ swz_a<BK>(r)) * 16));
     }
-    b_base = (const int8_t*)uniform64((int64_t)((const int8_t*)p.x2 + ((int64_t)c.g * n + c.col0) * (k / 2)));
+    const int64_t colb = B8 ? k : k / 2;  // bytes of one weight column
+    b_base = (const int8_t*)uniform64((int64_t)((const int8_t*)p.x2 + ((int64_t)c.g * n + c.col0) * colb));
 #pragma unroll
     for (int q = 0; q < B_INSTR; ++q) {
       const int slot = (q * 4 + wave) * 64 + lane;
-      const int r = slot / 2, cpos = slot % 2;
+      const int64_t cpr = B_COLB / 16;  // 16-byte chunks of a column per k-step
+      const int r = slot / cpr, cpos = slot % cpr;
       const int64_t col = min(c.col0 + r, n - 1);    // columns past n: loaded, never stored
-      b_off[q] = (uint32_t)((col - c.col0) * (k / 2) + cpos * 16);
+      // fp8 columns are stored and read like A rows (same swizzle)
+      b_off[q] = (uint32_t)((col - c.col0) * colb + (B8 ? (cpos ^ swz_a<BK>(r)) : cpos) * 16);
     }
     sa_base = (const uint32_t*)uniform64((int64_t)(sa_words + c.row0 * kdw));
     sa_off = (uint32_t)((min(c.row0 + tid, p.m - 1) - c.row0) * kdw * 4);
@@ -1222,9 +1231,12 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
     for (int q = 0; q < B_INSTR; ++q)
       lds_dma16_sv(b_base + (int64_t)kt * B_COLB, b_off[q],
                    __builtin_amdgcn_readfirstlane(lds_addr(sB + st * B_BYTES + (q * 4 + wave) * 64 * 16)));
-    // the dword holding the two block scales of k-step kt (and of its neighbour)
-    lds_dma4_sv(sb_base + kt / 2, sb_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSB[st][wave * 64])));
-    if (lo_wave) lds_dma4_sv(sa_base + kt / 2, sa_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSA[st][wave * 64])));
+    if constexpr (!B8) {
+      // the dword holding the two block scales of k-step kt (and of its neighbour)
+      lds_dma4_sv(sb_base + kt / 2, sb_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSB[st][wave * 64])));
+      if (lo_wave)
+        lds_dma4_sv(sa_base + kt / 2, sa_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSA[st][wave * 64])));
+    }
   };
 
   auto coord = [&](int tt) {
@@ -1282,22 +1294,29 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
         const v4i lo = *(const LDS_PTR(v4i))(a_st + r * BK + ((h ^ swz_a<BK>(r)) << 4));
         const v4i hi = *(const LDS_PTR(v4i))(a_st + r * BK + (((2 + h) ^ swz_a<BK>(r)) << 4));
         af[i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        sa[i] = (int)(sSA[st][r] >> sel);
+        sa[i] = B8 ? 127 : (int)(sSA[B8 ? 0 : st][r] >> sel);
       }
       v8i bf[FN];
 #pragma unroll
       for (int jj = 0; jj < FN; ++jj) {
         const int cl = wn * WTN + jj * 32 + (lane & 31);
-        const v4i w = *(const LDS_PTR(v4i))(b_st + cl * B_COLB + h * 16);
-        bf[jj] = v8i{w.x, w.y, w.z, w.w, 0, 0, 0, 0};
-        sb[jj] = (int)(sSB[st][cl] >> sel);
+        if constexpr (B8) {
+          const v4i lo = *(const LDS_PTR(v4i))(b_st + cl * BK + ((h ^ swz_a<BK>(cl)) << 4));
+          const v4i hi = *(const LDS_PTR(v4i))(b_st + cl * BK + (((2 + h) ^ swz_a<BK>(cl)) << 4));
+          bf[jj] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          sb[jj] = 127;
+        } else {
+          const v4i w = *(const LDS_PTR(v4i))(b_st + cl * B_COLB + h * 16);
+          bf[jj] = v8i{w.x, w.y, w.z, w.w, 0, 0, 0, 0};
+          sb[jj] = (int)(sSB[st][cl] >> sel);
+        }
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int jj = 0; jj < FN; ++jj)
-          acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[jj], acc[i][jj], 0, 4, 0, sa[i], 0,
-                                                                        sb[jj]);
+          acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[jj], acc[i][jj], 0, B8 ? 0 : 4, 0,
+                                                                        sa[i], 0, sb[jj]);
     }
     // epilogue: y = acc * logit, guarded by the tile's valid rows and n
 #pragma unroll
@@ -1308,6 +1327,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
         if (lr >= c.valid_rows) continue;
         const int64_t row = c.row0 + lr;
         const float lg = p.logit ? p.logit[row] : 1.0f;
+        const float pt = (B8 && p.pertoken) ? p.pertoken[row] : 1.0f;
         int64_t d = row;
         if constexpr (COMBINE == kCombineAtomic) {
           d = dest_row(p, row);
@@ -1317,7 +1337,17 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
         for (int jj = 0; jj < FN; ++jj) {
           const int64_t col = c.col0 + wn * WTN + jj * 32 + (lane & 31);
           if (col >= n) continue;
-          const float v = acc[i][jj][r] * lg;
+          float v = acc[i][jj][r];
+          if constexpr (B8) {  // ((acc * scale) * pertokenScale) * logit, each rounded
+            float sc = 1.0f;
+            if (p.scale) {
+              sc = p.scale_bf16 ? __uint_as_float((uint32_t)((const uint16_t*)p.scale)[(int64_t)c.g * n + col] << 16)
+                                : ((const float*)p.scale)[(int64_t)c.g * n + col];
+            }
+            v = v * sc;
+            v = v * pt;
+          }
+          v = v * lg;
           if constexpr (COMBINE == kCombineOrdered)
             __builtin_nontemporal_store(v, p.y + row * n + col);
           else
@@ -1545,8 +1575,9 @@ bool uses_continuous_pipeline(bool int4, int64_t k, int bm, int bk, int stages) 
   return bm >= 64 && k / bk >= stages;
 }
 
-const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool mx) {
+const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool mx, bool fp8) {
   if (mx) return "mx_gemm_kernel<128,256,64,2x2,s4,fp8xfp4>";
+  if (fp8) return "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8>";
   // per tile: i8, i4, i8 cont, i4 cont, i8 transposed weights, i8 cont transposed weights
   static const char* names[kNumTiles][6] = {
       {"gmm_kernel<256,256,64,2x2,s3,i8>", "gmm_kernel<256,256,64,2x2,s3,i4>", "gmm_kernel<256,256,64,2x2,s3,i8,cont>",
@@ -1679,9 +1710,14 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
     const size_t dyn = ((size_t)(2 * kp.e + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
     if (a.mx) {
       if (kp.combine == kCombineOrdered)
-        hipLaunchKernelGGL(mx_gemm_kernel<kCombineOrdered>, dim3(plan.grid), dim3(kThreads), dyn, s, kp);
+        hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, false>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
       else
-        hipLaunchKernelGGL(mx_gemm_kernel<kCombineAtomic>, dim3(plan.grid), dim3(kThreads), dyn, s, kp);
+        hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, false>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
+    } else if (a.fp8) {
+      if (kp.combine == kCombineOrdered)
+        hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, true>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
+      else
+        hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, true>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
     } else switch (plan.tile) {
       case kTile256x256: launch_gemm<256, 256, 64, 2, 2, 3, 1>(kp, a.int4, a.trans_b, plan.grid, s); break;
       case kTile128x256: launch_gemm<128, 256, 64, 2, 2, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;

@@ -87,6 +87,8 @@ class Problem:
     seed: int = 0
     counts: Optional[np.ndarray] = None  # rows per expert (for statistics)
     x2_transposed: bool = False          # True -> int8 x2 is given as (e,n,k)
+    fp8: bool = False                    # FP8 mode: x1 uint8 FP8-E4M3 codes (m,k), x2 uint8 codes (e,n,k);
+                                         # scale and pertoken_scale as in the int8 mode
     mx: bool = False                     # MxA8W4: x1 uint8 FP8-E4M3 codes (m,k); x2 uint8 (e,n,k/2)
                                          # FP4-E2M1 pairs (low nibble = even k); pertoken_scale uint8
                                          # E8M0 (m,k/64,2); scale uint8 E8M0 (e,n,k/64,2)
@@ -336,7 +338,7 @@ def mx_problem(seed: int, m: int, k: int, n: int, e: int, *, group_list_type: in
         shared = f32_to_bf16_bits(rng.standard_normal((bsdp, n)).astype(np.float32) * 64.0)
     return Problem(f"mx{seed}", m, k, n, e, x1, x2, False, scale, False, pts, logit,
                    _group_list(counts, group_list_type), group_list_type, ri, shared, shared_offset, output_bs,
-                   seed, counts, True, True)
+                   seed, counts, True, mx=True)
 
 
 def make_mx_config(name: str = "mxa8w4", seed: int = 0) -> Problem:
@@ -358,4 +360,57 @@ def make_mx_config(name: str = "mxa8w4", seed: int = 0) -> Problem:
     scale = _e8m0(rng, (e, n, k // 64, 2))
     shared = f32_to_bf16_bits(rng.standard_normal((8192, n)).astype(np.float32))
     return Problem(name, m, k, n, e, x1, x2, False, scale, False, pts, logit,
-                   _group_list(counts, 0), 0, ri, shared, 4096, obs, seed, counts, True, True)
+                   _group_list(counts, 0), 0, ri, shared, 4096, obs, seed, counts, True, mx=True)
+
+
+def fp8_problem(seed: int, m: int, k: int, n: int, e: int, *, scale_bf16: bool = False, group_list_type: int = 0,
+                with_scale: bool = True, with_pts: bool = True, with_logit: bool = True,
+                with_row_index: bool = True, bsdp: int = 0, shared_offset: int = 0,
+                output_bs: Optional[int] = None, empty_frac: float = 0.25, uncovered: int = 0) -> Problem:
+    """A random FP8 problem: FP8 E4M3 activations and weights (e,n,k), fp32 or
+    bf16 per-channel scale, fp32 per-token scale."""
+    rng = np.random.default_rng(seed)
+    covered = m - uncovered
+    w = rng.uniform(0.2, 1.0, size=e) * (rng.uniform(size=e) >= empty_frac)
+    if w.sum() == 0:
+        w[rng.integers(e)] = 1.0
+    counts = _largest_remainder(w, covered) if covered > 0 else np.zeros(e, dtype=np.int64)
+    if output_bs is None:
+        output_bs = max(1, m // 2)
+    ri = rng.integers(0, output_bs, size=m).astype(np.int64) if with_row_index else None
+    logit = rng.uniform(0.0, 1.0, size=m).astype(np.float32) if with_logit else None
+    x1 = _fp8_codes(rng, (m, k))
+    x2 = _fp8_codes(rng, (e, n, k))
+    scale = None
+    if with_scale:
+        sc = rng.uniform(0.25, 2.0, size=(e, 1, n)).astype(np.float32)
+        scale = f32_to_bf16_bits(sc) if scale_bf16 else sc
+    pts = rng.uniform(0.25, 2.0, size=m).astype(np.float32) if with_pts else None
+    shared = None
+    if bsdp > 0:
+        shared = f32_to_bf16_bits(rng.standard_normal((bsdp, n)).astype(np.float32) * 64.0)
+    return Problem(f"fp8{seed}", m, k, n, e, x1, x2, False, scale, scale_bf16 and with_scale, pts, logit,
+                   _group_list(counts, group_list_type), group_list_type, ri, shared, shared_offset, output_bs,
+                   seed, counts, True, fp8=True)
+
+
+def make_fp8_config(name: str = "fp8", seed: int = 0) -> Problem:
+    """FP8 E4M3 at the prefill shape: routing, logit, bf16 per-channel scale,
+    pertokenScale and sharedInput drawn as for the prefill workload; FP8
+    activations and weights (e,n,k) drawn like the MxA8W4 activations."""
+    if name != "fp8":
+        raise ValueError(name)
+    rng = np.random.default_rng(seed)
+    T, K, e, k, n, obs = 16384, 8, 32, 2048, 7168, 16384
+    m = T * K
+    u = rng.uniform(-0.2, 0.2, size=e)
+    counts = _largest_remainder(4096.0 * (1.0 + u), m)
+    ri = _row_index(rng, T, K, np.int64)
+    logit = _topk_softmax_logit(rng, T, K, ri)
+    x1 = _fp8_codes(rng, (m, k))
+    x2 = _fp8_codes(rng, (e, n, k))
+    scale = f32_to_bf16_bits(rng.uniform(1e-3, 1e-2, size=(e, 1, n)).astype(np.float32))
+    pts = rng.uniform(1e-3, 1e-2, size=m).astype(np.float32)
+    shared = f32_to_bf16_bits(rng.standard_normal((8192, n)).astype(np.float32))
+    return Problem(name, m, k, n, e, x1, x2, False, scale, True, pts, logit,
+                   _group_list(counts, 0), 0, ri, shared, 4096, obs, seed, counts, True, fp8=True)

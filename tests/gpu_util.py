@@ -26,6 +26,17 @@ def to_device(p, dev="cuda"):
             "row_index": T(p.row_index),
             "shared_input": bf16(p.shared_input),
         }
+    if getattr(p, "fp8", False):
+        return {
+            "x1": T(p.x1).view(torch.float8_e4m3fn),
+            "x2": T(p.x2).view(torch.float8_e4m3fn),
+            "scale": None if p.scale is None else (bf16(p.scale) if p.scale_bf16 else T(p.scale)),
+            "pertoken_scale": T(p.pertoken_scale),
+            "logit": T(p.logit),
+            "group_list": T(p.group_list),
+            "row_index": T(p.row_index),
+            "shared_input": bf16(p.shared_input),
+        }
     return {
         "x1": T(p.x1),
         "x2": T(p.x2),

@@ -66,3 +66,37 @@ def test_mx_workload_sampled_rows():
     _check(p, out.cpu().numpy()[dsel], ref, bound)
     out2, _ = G.run_gpu(p, d, deterministic=False, combine="atomic")
     _check(p, out2.cpu().numpy()[dsel], ref, bound)
+
+
+# ---------------------------------------------------------------- FP8 mode
+
+FP8_CASES = {
+    "ragged_bf16_shared": dict(seed=11, m=300, k=256, n=272, e=3, scale_bf16=True, output_bs=200, bsdp=40,
+                               shared_offset=7),
+    "counts_uncovered": dict(seed=12, m=700, k=192, n=528, e=5, group_list_type=1, uncovered=13, output_bs=333),
+    "no_factors_identity": dict(seed=13, m=257, k=64, n=16, e=2, with_scale=False, with_pts=False,
+                                with_logit=False, with_row_index=False, output_bs=257),
+    "many_empty": dict(seed=14, m=900, k=128, n=256, e=40, empty_frac=0.7, output_bs=300),
+    "long_k": dict(seed=15, m=400, k=2048, n=320, e=2, output_bs=150, bsdp=20, shared_offset=100),
+}
+
+
+@pytest.mark.parametrize("name", list(FP8_CASES), ids=list(FP8_CASES))
+def test_fp8_random_case_all_elements(name):
+    p = W.fp8_problem(**FP8_CASES[name])
+    ref, bound, _ = MX.run(p)
+    d = G.to_device(p)
+    for det, combine in ((True, "auto"), (False, "atomic")):
+        out, _ = G.run_gpu(p, d, deterministic=det, combine=combine)
+        _check(p, out.cpu().numpy(), ref, bound)
+
+
+def test_fp8_workload_sampled_rows():
+    p = W.make_fp8_config("fp8", 0)
+    rng = np.random.default_rng(101)
+    dsel = np.array(sorted(set(rng.choice(p.output_bs, size=24, replace=False).tolist())
+                           | {0, p.output_bs - 1, 4095, 4096, 12287, 12288}), dtype=np.int64)
+    ref, bound = MX.out_rows(p, dsel)
+    d = G.to_device(p)
+    out, _ = G.run_gpu(p, d, deterministic=True)
+    _check(p, out.cpu().numpy()[dsel], ref, bound)

@@ -196,3 +196,61 @@ def test_bound_covers_the_block_alignment_model():
                 continue
             y = (_block_truncated_acc(p, rows, g, keep) * L[rows, None].astype(np.float32)).astype(np.float64)
             assert (np.abs(y - out[rows]) <= bound[rows]).all(), keep
+
+
+# ---------------------------------------------------------------- FP8 mode (x1 and x2 FP8 E4M3)
+
+@pytest.mark.parametrize("seed", [21, 22])
+def test_fp8_brute_force_matches_oracle(seed):
+    p = W.fp8_problem(seed, 9, 64, 6, 3, empty_frac=0.2, output_bs=5, bsdp=2, shared_offset=1)
+    _, _, acc = MX.run(p)
+    assert np.allclose(acc, MX.brute(p), rtol=1e-12, atol=0.0)
+
+
+def test_fp8_integer_inputs_agree_with_the_int8_oracle():
+    """Integer-valued FP8 activations and weights compute the integer GEMM:
+    acc equals the int8 oracle's int32 accumulator, and y (= the output with
+    identity routing) agrees with the int8 oracle's fp32 epilogue to within
+    its three roundings."""
+    rng = np.random.default_rng(23)
+    fp8, _ = _int_codes()
+    vals = np.array(sorted(fp8))
+    codes = np.array([fp8[v] for v in sorted(fp8)], dtype=np.uint8)
+    p = W.fp8_problem(24, 60, 128, 40, 3, output_bs=60, with_row_index=False, scale_bf16=True)
+    a_idx = rng.integers(0, len(vals), size=(p.m, p.k))
+    w_idx = rng.integers(0, len(vals), size=(p.e, p.n, p.k))
+    p.x1, p.x2 = codes[a_idx], codes[w_idx]
+    out, _, acc = MX.run(p)
+    q = W.Problem("int", p.m, p.k, p.n, p.e, vals[a_idx].astype(np.int8),
+                  np.ascontiguousarray(np.transpose(vals[w_idx], (0, 2, 1))).astype(np.int8), False, p.scale, True,
+                  p.pertoken_scale, p.logit, p.group_list, p.group_list_type, None, None, 0, p.output_bs, 0, p.counts)
+    iout, iacc = oracle.run(q)
+    s, e = MX.group_ranges(p)
+    cov = np.zeros(p.m, dtype=bool)
+    for a, b in zip(s, e):
+        cov[a:b] = True
+    assert (acc[cov] == iacc[cov].astype(np.float64)).all()
+    rel = np.abs(iout[cov].astype(np.float64) - out[cov]) / np.maximum(np.abs(out[cov]), 1e-30)
+    assert rel.max() <= 4 * 2.0 ** -24
+
+
+def test_fp8_bound_covers_fp32_evaluation():
+    p = W.fp8_problem(25, 50, 256, 24, 2, output_bs=18, bsdp=4, shared_offset=2)
+    out, bound, _ = MX.run(p)
+    s, e = MX.group_ranges(p)
+    ri = np.asarray(p.row_index)
+    y = np.zeros((p.m, p.n), dtype=np.float32)
+    for g in range(p.e):
+        rows = np.arange(s[g], e[g])
+        if rows.size == 0:
+            continue
+        acc = _block_truncated_acc(p, rows, g, 13)
+        S = np.asarray(p.scale, dtype=np.float32)[g, 0]
+        v = (acc * S[None, :]).astype(np.float32)
+        v = (v * np.asarray(p.pertoken_scale, dtype=np.float32)[rows, None]).astype(np.float32)
+        y[rows] = (v * np.asarray(p.logit, dtype=np.float32)[rows, None]).astype(np.float32)
+    got = np.stack([MX._seed_row(p, d) for d in range(p.output_bs)]).astype(np.float32)
+    for i in range(int(e[-1])):
+        got[ri[i]] = (got[ri[i]] + y[i]).astype(np.float32)
+    assert (np.abs(got.astype(np.float64) - out) <= bound).all()
+    assert bound.max() <= 0.05 * np.abs(out).max()
