@@ -123,7 +123,9 @@ typedef struct {
   /* bias, offset, antiquantScale, antiquantOffset: reserved by the operator
    * ("pass a null pointer"); must be absent, else UNSUPPORTED.                 */
   gmmfr_tensor bias, offset, antiquant_scale, antiquant_offset;
-  /* pertokenScale: FLOAT32 (m).                                        optional
+  /* pertokenScale: FLOAT32 (m) per-token scale, or FLOAT32 (1): one static
+   * per-tensor activation scale applied to every row (function description:
+   * Atlas 350 static pertensor-perchannel quantisation).             optional
    * MX: FLOAT8_E8M0 (m,k/64,2), the block scale of x1 for each 32 k of each
    * row.                                                                required */
   gmmfr_tensor pertoken_scale;

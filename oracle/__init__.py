@@ -49,6 +49,7 @@ class _Problem(ctypes.Structure):
         ("bsdp", ctypes.c_int64),
         ("shared_input_offset", ctypes.c_int64),
         ("output_bs", ctypes.c_int64),
+        ("pertoken_per_tensor", ctypes.c_int32),
     ]
 
 
@@ -93,6 +94,9 @@ def _c_problem(p, keep):
     if p.scale is not None:
         scale = arr(p.scale, np.uint16 if p.scale_bf16 else np.float32)
     pts = arr(p.pertoken_scale, np.float32)
+    # pertokenScale (m) per token, or (1): one static per-tensor scale
+    if pts is not None and pts.shape != (int(p.m),) and pts.shape != (1,):
+        raise OracleError(3)
     logit = arr(p.logit, np.float32)
     gl = arr(p.group_list, np.int64)
     ri = None
@@ -109,6 +113,7 @@ def _c_problem(p, keep):
     c.scale = _ptr(scale)
     c.scale_type = (ORC_BF16 if p.scale_bf16 else ORC_F32) if scale is not None else ORC_NONE
     c.pertoken_scale = _ptr(pts)
+    c.pertoken_per_tensor = int(pts is not None and pts.shape == (1,))
     c.logit = _ptr(logit)
     c.group_list = _ptr(gl)
     c.group_list_type = int(p.group_list_type)

@@ -85,7 +85,8 @@ def brute(p):
         d = i if p.row_index is None else int(p.row_index[i])
         if not 0 <= d < p.output_bs:
             raise ValueError("rowIndex outside the output")
-        P = F32(1.0) if p.pertoken_scale is None else F32(p.pertoken_scale[i])
+        # per token, or one static per-tensor value for every row
+        P = F32(1.0) if p.pertoken_scale is None else F32(p.pertoken_scale[i if len(p.pertoken_scale) > 1 else 0])
         L = F32(1.0) if p.logit is None else F32(p.logit[i])
         for j in range(n):
             y = F32(int(acc[i, j]))

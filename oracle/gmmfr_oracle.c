@@ -61,11 +61,13 @@ static float scale_at(const orc_problem* p, int64_t g, int64_t j) {
 /* Step 4: y = ((float(acc) * S_g[j]) * P_i) * L_i, each product rounded to
  * fp32.  The (acc * deqScale) * perTokenScale order is the one the worked
  * example of "matmul支持pertoken量化模式" spells out; the routing weight
- * (logit) comes last.  A missing factor is 1.0, and x * 1.0f == x exactly. */
+ * (logit) comes last.  A missing factor is 1.0, and x * 1.0f == x exactly.
+ * A per-tensor pertokenScale ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2",
+ * function description: static pertensor-perchannel) is P_i = P_0 for all i. */
 static float dequant(const orc_problem* p, int64_t g, int64_t i, int64_t j, int32_t acc) {
   float y = (float)acc;             /* int32 -> fp32, round to nearest even */
   y = y * scale_at(p, g, j);
-  y = y * (p->pertoken_scale ? p->pertoken_scale[i] : 1.0f);
+  y = y * (p->pertoken_scale ? p->pertoken_scale[p->pertoken_per_tensor ? 0 : i] : 1.0f);
   y = y * (p->logit ? p->logit[i] : 1.0f);
   return y;
 }

@@ -67,6 +67,8 @@ typedef struct {
   int64_t bsdp;
   int64_t shared_input_offset;
   int64_t output_bs;
+  int32_t pertoken_per_tensor; /* 1: pertoken_scale holds one value, used for every
+                                * row (static per-tensor activation scale)     */
 } orc_problem;
 
 /* Whole computation: out (output_bs,n) fp32, fully written; acc (m,n) int32

@@ -146,7 +146,11 @@ def _post(p, rows, g):
     L = np.ones(len(rows)) if p.logit is None else np.asarray(p.logit, dtype=np.float64)[rows]
     if not _is_fp8(p):
         return np.repeat(L[:, None], p.n, axis=1), 1
-    P = np.ones(len(rows)) if p.pertoken_scale is None else np.asarray(p.pertoken_scale, dtype=np.float64)[rows]
+    if p.pertoken_scale is None:
+        P = np.ones(len(rows))
+    else:  # per token, or one static per-tensor value for every row
+        pts = np.asarray(p.pertoken_scale, dtype=np.float64)
+        P = pts[rows] if len(pts) > 1 else np.full(len(rows), pts[0])
     if p.scale is None:
         S = np.ones(p.n)
     elif p.scale_bf16:

@@ -25,6 +25,7 @@ struct Derived {
   bool mx;       // MxA8W4: FP8 x1, FP4 x2 (e,n,k), E8M0 block scales
   bool fp8;      // FP8 x1 and x2 (e,n,k), per-channel scale, per-token pertokenScale
   bool scale_bf16;
+  bool pts_scalar;  // pertokenScale of shape (1): one static per-tensor activation scale
   bool row_index_i32;
 };
 
@@ -133,6 +134,7 @@ int validate_mx(const gmmfr_args* a, Derived* d) {
     d->mx = true;
     d->fp8 = false;
     d->scale_bf16 = false;
+    d->pts_scalar = false;
     d->row_index_i32 = false;
   }
   return GMMFR_OK;
@@ -169,7 +171,10 @@ int validate_fp8(const gmmfr_args* a, Derived* d) {
   if (n < 16 || n % 16 != 0) return GMMFR_ERR_SHAPE;
   if (n > (int64_t(1) << 24) || m * n >= (int64_t(1) << 40)) return GMMFR_ERR_SHAPE;
   if (present(a->scale) && !dims_are(a->scale, 3, e, 1, n)) return GMMFR_ERR_SHAPE;
-  if (present(a->pertoken_scale) && !dims_are(a->pertoken_scale, 1, m)) return GMMFR_ERR_SHAPE;
+  // pertokenScale (m) per token, or (1): the static per-tensor activation
+  // scale (function description: Atlas 350 static pertensor-perchannel)
+  if (present(a->pertoken_scale) && !dims_are(a->pertoken_scale, 1, m) && !dims_are(a->pertoken_scale, 1, 1))
+    return GMMFR_ERR_SHAPE;
   if (!dims_are(a->group_list, 1, e)) return GMMFR_ERR_SHAPE;
   if (present(a->logit) && !dims_are(a->logit, 1, m)) return GMMFR_ERR_SHAPE;
   if (present(a->row_index) && !dims_are(a->row_index, 1, m)) return GMMFR_ERR_SHAPE;
@@ -187,6 +192,7 @@ int validate_fp8(const gmmfr_args* a, Derived* d) {
     d->mx = false;
     d->fp8 = true;
     d->scale_bf16 = present(a->scale) && a->scale.dtype == GMMFR_DT_BFLOAT16;
+    d->pts_scalar = present(a->pertoken_scale) && a->pertoken_scale.dims[0] == 1;
     d->row_index_i32 = false;
   }
   return GMMFR_OK;
@@ -245,7 +251,10 @@ int validate(const gmmfr_args* a, Derived* d) {
   if (n < 16 || n % 16 != 0 || (int4 && n % 32 != 0)) return GMMFR_ERR_SHAPE;
   if (n > (int64_t(1) << 24) || m * n >= (int64_t(1) << 40)) return GMMFR_ERR_SHAPE;
   if (present(a->scale) && !dims_are(a->scale, 3, e, 1, n)) return GMMFR_ERR_SHAPE;
-  if (present(a->pertoken_scale) && !dims_are(a->pertoken_scale, 1, m)) return GMMFR_ERR_SHAPE;
+  // pertokenScale (m) per token, or (1): the static per-tensor activation
+  // scale (function description: Atlas 350 static pertensor-perchannel)
+  if (present(a->pertoken_scale) && !dims_are(a->pertoken_scale, 1, m) && !dims_are(a->pertoken_scale, 1, 1))
+    return GMMFR_ERR_SHAPE;
   if (!dims_are(a->group_list, 1, e)) return GMMFR_ERR_SHAPE;
   if (present(a->logit) && !dims_are(a->logit, 1, m)) return GMMFR_ERR_SHAPE;
   if (present(a->row_index) && !dims_are(a->row_index, 1, m)) return GMMFR_ERR_SHAPE;
@@ -266,6 +275,7 @@ int validate(const gmmfr_args* a, Derived* d) {
     d->mx = false;
     d->fp8 = false;
     d->scale_bf16 = present(a->scale) && a->scale.dtype == GMMFR_DT_BFLOAT16;
+    d->pts_scalar = present(a->pertoken_scale) && a->pertoken_scale.dims[0] == 1;
     d->row_index_i32 = present(a->row_index) && a->row_index.dtype == GMMFR_DT_INT32;
   }
   return GMMFR_OK;
@@ -344,6 +354,7 @@ LaunchArgs to_launch(const gmmfr_args* a, const Derived& d) {
   l.e = (int32_t)d.e;
   l.group_list_type = (int32_t)a->group_list_type;
   l.scale_bf16 = d.scale_bf16;
+  l.pertoken_scalar = d.pts_scalar;
   l.row_index_i32 = d.row_index_i32;
   l.int4 = d.int4;
   l.trans_b = d.trans_b;

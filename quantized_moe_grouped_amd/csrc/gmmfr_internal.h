@@ -29,7 +29,7 @@ struct LaunchArgs {
   const int8_t* x1;
   const void* x2;            // int8 (e,k,n), int8 (e,n,k) when trans_b, or packed int4 (e,k,n/8) words
   const void* scale;         // f32 / bf16 (e,1,n) or nullptr
-  const float* pertoken;     // (m) or nullptr
+  const float* pertoken;     // (m), (1) when pertoken_scalar, or nullptr
   const float* logit;        // (m) or nullptr
   const int64_t* group_list; // (e)
   const void* row_index;     // int64 / int32 (m) or nullptr (identity)
@@ -40,6 +40,7 @@ struct LaunchArgs {
   int32_t e;
   int32_t group_list_type;
   int32_t scale_bf16;
+  int32_t pertoken_scalar;   // one pertokenScale value for every row
   int32_t row_index_i32;
   int32_t int4;
   int32_t trans_b;           // int8 weights given as (e,n,k)

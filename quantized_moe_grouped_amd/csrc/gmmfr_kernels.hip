@@ -46,6 +46,7 @@ struct KParams {
   int64_t m, k, n;
   int64_t bsdp, shared_offset, output_bs;
   int32_t e, group_list_type, scale_bf16, row_index_i32;
+  int32_t pertoken_scalar;  // pertoken holds one value for every row
   int32_t n_tiles_n;
   int32_t combine;
   int32_t* tile_ctr;    // per-XCD tile queues (kTileQueues counters, 64 bytes apart), zeroed before the GEMM
@@ -370,10 +371,14 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t s_scale[2][BN];
 
   // An absent pertokenScale or logit reads as 1.0 from LDS (the copies below
-  // skip it), so the epilogue reads row factors without branching; the
-  // barriers of the table build publish the fill.
-  if (!p.pertoken)
-    for (int i = threadIdx.x; i < 2 * BM; i += kThreads) (&s_pts[0][0])[i] = 1.0f;
+  // skip it), so the epilogue reads row factors without branching; a
+  // per-tensor pertokenScale is filled in once the same way.  The barriers
+  // of the table build publish the fill.
+  const bool pts_rows = p.pertoken && !p.pertoken_scalar;
+  if (!pts_rows) {
+    const float v = p.pertoken ? p.pertoken[0] : 1.0f;
+    for (int i = threadIdx.x; i < 2 * BM; i += kThreads) (&s_pts[0][0])[i] = v;
+  }
   if (!p.logit)
     for (int i = threadIdx.x; i < 2 * BM; i += kThreads) (&s_logit[0][0])[i] = 1.0f;
   build_group_table(p, BM, s_ends, s_tile_pre, s_scan);
@@ -538,7 +543,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   uint32_t fr_pts = 0x3F800000u, fr_logit = 0x3F800000u, fr_ridx0 = 0, fr_ridx1 = 0, fr_scale = 0;
   auto fetch_rows = [&](const TileCoord& c) {
     if (tid < BM) {
-      if (p.pertoken) fr_pts = ((const uint32_t*)p.pertoken)[row_word_src(c, tid, 1)];
+      if (pts_rows) fr_pts = ((const uint32_t*)p.pertoken)[row_word_src(c, tid, 1)];
       if (p.logit) fr_logit = ((const uint32_t*)p.logit)[row_word_src(c, tid, 1)];
     }
     const uint32_t* ri = (const uint32_t*)p.row_index;
@@ -548,7 +553,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   };
   auto store_rows = [&](int pb) {
     if (tid < BM) {
-      s_pts[pb][tid] = __uint_as_float(fr_pts);
+      if (pts_rows) s_pts[pb][tid] = __uint_as_float(fr_pts);
       s_logit[pb][tid] = __uint_as_float(fr_logit);
     }
     if (tid < ridx_words) s_ridx[pb][tid] = fr_ridx0;
@@ -573,7 +578,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       }
     };
     auto row_off = [&](int q, int wpr) { return (int)(min(c.row0 + q / wpr, p.m - 1) - c.row0) * wpr + q % wpr; };
-    if (p.pertoken)
+    if (pts_rows)
       words((const uint32_t*)p.pertoken + c.row0, (uint32_t*)s_pts[pb], BM, [&](int q) { return row_off(q, 1); });
     if (p.logit)
       words((const uint32_t*)p.logit + c.row0, (uint32_t*)s_logit[pb], BM, [&](int q) { return row_off(q, 1); });
@@ -1327,7 +1332,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
         if (lr >= c.valid_rows) continue;
         const int64_t row = c.row0 + lr;
         const float lg = p.logit ? p.logit[row] : 1.0f;
-        const float pt = (B8 && p.pertoken) ? p.pertoken[row] : 1.0f;
+        const float pt = (B8 && p.pertoken) ? p.pertoken[p.pertoken_scalar ? 0 : row] : 1.0f;
         int64_t d = row;
         if constexpr (COMBINE == kCombineAtomic) {
           d = dest_row(p, row);
@@ -1674,6 +1679,7 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
   kp.e = a.e;
   kp.group_list_type = a.group_list_type;
   kp.scale_bf16 = a.scale_bf16;
+  kp.pertoken_scalar = a.pertoken_scalar;
   kp.row_index_i32 = a.row_index_i32;
   kp.n_tiles_n = (int32_t)((a.n + ts.bn - 1) / ts.bn);
   kp.combine = plan.combine;

@@ -289,6 +289,15 @@ def with_transposed_weights(p: Problem) -> Problem:
                                name=p.name + "-tb")
 
 
+
+def with_per_tensor_scale(p: Problem, value: float | None = None) -> Problem:
+    """The same problem with one static per-tensor activation scale in place of
+    the per-token pertokenScale: its first entry, or ``value``."""
+    if value is None:
+        value = float(p.pertoken_scale[0]) if p.pertoken_scale is not None and len(p.pertoken_scale) else 0.005
+    return dataclasses.replace(p, pertoken_scale=np.array([value], dtype=np.float32), name=p.name + "-pt")
+
+
 # ---------------------------------------------------------------- MxA8W4 inputs
 
 

@@ -164,6 +164,7 @@ CASES = [
     ("scale_shape", dict(scale=_fake(B.DT_FLOAT32, 8, 7168)), B.ERR_SHAPE),
     ("group_list_len", dict(group_list=_fake(B.DT_INT64, 7)), B.ERR_SHAPE),
     ("pts_len", dict(pertoken_scale=_fake(B.DT_FLOAT32, 511)), B.ERR_SHAPE),
+    ("pts_len_two", dict(pertoken_scale=_fake(B.DT_FLOAT32, 2)), B.ERR_SHAPE),
     ("out_rows", dict(out=_fake(B.DT_FLOAT32, 255, 7168)), B.ERR_SHAPE),
     ("shared_too_tall", dict(shared_input=_fake(B.DT_BFLOAT16, 257, 7168)), B.ERR_ATTR),
     ("shared_offset", dict(shared_input=_fake(B.DT_BFLOAT16, 128, 7168), shared_input_offset=129), B.ERR_ATTR),
@@ -192,6 +193,14 @@ def test_transposed_weights_accepted():
     assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
     assert info.gemm_kernel.decode().endswith(",tb>")
 
+
+
+def test_per_tensor_pertoken_scale_accepted():
+    """pertokenScale of shape (1): the static per-tensor activation scale
+    (function description: static pertensor-perchannel)."""
+    a = _args()
+    a.pertoken_scale = _fake(B.DT_FLOAT32, 1)
+    assert _ws(a)[0] == B.OK
 
 def test_int4_shapes_accepted_and_checked():
     assert _ws(_args(int4=True))[0] == B.OK
@@ -252,3 +261,60 @@ def test_make_args_keepalive_holds_every_tensor():
     del keep
     gc.collect()
     assert ref() is None
+
+
+# ---------------------------------------------------------------- MxA8W4 and FP8 modes
+
+def _mx_args(m=512, k=2048, n=7168, e=8, obs=256, **over):
+    """MxA8W4 (Atlas 350 MxA8W4 notes): FP8 x1, FP4 x2 (e,n,k/2 bytes),
+    E8M0 block scales (m,k/64,2) and (e,n,k/64,2), transpose_x2 = 1."""
+    a = _args(m=m, k=k, n=n, e=e, obs=obs)
+    a.x1 = _fake(B.DT_FLOAT8_E4M3FN, m, k)
+    a.x2 = _fake(B.DT_FLOAT4_E2M1X2, e, n, k // 2)
+    a.scale = _fake(B.DT_FLOAT8_E8M0, e, n, k // 64, 2)
+    a.pertoken_scale = _fake(B.DT_FLOAT8_E8M0, m, k // 64, 2)
+    a.transpose_x2 = 1
+    for key, v in over.items():
+        setattr(a, key, v)
+    return a
+
+
+def _fp8_args(m=512, k=2048, n=7168, e=8, obs=256, **over):
+    """FP8 E4M3 x1 and x2 (e,n,k), per-channel scale, per-token pertokenScale."""
+    a = _args(m=m, k=k, n=n, e=e, obs=obs)
+    a.x1 = _fake(B.DT_FLOAT8_E4M3FN, m, k)
+    a.x2 = _fake(B.DT_FLOAT8_E4M3FN, e, n, k)
+    a.transpose_x2 = 1
+    for key, v in over.items():
+        setattr(a, key, v)
+    return a
+
+
+MX_CASES = [
+    ("mx_ok", _mx_args, {}, B.OK),
+    ("mx_no_pertoken", _mx_args, dict(pertoken_scale=B.Tensor()), B.ERR_NULLPTR),
+    ("mx_no_scale", _mx_args, dict(scale=B.Tensor()), B.ERR_NULLPTR),
+    ("mx_pertoken_fp32", _mx_args, dict(pertoken_scale=_fake(B.DT_FLOAT32, 512, 32, 2)), B.ERR_DTYPE),
+    ("mx_per_tensor_pertoken", _mx_args, dict(pertoken_scale=_fake(B.DT_FLOAT8_E8M0, 1)), B.ERR_SHAPE),
+    ("mx_row_index_i32", _mx_args, dict(row_index=_fake(B.DT_INT32, 512)), B.ERR_DTYPE),
+    ("mx_untransposed", _mx_args, dict(transpose_x2=0), B.ERR_ATTR),
+    ("mx_acc_dump", _mx_args, dict(acc_out=_fake(B.DT_INT32, 512, 7168)), B.ERR_UNSUPPORTED),
+    ("mx_k_not_mult_128", _mx_args, dict(x1=_fake(B.DT_FLOAT8_E4M3FN, 512, 2112),
+                                         x2=_fake(B.DT_FLOAT4_E2M1X2, 8, 7168, 1056)), B.ERR_SHAPE),
+    ("mx_scale_shape", _mx_args, dict(scale=_fake(B.DT_FLOAT8_E8M0, 8, 7168, 64)), B.ERR_SHAPE),
+    ("fp8_ok", _fp8_args, {}, B.OK),
+    ("fp8_per_tensor_pertoken", _fp8_args, dict(pertoken_scale=_fake(B.DT_FLOAT32, 1)), B.OK),
+    ("fp8_pertoken_len", _fp8_args, dict(pertoken_scale=_fake(B.DT_FLOAT32, 2)), B.ERR_SHAPE),
+    ("fp8_bf16_scale", _fp8_args, dict(scale=_fake(B.DT_BFLOAT16, 8, 1, 7168)), B.OK),
+    ("fp8_untransposed", _fp8_args, dict(transpose_x2=0, x2=_fake(B.DT_FLOAT8_E4M3FN, 8, 2048, 7168)),
+     B.ERR_UNSUPPORTED),
+    ("fp8_row_index_i32", _fp8_args, dict(row_index=_fake(B.DT_INT32, 512)), B.ERR_DTYPE),
+    ("fp8_acc_dump", _fp8_args, dict(acc_out=_fake(B.DT_INT32, 512, 7168)), B.ERR_UNSUPPORTED),
+    ("fp8_x2_int8", _fp8_args, dict(x2=_fake(B.DT_INT8, 8, 7168, 2048)), B.ERR_DTYPE),
+]
+
+
+@pytest.mark.parametrize("name,make,over,code", MX_CASES, ids=[c[0] for c in MX_CASES])
+def test_mx_and_fp8_stage_one(name, make, over, code):
+    st, _ = _ws(make(**over))
+    assert st == code, (B.STATUS_NAMES.get(st), B.STATUS_NAMES.get(code))

@@ -91,6 +91,17 @@ def test_fp8_random_case_all_elements(name):
         _check(p, out.cpu().numpy(), ref, bound)
 
 
+
+@pytest.mark.parametrize("name", ["ragged_bf16_shared", "many_empty"])
+def test_fp8_per_tensor_scale(name):
+    """pertokenScale of shape (1): one static per-tensor activation scale."""
+    p = W.with_per_tensor_scale(W.fp8_problem(**FP8_CASES[name]))
+    ref, bound, _ = MX.run(p)
+    d = G.to_device(p)
+    for det, combine in ((True, "auto"), (False, "atomic")):
+        out, _ = G.run_gpu(p, d, deterministic=det, combine=combine)
+        _check(p, out.cpu().numpy(), ref, bound)
+
 def test_fp8_workload_sampled_rows():
     p = W.make_fp8_config("fp8", 0)
     rng = np.random.default_rng(101)

@@ -103,6 +103,22 @@ def test_random_case_transposed_weights(name):
     _check_full(p, hints=(None, 8, 100, 300, (0, 256)))
 
 
+
+# one static per-tensor activation scale (function description: static
+# pertensor-perchannel): pertokenScale of shape (1)
+PT_CASES = ["ragged_n_shared", "int4", "many_empty_experts", "single_row", "long_k_i32_index_bf16_shared"]
+
+
+@pytest.mark.parametrize("name", PT_CASES, ids=PT_CASES)
+def test_random_case_per_tensor_scale(name):
+    p = W.with_per_tensor_scale(W.random_problem(**CASES[name]))
+    _check_full(p, hints=(None, 8, 300, (0, 256)))
+
+
+def test_per_tensor_scale_transposed_weights():
+    p = W.with_per_tensor_scale(W.with_transposed_weights(W.random_problem(**CASES["long_k_no_factors"])), 0.75)
+    _check_full(p, hints=(None, 8, (0, 256)))
+
 def test_zero_rows_gives_seed():
     p = W.random_problem(9, 0, 64, 64, 2, output_bs=20, bsdp=6, shared_offset=3)
     ref, _ = oracle.run(p)

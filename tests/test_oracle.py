@@ -271,6 +271,37 @@ def test_missing_factors_equal_unit_factors():
     assert np.array_equal(oracle.run(q)[0], oracle.run(r)[0])
 
 
+
+def test_per_tensor_scale_is_every_rows_scale():
+    """A pertokenScale of shape (1) ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2",
+    function description: static pertensor-perchannel) scales every row: the
+    same as a per-token array holding that value in every entry; with no seed,
+    a power of two 2**s gives 2**s times the unscaled output exactly; the
+    brute force agrees on a tiny case."""
+    p = _base()
+    v = float(p.pertoken_scale[3])
+    q = W.with_per_tensor_scale(p, v)
+    assert q.pertoken_scale.shape == (1,)
+    r = copy.deepcopy(p)
+    r.pertoken_scale = np.full(p.m, v, dtype=np.float32)
+    assert np.array_equal(oracle.run(q)[0], oracle.run(r)[0])
+    base = _base(bsdp=0)
+    base.shared_input = None
+    none = copy.deepcopy(base)
+    none.pertoken_scale = None
+    for s in (-3, 5):
+        two = W.with_per_tensor_scale(base, 2.0 ** s)
+        assert np.array_equal(oracle.run(two)[0], oracle.run(none)[0] * np.float32(2.0 ** s))
+    small = W.with_per_tensor_scale(W.random_problem(21, 11, 32, 8, 2, bsdp=2, output_bs=7), 0.37)
+    bo, ba = brute.brute(small)
+    so, sa = oracle.run(small)
+    assert (sa.astype(np.int64) == ba).all() and np.array_equal(so, bo)
+    bad = copy.deepcopy(p)
+    bad.pertoken_scale = np.ones(2, dtype=np.float32)
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.run(bad)
+    assert e.value.status == "SHAPE"
+
 def test_absent_row_index_is_identity():
     p = _base(with_row_index=False, output_bs=96, bsdp=0)
     q = copy.deepcopy(p)

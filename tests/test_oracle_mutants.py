@@ -16,7 +16,9 @@ SRC = open(oracle_build.SRC).read()
 # (name, original text, mistaken text)
 MUTANTS = [
     ("drop_logit", "y = y * (p->logit ? p->logit[i] : 1.0f);", ""),
-    ("drop_pertoken", "y = y * (p->pertoken_scale ? p->pertoken_scale[i] : 1.0f);", ""),
+    ("drop_pertoken", "y = y * (p->pertoken_scale ? p->pertoken_scale[p->pertoken_per_tensor ? 0 : i] : 1.0f);", ""),
+    ("per_tensor_scale_ignored", "p->pertoken_scale[p->pertoken_per_tensor ? 0 : i]",
+     "(p->pertoken_per_tensor ? 1.0f : p->pertoken_scale[i])"),
     ("scale_ignores_expert", "return ((const float*)p->scale)[g * p->n + j];",
      "return ((const float*)p->scale)[j];"),
     ("nibble_high_first", "(word >> (4 * (j % 8)))", "(word >> (4 * (7 - j % 8)))"),
@@ -47,6 +49,7 @@ PINS = [
     T.test_zero_activations_give_the_seed,
     T.test_int4_equals_int8_with_small_values,
     T.test_rounding_error_within_bound,
+    T.test_per_tensor_scale_is_every_rows_scale,
     lambda: [T.test_brute_force_matches_oracle(c) for c in T._tiny_cases()[:40]],
 ]
 

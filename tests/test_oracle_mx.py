@@ -254,3 +254,22 @@ def test_fp8_bound_covers_fp32_evaluation():
         got[ri[i]] = (got[ri[i]] + y[i]).astype(np.float32)
     assert (np.abs(got.astype(np.float64) - out) <= bound).all()
     assert bound.max() <= 0.05 * np.abs(out).max()
+
+
+def test_fp8_per_tensor_scale_is_every_rows_scale():
+    """A pertokenScale of shape (1) (static pertensor-perchannel) is the same as
+    a per-token array holding that value in every entry, and a power of two
+    2**s scales every row's output by 2**s exactly (no seed)."""
+    p = W.fp8_problem(26, 40, 64, 16, 2, output_bs=25, bsdp=0)
+    v = float(p.pertoken_scale[5])
+    q = W.with_per_tensor_scale(p, v)
+    r = copy.deepcopy(p)
+    r.pertoken_scale = np.full(p.m, v, dtype=np.float32)
+    oq, bq, _ = MX.run(q)
+    orr, br, _ = MX.run(r)
+    assert np.array_equal(oq, orr) and np.array_equal(bq, br)
+    none = copy.deepcopy(p)
+    none.pertoken_scale = None
+    on, _, _ = MX.run(none)
+    o8, _, _ = MX.run(W.with_per_tensor_scale(p, 8.0))
+    assert np.array_equal(o8, on * 8.0)
