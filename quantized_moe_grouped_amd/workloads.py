@@ -423,3 +423,70 @@ def make_fp8_config(name: str = "fp8", seed: int = 0) -> Problem:
     shared = f32_to_bf16_bits(rng.standard_normal((8192, n)).astype(np.float32))
     return Problem(name, m, k, n, e, x1, x2, False, scale, True, pts, logit,
                    _group_list(counts, 0), 0, ri, shared, 4096, obs, seed, counts, True, fp8=True)
+
+
+# ---------------------------------------------------------------- activation quant + routing permute inputs
+
+
+@dataclasses.dataclass
+class RouteProblem:
+    """Inputs of the step that produces the grouped matmul's inputs: bf16
+    hidden states of T tokens and the router's top-K choice per token.
+
+    hidden        uint16 (bf16 bits) (T,k)
+    expert_ids    int32 or int64 (T,K): global expert of each (token, slot);
+                  local experts are [expert_offset, expert_offset + e)
+    topk_weights  float32 (T,K) routing weights, or None
+    """
+
+    name: str
+    T: int
+    k: int
+    K: int
+    e: int
+    hidden: np.ndarray
+    expert_ids: np.ndarray
+    topk_weights: Optional[np.ndarray]
+    expert_offset: int = 0
+    group_list_type: int = 1
+    seed: int = 0
+
+    @property
+    def m(self) -> int:
+        return self.T * self.K
+
+
+def route_problem(seed: int, T: int, k: int, K: int, e: int, *, n_gate: Optional[int] = None,
+                  expert_offset: int = 0, ids_dtype=np.int64, with_weights: bool = True,
+                  group_list_type: int = 1, zero_tokens: int = 0, repeat_slots: bool = False) -> RouteProblem:
+    """Seeded router outputs and hidden states.  Draw order: gate scores ->
+    hidden.  Gate scores N(0,1) over n_gate experts (default e + expert_offset,
+    so every id below expert_offset belongs to another rank); each token takes
+    its K largest, with softmax weights (float64, stored fp32).  Hidden values
+    are N(0,1) times a per-token magnitude 2^U(-4,4), rounded to bf16; the
+    first ``zero_tokens`` tokens are all zero.  ``repeat_slots`` gives every
+    token's last slot the expert of its first (a repeated expert)."""
+    rng = np.random.default_rng(seed)
+    n_gate = e + expert_offset if n_gate is None else n_gate
+    if K > n_gate:
+        raise ValueError("K exceeds the number of gate experts")
+    scores = rng.standard_normal((T, n_gate))
+    ids = np.argsort(-scores, axis=1, kind="stable")[:, :K]
+    top = np.take_along_axis(scores, ids, axis=1)
+    w = np.exp(top - top[:, :1]) if K > 0 else top
+    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32) if K > 0 else w.astype(np.float32)
+    if repeat_slots and K > 1:
+        ids[:, K - 1] = ids[:, 0]
+    mag = np.exp2(rng.uniform(-4.0, 4.0, size=(T, 1)))
+    hidden = (rng.standard_normal((T, k)) * mag).astype(np.float32)
+    hidden[:zero_tokens] = 0.0
+    return RouteProblem(f"route{seed}", T, k, K, e, f32_to_bf16_bits(hidden), ids.astype(ids_dtype),
+                        w if with_weights else None, expert_offset, group_list_type, seed)
+
+
+def make_route_config(name: str = "dispatch", seed: int = 0) -> RouteProblem:
+    """The prefill workload's producer step: 16384 tokens of hidden size 2048,
+    top-8 of 32 experts (131072 rows), int64 ids, counts as groupList."""
+    if name != "dispatch":
+        raise ValueError(name)
+    return route_problem(seed, 16384, 2048, 8, 32, ids_dtype=np.int64, group_list_type=1)
