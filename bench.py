@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="prefill", choices=["tiny", "decode", "skewed", "prefill", "int4", "mxa8w4", "fp8"])
+    ap.add_argument("--config", default="prefill",
+                    choices=["tiny", "decode", "skewed", "prefill", "int4", "mxa8w4", "fp8", "dispatch"])
     ap.add_argument("--combine", default="auto", choices=["auto", "atomic", "ordered"])
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
@@ -146,6 +147,96 @@ def traffic_from_profiles(kernel_name: str, workload: str):
         return None
 
 
+def dispatch_bytes(rp):
+    """Algorithmic bytes of the producer step, each array moved once: (step,
+    quantisation kernel).  The kernel reads the hidden rows and the entry -> row
+    map and writes x1 and pertokenScale; the step adds the router outputs read
+    and rowIndex, logit and groupList written."""
+    m = rp.T * rp.K
+    kern = rp.T * rp.k * 2 + m * 4 + m * rp.k + m * 4
+    step = (rp.T * rp.k * 2 + m * rp.expert_ids.itemsize + (0 if rp.topk_weights is None else m * 4)
+            + m * rp.k + m * 4 + (0 if rp.topk_weights is None else m * 4) + m * 8 + rp.e * 8)
+    return step, kern
+
+
+def bench_dispatch(args):
+    """The producer step (per-token int8 quantisation of bf16 hidden states and
+    the routing permute) at the prefill workload's shape; HBM-bound, reported
+    in GB/s of algorithmic bytes."""
+    import numpy as np
+    import torch
+    from quantized_moe_grouped_amd import binding as B
+    from quantized_moe_grouped_amd import workloads as W
+
+    rp = W.make_route_config("dispatch", args.seed)
+    dev = "cuda"
+    hidden = torch.from_numpy(rp.hidden.view(np.int16)).to(dev).view(torch.bfloat16)
+    ids = torch.from_numpy(rp.expert_ids).to(dev)
+    w = torch.from_numpy(rp.topk_weights).to(dev)
+    m = rp.T * rp.K
+    x1 = torch.empty((m, rp.k), dtype=torch.int8, device=dev)
+    pts = torch.empty(m, dtype=torch.float32, device=dev)
+    logit = torch.empty(m, dtype=torch.float32, device=dev)
+    ri = torch.empty(m, dtype=torch.int64, device=dev)
+    gl = torch.empty(rp.e, dtype=torch.int64, device=dev)
+    cargs, keep = B.make_qp_args(hidden, ids, x1, pts, ri, gl, topk_weights=w, logit=logit,
+                                 group_list_type=rp.group_list_type)
+    ws = torch.empty(max(B.qp_workspace_size(cargs), 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = Hip()
+    ev_all = (hip.event(), hip.event())
+    ev_q = [(hip.event(), hip.event()) for _ in range(args.steps)]
+
+    def call(evs=(None, None)):
+        st = B.lib().gmm_quant_permute_profiled(ctypes.byref(cargs), ctypes.c_void_p(ws.data_ptr()),
+                                                ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream), evs[0], evs[1])
+        if st != 0:
+            raise B.GmmfrError(st, "gmm_quant_permute_profiled")
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    hip.record(ev_all[0], stream)
+    for s in range(args.steps):
+        call(ev_q[s])
+    hip.record(ev_all[1], stream)
+    torch.cuda.synchronize()
+    ms_step = hip.elapsed_ms(*ev_all) / args.steps
+    q_ms = [hip.elapsed_ms(a, b) for a, b in ev_q]
+    q_avg = sum(q_ms) / len(q_ms)
+    step_bytes, kern_bytes = dispatch_bytes(rp)
+    print(f"[bench] step {ms_step:.4f} ms, quant kernel {q_avg:.4f} ms", file=sys.stderr, flush=True)
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    kgbs = kern_bytes / (q_avg * 1e-3) / 1e9
+    res = {
+        "metric": "GB/s (and % of HBM roofline) of per-token int8 quantisation + routing permute at 1 GPU",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16->int8",
+        "data": "synthetic (seeded generator; bf16 hidden states, top-8 of 32 router choices with softmax weights)",
+        "config": {"workload": "dispatch", "tokens": rp.T, "k": rp.k, "top_k": rp.K, "e": rp.e, "m": m,
+                   "ids": str(rp.expert_ids.dtype), "group_list_type": rp.group_list_type, "seed": args.seed,
+                   "algorithmic_bytes_per_step": step_bytes,
+                   "path_roofline_frac": round(gbs / PEAK_HBM_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "quant_rows_kernel", "achieved": round(kgbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
+                     "launch_ms": round(q_avg, 5), "bytes_per_launch": kern_bytes, "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import quant as Q
+        reps, t0 = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t0 < 10.0:
+            Q.run(rp)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        res["cpu_baseline"] = {"value": round(step_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"the whole workload ({rp.T} tokens), {reps} runs, {dt:.2f} s each"}
+    print(json.dumps(res), flush=True)
+    del keep
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -172,6 +263,9 @@ def main():
         dt = (time.perf_counter() - t0) / 5
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30,
                           "copy_GBps_read_plus_write": round(2 * (1 << 30) / dt / 1e9, 1)}), flush=True)
+        return
+    if args.config == "dispatch":
+        bench_dispatch(args)
         return
     print(f"[bench] generating {args.config} seed {args.seed}", file=sys.stderr, flush=True)
     if args.config == "mxa8w4":

@@ -214,6 +214,63 @@ typedef struct {
 
 int gmm_finalize_routing_plan(const gmmfr_args* args, gmmfr_plan_info* info);
 
+/*
+ * Producer step: dynamic per-token int8 quantisation of bf16 hidden states and
+ * the routing permute, which together make this library's x1, pertokenScale,
+ * logit, rowIndex and groupList from a router's top-K choice.  The pages name
+ * the step ("aclnnAlltoAllvQuantGroupedMatMul", function and formula: a
+ * permute after the dispatch, before the expert matmul; quantisation modes:
+ * per-token dynamic quantisation) and show the per-token cast multiplying by
+ * an inverse scale (PTOAS issue #1568, background); the formulas are lost, so
+ * the plain symmetric reading is taken:
+ *
+ *   per token t (x = its k bf16 values widened to fp32):
+ *     amax = max_j |x[j]|,  scale_t = fl(amax / 127),  inv = fl(127 / amax)
+ *     (inv = 0 when amax = 0),  q[j] = clamp(rne(fl(x[j] * inv)), -127, 127)
+ *   entry f = t*K + j goes to local expert g = expert_ids[t][j] - expert_offset;
+ *   entries with g outside [0, e) produce no row (they belong to other ranks);
+ *   rows are the local entries sorted by g, ties in ascending f; the row of
+ *   entry f gets x1 = q of token t, pertokenScale = scale_t,
+ *   logit = topk_weights[t][j], rowIndex = t;
+ *   groupList[g] = rows of expert g (type 1) or their cumulative end (type 0).
+ *
+ * Rows at and past sum(groupList counts) are not written (the grouped matmul
+ * never reads them).  Hidden values must be finite; expert ids are device data
+ * and are not validated beyond routing the out-of-range ones nowhere.
+ */
+typedef struct {
+  gmmfr_tensor hidden;         /* BFLOAT16 (T,k)                                required */
+  gmmfr_tensor expert_ids;     /* INT32 or INT64 (T,K): global expert per slot  required */
+  gmmfr_tensor topk_weights;   /* FLOAT32 (T,K) routing weights; given iff logit is given */
+  gmmfr_tensor x1;             /* out INT8 (T*K,k)                              required */
+  gmmfr_tensor pertoken_scale; /* out FLOAT32 (T*K)                             required */
+  gmmfr_tensor logit;          /* out FLOAT32 (T*K); given iff topk_weights is given      */
+  gmmfr_tensor row_index;      /* out INT64 or INT32 (T*K)                      required */
+  gmmfr_tensor group_list;     /* out INT64 (e)                                 required */
+  int64_t expert_offset;       /* local experts are [expert_offset, expert_offset + e)    */
+  int64_t group_list_type;     /* 0 cumulative ends, 1 counts                             */
+} gmmqp_args;
+
+/* Limits: 0 <= T, 1 <= K <= 64, T*K < 2^31, 16 <= k <= 65536 with k % 16 == 0,
+ * 1 <= e <= 1024, every base pointer 16-byte aligned.
+ * Stage 1: validate (host only) and report the workspace size: one int32 per
+ * (expert, chunk of 256 entries), one per expert and T*K more, in 256-byte
+ * aligned sections. */
+int gmm_quant_permute_workspace(const gmmqp_args* args, size_t* workspace_bytes);
+
+/* Stage 2: validate again and enqueue on `stream` (hipStream_t; NULL = null
+ * stream).  Every output is caller-owned device memory; the workspace needs no
+ * initialisation.  Returns GMMFR_OK, a validation status, GMMFR_ERR_WORKSPACE
+ * or GMMFR_ERR_HIP. */
+int gmm_quant_permute(const gmmqp_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Diagnostic variant of gmm_quant_permute for measurement: identical work,
+ * plus hipEventRecord(quant_start) right before and hipEventRecord(quant_stop)
+ * right after the quantisation kernel, on `stream` (caller-created hipEvent_t,
+ * either may be NULL; none recorded on error or when T == 0). */
+int gmm_quant_permute_profiled(const gmmqp_args* args, void* workspace, size_t workspace_bytes, void* stream,
+                               void* quant_start, void* quant_stop);
+
 /* Short static text for a status code. */
 const char* gmmfr_status_string(int status);
 

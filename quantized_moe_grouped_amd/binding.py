@@ -23,7 +23,8 @@ DT_FLOAT8_E4M3FN, DT_FLOAT4_E2M1X2, DT_FLOAT8_E8M0 = 7, 8, 9
 COMBINE = {"auto": 0, "atomic": 1, "ordered": 2}
 
 EXPORTED = ("gmm_finalize_routing_workspace", "gmm_finalize_routing", "gmm_finalize_routing_profiled",
-            "gmm_finalize_routing_plan", "gmmfr_status_string")
+            "gmm_finalize_routing_plan", "gmmfr_status_string", "gmm_quant_permute_workspace",
+            "gmm_quant_permute", "gmm_quant_permute_profiled")
 
 
 class GmmfrError(RuntimeError):
@@ -48,6 +49,14 @@ class Args(ctypes.Structure):
         ("transpose_x1", ctypes.c_int32), ("transpose_x2", ctypes.c_int32),
         ("deterministic", ctypes.c_int32), ("combine", ctypes.c_int32),
         ("tuning_config", ctypes.POINTER(ctypes.c_int64)), ("tuning_config_len", ctypes.c_int64),
+    ]
+
+
+class QpArgs(ctypes.Structure):
+    _fields_ = [
+        ("hidden", Tensor), ("expert_ids", Tensor), ("topk_weights", Tensor), ("x1", Tensor),
+        ("pertoken_scale", Tensor), ("logit", Tensor), ("row_index", Tensor), ("group_list", Tensor),
+        ("expert_offset", ctypes.c_int64), ("group_list_type", ctypes.c_int64),
     ]
 
 
@@ -76,6 +85,13 @@ def lib():
         L.gmm_finalize_routing_profiled.restype = ctypes.c_int
         L.gmm_finalize_routing_plan.argtypes = [ctypes.POINTER(Args), ctypes.POINTER(PlanInfo)]
         L.gmm_finalize_routing_plan.restype = ctypes.c_int
+        L.gmm_quant_permute_workspace.argtypes = [ctypes.POINTER(QpArgs), ctypes.POINTER(ctypes.c_size_t)]
+        L.gmm_quant_permute_workspace.restype = ctypes.c_int
+        L.gmm_quant_permute.argtypes = [ctypes.POINTER(QpArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.gmm_quant_permute.restype = ctypes.c_int
+        L.gmm_quant_permute_profiled.argtypes = [ctypes.POINTER(QpArgs), ctypes.c_void_p, ctypes.c_size_t,
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.gmm_quant_permute_profiled.restype = ctypes.c_int
         L.gmmfr_status_string.argtypes = [ctypes.c_int]
         L.gmmfr_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -204,3 +220,69 @@ def gmm_finalize_routing(x1, x2, group_list, out, *, workspace=None, stream=None
         workspace = torch.empty(need, dtype=torch.uint8, device=out.device)
     run(args, workspace, stream)
     del keep
+
+
+# ---------------------------------------------------------------- producer step
+
+
+def make_qp_args(hidden, expert_ids, x1, pertoken_scale, row_index, group_list, *, topk_weights=None,
+                 logit=None, expert_offset: int = 0, group_list_type: int = 1):
+    """C arguments of gmm_quant_permute.  hidden is bf16 (T,k) and expert_ids
+    int32/int64 (T,K); the outputs are x1 int8 (T*K,k), pertoken_scale fp32
+    (T*K), row_index int32/int64 (T*K), group_list int64 (e), and logit fp32
+    (T*K) when topk_weights (T,K) is given.  Returns (args, keepalive)."""
+    a = QpArgs()
+    a.hidden = _desc(hidden)
+    a.expert_ids = _desc(expert_ids)
+    a.topk_weights = _desc(topk_weights)
+    a.x1 = _desc(x1)
+    a.pertoken_scale = _desc(pertoken_scale)
+    a.logit = _desc(logit)
+    a.row_index = _desc(row_index)
+    a.group_list = _desc(group_list)
+    a.expert_offset = int(expert_offset)
+    a.group_list_type = int(group_list_type)
+    return a, (hidden, expert_ids, topk_weights, x1, pertoken_scale, logit, row_index, group_list)
+
+
+def qp_workspace_size(args: QpArgs) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().gmm_quant_permute_workspace(ctypes.byref(args), ctypes.byref(n))
+    if st != OK:
+        raise GmmfrError(st, "gmm_quant_permute_workspace")
+    return int(n.value)
+
+
+def quant_permute(hidden, expert_ids, num_experts: int, *, topk_weights=None, expert_offset: int = 0,
+                  group_list_type: int = 1, row_index_dtype=None, workspace=None, stream=None) -> dict:
+    """Allocate the outputs with torch and enqueue gmm_quant_permute on `stream`
+    (default: the current stream).  Returns the output tensors by name."""
+    import torch
+    dev = hidden.device
+    T, k = hidden.shape
+    K = expert_ids.shape[1]
+    m = T * K
+    out = dict(x1=torch.empty((m, k), dtype=torch.int8, device=dev),
+               pertoken_scale=torch.empty(m, dtype=torch.float32, device=dev),
+               row_index=torch.empty(m, dtype=row_index_dtype or torch.int64, device=dev),
+               group_list=torch.empty(num_experts, dtype=torch.int64, device=dev),
+               logit=None if topk_weights is None else torch.empty(m, dtype=torch.float32, device=dev))
+    args, keep = make_qp_args(hidden, expert_ids, out["x1"], out["pertoken_scale"], out["row_index"],
+                              out["group_list"], topk_weights=topk_weights, logit=out["logit"],
+                              expert_offset=expert_offset, group_list_type=group_list_type)
+    need = qp_workspace_size(args)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    ws_ptr = 0 if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().gmm_quant_permute(ctypes.byref(args), ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes),
+                                 ctypes.c_void_p(stream))
+    if st != OK:
+        raise GmmfrError(st, "gmm_quant_permute")
+    del keep
+    out["workspace"] = workspace
+    return out

@@ -11,7 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgmmfr.so")
-SOURCES = [os.path.join(CSRC, "gmmfr_kernels.hip"), os.path.join(CSRC, "gmmfr_api.cpp")]
+SOURCES = [os.path.join(CSRC, "gmmfr_kernels.hip"), os.path.join(CSRC, "gmmfr_api.cpp"),
+           os.path.join(CSRC, "quant_permute.hip")]
 ARCH = os.environ.get("GMMFR_ARCH", "gfx950")
 
 FLAGS = [
@@ -33,7 +34,10 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-x", "hip", SOURCES[0], "-x", "hip", SOURCES[1], "-o", tmp]
+    cmd = [hipcc(), *FLAGS]
+    for src in SOURCES:
+        cmd += ["-x", "hip", src]
+    cmd += ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -318,3 +318,67 @@ MX_CASES = [
 def test_mx_and_fp8_stage_one(name, make, over, code):
     st, _ = _ws(make(**over))
     assert st == code, (B.STATUS_NAMES.get(st), B.STATUS_NAMES.get(code))
+
+
+# ---------------------------------------------------------------- producer step (quantise + permute)
+
+def _qp_args(T=512, k=2048, K=8, e=32, **over):
+    a = B.QpArgs()
+    a.hidden = _fake(B.DT_BFLOAT16, T, k)
+    a.expert_ids = _fake(B.DT_INT64, T, K)
+    a.topk_weights = _fake(B.DT_FLOAT32, T, K)
+    a.x1 = _fake(B.DT_INT8, T * K, k)
+    a.pertoken_scale = _fake(B.DT_FLOAT32, T * K)
+    a.logit = _fake(B.DT_FLOAT32, T * K)
+    a.row_index = _fake(B.DT_INT64, T * K)
+    a.group_list = _fake(B.DT_INT64, e)
+    a.group_list_type = 1
+    for key, v in over.items():
+        setattr(a, key, v)
+    return a
+
+
+def _qp_ws(a):
+    n = ctypes.c_size_t(12345)
+    st = B.lib().gmm_quant_permute_workspace(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+def test_quant_permute_workspace_formula():
+    """Three int32 sections: one per (expert, chunk of 256 entries), one per
+    expert, one per entry."""
+    st, ws = _qp_ws(_qp_args(T=512, K=8, e=32))
+    nchunks = (512 * 8 + 255) // 256
+    r = lambda v: (v + 255) // 256 * 256
+    assert st == B.OK and ws == r(32 * nchunks * 4) + r(32 * 4) + r(512 * 8 * 4)
+    assert _qp_ws(_qp_args(T=0, K=8, e=4, x1=_fake(B.DT_INT8, 0, 2048))) == (B.OK, 256)
+
+
+QP_CASES = [
+    ("ok_int32_ids_rows", dict(expert_ids=_fake(B.DT_INT32, 512, 8), row_index=_fake(B.DT_INT32, 4096)), B.OK),
+    ("ok_no_weights", dict(topk_weights=B.Tensor(), logit=B.Tensor()), B.OK),
+    ("weights_without_logit", dict(logit=B.Tensor()), B.ERR_NULLPTR),
+    ("logit_without_weights", dict(topk_weights=B.Tensor()), B.ERR_NULLPTR),
+    ("no_hidden", dict(hidden=B.Tensor()), B.ERR_NULLPTR),
+    ("hidden_f32", dict(hidden=_fake(B.DT_FLOAT32, 512, 2048)), B.ERR_DTYPE),
+    ("ids_f32", dict(expert_ids=_fake(B.DT_FLOAT32, 512, 8)), B.ERR_DTYPE),
+    ("x1_fp8", dict(x1=_fake(B.DT_FLOAT8_E4M3FN, 4096, 2048)), B.ERR_DTYPE),
+    ("group_list_i32", dict(group_list=_fake(B.DT_INT32, 32)), B.ERR_DTYPE),
+    ("group_list_type", dict(group_list_type=2), B.ERR_ATTR),
+    ("k_not_mult_16", dict(hidden=_fake(B.DT_BFLOAT16, 512, 2040), x1=_fake(B.DT_INT8, 4096, 2040)), B.ERR_SHAPE),
+    ("top_k_65", dict(expert_ids=_fake(B.DT_INT64, 512, 65), topk_weights=_fake(B.DT_FLOAT32, 512, 65)),
+     B.ERR_SHAPE),
+    ("ids_rows", dict(expert_ids=_fake(B.DT_INT64, 511, 8)), B.ERR_SHAPE),
+    ("x1_rows", dict(x1=_fake(B.DT_INT8, 4095, 2048)), B.ERR_SHAPE),
+    ("pts_len", dict(pertoken_scale=_fake(B.DT_FLOAT32, 512)), B.ERR_SHAPE),
+    ("too_many_experts", dict(group_list=_fake(B.DT_INT64, 1025)), B.ERR_SHAPE),
+    ("misaligned_x1", dict(x1=_fake(B.DT_INT8, 4096, 2048, ptr=0x7000008)), B.ERR_ALIGN),
+]
+
+
+@pytest.mark.parametrize("name,over,code", QP_CASES, ids=[c[0] for c in QP_CASES])
+def test_quant_permute_stage_one(name, over, code):
+    st, ws = _qp_ws(_qp_args(**over))
+    assert st == code, (B.STATUS_NAMES.get(st), B.STATUS_NAMES.get(code))
+    if code != B.OK:
+        assert ws == 12345
