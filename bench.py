@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, GB/s
 KERNEL_SRC = os.path.join(ROOT, "quantized_moe_grouped_amd", "csrc", "gmmfr_kernels.hip")
+QP_SRC = os.path.join(ROOT, "quantized_moe_grouped_amd", "csrc", "quant_permute.hip")
 
 
 def parse():
@@ -131,15 +132,15 @@ def cpu_baseline(p, rows_wanted: int):
             "seconds": dt}
 
 
-def traffic_from_profiles(kernel_name: str, workload: str):
+def traffic_from_profiles(kernel_name: str, workload: str, prefix: str = "gmm_kernel", src: str = KERNEL_SRC):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"gmm_kernel_{workload}_hbm_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{prefix}_{workload}_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
-        src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        src_hash = hashlib.sha256(open(src, "rb").read()).hexdigest()
         if rec.get("kernel_source_sha256") != src_hash or rec.get("kernel") != kernel_name:
             return None
         return rec.get("bytes_per_launch")
@@ -220,7 +221,8 @@ def bench_dispatch(args):
                    "path_roofline_frac": round(gbs / PEAK_HBM_GBS, 4)},
         "roofline": {"bound": "hbm", "kernel": "quant_rows_kernel", "achieved": round(kgbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
-                     "launch_ms": round(q_avg, 5), "bytes_per_launch": kern_bytes, "traffic": None},
+                     "launch_ms": round(q_avg, 5), "bytes_per_launch": kern_bytes,
+                     "traffic": traffic_from_profiles("quant_rows_kernel", "dispatch", "quant_rows_kernel", QP_SRC)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
