@@ -1177,6 +1177,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   __shared__ __attribute__((aligned(16))) int8_t sB[STAGES * B_BYTES];
   __shared__ __attribute__((aligned(16))) uint32_t sSA[SC_STAGES][BM];  // the scale dword of each row
   __shared__ __attribute__((aligned(16))) uint32_t sSB[SC_STAGES][BN];  // and of each column
+  __shared__ float s_lg[BM], s_pt[BM];  // the tile's per-row logit and pertokenScale, for the epilogue
   extern __shared__ __attribute__((aligned(16))) int32_t s_dyn[];
   int32_t* s_ends = s_dyn;
   int32_t* s_tile_pre = s_dyn + p.e;
@@ -1203,6 +1204,11 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   const uint32_t* sb_base = sb_words;
   uint32_t a_off[A_INSTR], b_off[B_INSTR], sa_off = 0, sb_off = 0;
   auto set_sources = [&](const TileCoord& c) {
+    // The lane and wave indices pass through an opaque point: the per-lane
+    // offsets are computed here for each tile, not hoisted out of the tile
+    // loop (where they would stay live, or spill, across the k-loop).
+    int lane = tid & 63, wave = tid >> 6, tid = threadIdx.x;
+    asm volatile("" : "+v"(lane), "+v"(wave), "+v"(tid));
     a_base = (const int8_t*)uniform64((int64_t)(p.x1 + c.row0 * k));
 #pragma unroll
     for (int q = 0; q < A_INSTR; ++q) {
@@ -1256,17 +1262,28 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   const int G = gridDim.x;
   const bool blocked = G % kTileQueues == 0;
   const int vq = blockIdx.x % kTileQueues, lw = blockIdx.x / kTileQueues, per_q = G / kTileQueues;
+  auto tile_at = [&](int jj) -> int {
+    if (blocked) return queue_tile(vq, jj * per_q + lw, total_tiles);
+    const int64_t tt = (int64_t)jj * G + blockIdx.x;
+    return tt < total_tiles ? (int)tt : -1;
+  };
   for (int j = 0;; ++j) {
-    int t;
-    if (blocked) {
-      t = queue_tile(vq, j * per_q + lw, total_tiles);
-    } else {
-      const int64_t tt = (int64_t)j * G + blockIdx.x;
-      t = tt < total_tiles ? (int)tt : -1;
-    }
+    const int t = tile_at(j);
     if (t < 0) break;
     const TileCoord c = coord(t);
-    __syncthreads();  // every wave is done with the previous tile's stages
+    __syncthreads();  // every wave is done with the previous tile's stages and row factors
+    // The k-steps run at a raised wave priority and the epilogue at the base
+    // one (where the two workgroups of a CU share a SIMD, the one in its
+    // k-loop issues first), except in a workgroup's last two tiles.
+    if (tile_at(j + 2) >= 0) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+    // row factors of the tile, loaded now and put in LDS at the epilogue
+    float fr_lg = 1.0f, fr_pt = 1.0f;
+    if (tid < BM) {
+      const int64_t row = min(c.row0 + tid, p.m - 1);
+      if (p.logit) fr_lg = p.logit[row];
+      if (B8 && p.pertoken) fr_pt = p.pertoken[p.pertoken_scalar ? 0 : row];
+    }
     set_sources(c);
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
@@ -1323,7 +1340,29 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
           acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[jj], acc[i][jj], 0, B8 ? 0 : 4, 0,
                                                                         sa[i], 0, sb[jj]);
     }
-    // epilogue: y = acc * logit, guarded by the tile's valid rows and n
+    __builtin_amdgcn_s_setprio(0);
+    if (tid < BM) {
+      s_lg[tid] = fr_lg;
+      s_pt[tid] = fr_pt;
+    }
+    __syncthreads();
+    // lane-dependent epilogue addresses are computed here (opaque indices,
+    // as in set_sources)
+    int lane = tid & 63, h = lane >> 5, wm = wave / WAVES_N, wn = wave % WAVES_N;
+    asm volatile("" : "+v"(lane), "+v"(h), "+s"(wm), "+s"(wn));
+    // epilogue: y = acc * logit (FP8: ((acc * scale) * pertokenScale) * logit),
+    // guarded by the tile's valid rows and n; the lane's four column scales
+    // are read once per tile
+    float col_scale[FN];
+#pragma unroll
+    for (int jj = 0; jj < FN; ++jj) {
+      const int64_t col = min(c.col0 + wn * WTN + jj * 32 + (lane & 31), n - 1);
+      col_scale[jj] = 1.0f;
+      if (B8 && p.scale)
+        col_scale[jj] = p.scale_bf16
+                            ? __uint_as_float((uint32_t)((const uint16_t*)p.scale)[(int64_t)c.g * n + col] << 16)
+                            : ((const float*)p.scale)[(int64_t)c.g * n + col];
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -1331,8 +1370,8 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
         const int lr = wm * WTM + i * 32 + (r / 4) * 8 + h * 4 + (r % 4);
         if (lr >= c.valid_rows) continue;
         const int64_t row = c.row0 + lr;
-        const float lg = p.logit ? p.logit[row] : 1.0f;
-        const float pt = (B8 && p.pertoken) ? p.pertoken[p.pertoken_scalar ? 0 : row] : 1.0f;
+        const float lg = s_lg[lr];
+        const float pt = s_pt[lr];
         int64_t d = row;
         if constexpr (COMBINE == kCombineAtomic) {
           d = dest_row(p, row);
@@ -1344,12 +1383,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
           if (col >= n) continue;
           float v = acc[i][jj][r];
           if constexpr (B8) {  // ((acc * scale) * pertokenScale) * logit, each rounded
-            float sc = 1.0f;
-            if (p.scale) {
-              sc = p.scale_bf16 ? __uint_as_float((uint32_t)((const uint16_t*)p.scale)[(int64_t)c.g * n + col] << 16)
-                                : ((const float*)p.scale)[(int64_t)c.g * n + col];
-            }
-            v = v * sc;
+            v = v * col_scale[jj];
             v = v * pt;
           }
           v = v * lg;
