@@ -1177,13 +1177,31 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   __shared__ __attribute__((aligned(16))) int8_t sB[STAGES * B_BYTES];
   __shared__ __attribute__((aligned(16))) uint32_t sSA[SC_STAGES][BM];  // the scale dword of each row
   __shared__ __attribute__((aligned(16))) uint32_t sSB[SC_STAGES][BN];  // and of each column
-  __shared__ float s_lg[BM], s_pt[BM];  // the tile's per-row logit and pertokenScale, for the epilogue
+  // per-row logit and (FP8) pertokenScale of a tile for its epilogue, as raw
+  // words copied by the DMA path, double-buffered across consecutive tiles
+  __shared__ __attribute__((aligned(16))) float s_lg[2][BM];
+  __shared__ __attribute__((aligned(16))) float s_pt[2][BM];
+  // FP8: the tile's per-column scale words (fp32: one per column; bf16: one
+  // per column pair), double-buffered like the row factors
+  __shared__ __attribute__((aligned(16))) uint32_t s_cs[2][B8 ? BN : 1];
   extern __shared__ __attribute__((aligned(16))) int32_t s_dyn[];
   int32_t* s_ends = s_dyn;
   int32_t* s_tile_pre = s_dyn + p.e;
   int64_t* s_scan = (int64_t*)sA;
   static_assert(STAGES * A_BYTES >= kThreads * 8, "scan scratch fits in the A stages");
 
+  // an absent logit or pertokenScale reads as 1.0, a per-tensor
+  // pertokenScale as its one value (filled once; the table build's barriers
+  // publish the fill)
+  const bool lg_rows = p.logit != nullptr;
+  const bool pt_rows = B8 && p.pertoken != nullptr && !p.pertoken_scalar;
+  {
+    const float pt_fill = (B8 && p.pertoken && p.pertoken_scalar) ? p.pertoken[0] : 1.0f;
+    for (int q = threadIdx.x; q < 2 * BM; q += kThreads) {
+      if (!lg_rows) (&s_lg[0][0])[q] = 1.0f;
+      if (!pt_rows) (&s_pt[0][0])[q] = pt_fill;
+    }
+  }
   build_group_table(p, BM, s_ends, s_tile_pre, s_scan);
   const int total_tiles = s_tile_pre[p.e];
   const int tid = threadIdx.x;
@@ -1259,119 +1277,110 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
     return c;
   };
 
-  const int G = gridDim.x;
-  const bool blocked = G % kTileQueues == 0;
-  const int vq = blockIdx.x % kTileQueues, lw = blockIdx.x / kTileQueues, per_q = G / kTileQueues;
-  auto tile_at = [&](int jj) -> int {
-    if (blocked) return queue_tile(vq, jj * per_q + lw, total_tiles);
-    const int64_t tt = (int64_t)jj * G + blockIdx.x;
-    return tt < total_tiles ? (int)tt : -1;
-  };
-  for (int j = 0;; ++j) {
-    const int t = tile_at(j);
-    if (t < 0) break;
-    const TileCoord c = coord(t);
-    __syncthreads();  // every wave is done with the previous tile's stages and row factors
-    // The k-steps run at a raised wave priority and the epilogue at the base
-    // one (where the two workgroups of a CU share a SIMD, the one in its
-    // k-loop issues first), except in a workgroup's last two tiles.
-    if (tile_at(j + 2) >= 0) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
-    // row factors of the tile, loaded now and put in LDS at the epilogue
-    float fr_lg = 1.0f, fr_pt = 1.0f;
-    if (tid < BM) {
-      const int64_t row = min(c.row0 + tid, p.m - 1);
-      if (p.logit) fr_lg = p.logit[row];
-      if (B8 && p.pertoken) fr_pt = p.pertoken[p.pertoken_scalar ? 0 : row];
+  // row factors of tile c into buffer pb: one word per row from the waves
+  // covering rows 0..BM-1 (opaque indices, as in set_sources)
+  auto dma_rows = [&](const TileCoord& c, int pb) {
+    int tid = threadIdx.x, wave = tid >> 6;
+    asm volatile("" : "+v"(tid), "+v"(wave));
+    if constexpr (B8) {
+      if (p.scale) {  // column scales: every wave, one word per lane (the last ones clamped)
+        const int w = __builtin_amdgcn_readfirstlane(wave);
+        const int words = p.scale_bf16 ? BN / 2 : BN;
+        if (w * 64 < words) {
+          const int64_t last = p.scale_bf16 ? (n - c.col0) / 2 - 1 : n - c.col0 - 1;  // last word inside n
+          const uint32_t off = (uint32_t)(min((int64_t)tid, last) * 4);
+          const void* base = p.scale_bf16 ? (const void*)((const uint16_t*)p.scale + (int64_t)c.g * n + c.col0)
+                                          : (const void*)((const float*)p.scale + (int64_t)c.g * n + c.col0);
+          lds_dma4_sv((const void*)uniform64((int64_t)base), off,
+                      __builtin_amdgcn_readfirstlane(lds_addr(&s_cs[pb][w * 64])));
+        }
+      }
     }
-    set_sources(c);
+    if (wave * 64 < BM) {
+      const uint32_t off = (uint32_t)((min(c.row0 + tid, p.m - 1) - c.row0) * 4);
+      const int w = __builtin_amdgcn_readfirstlane(wave);
+      if (lg_rows)
+        lds_dma4_sv((const void*)uniform64((int64_t)(p.logit + c.row0)), off,
+                    __builtin_amdgcn_readfirstlane(lds_addr(&s_lg[pb][w * 64])));
+      if (pt_rows)
+        lds_dma4_sv((const void*)uniform64((int64_t)(p.pertoken + c.row0)), off,
+                    __builtin_amdgcn_readfirstlane(lds_addr(&s_pt[pb][w * 64])));
+    }
+  };
+
+  // one k-step on stage st (tile-local k-step kt): fragment reads, 8 MFMAs
+  auto compute = [&](int st, int kt, v16f (&acc)[FM][FN]) {
+    const int8_t* a_st = sA + st * A_BYTES;
+    const int8_t* b_st = sB + st * B_BYTES;
+    const int sel = 8 * (2 * (kt & 1) + h);  // byte of this lane's block in the scale dword
+    v8i af[FM];
+    int sa[FM], sb[FN];
 #pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st)
-      if (st < ktiles) issue_stage(st, st);
-    v16f acc[FM][FN];
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + i * 32 + (lane & 31);
+      const v4i lo = *(const LDS_PTR(v4i))(a_st + r * BK + ((h ^ swz_a<BK>(r)) << 4));
+      const v4i hi = *(const LDS_PTR(v4i))(a_st + r * BK + (((2 + h) ^ swz_a<BK>(r)) << 4));
+      af[i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      sa[i] = B8 ? 127 : (int)(sSA[B8 ? 0 : st][r] >> sel);
+    }
+    v8i bf[FN];
+#pragma unroll
+    for (int jj = 0; jj < FN; ++jj) {
+      const int cl = wn * WTN + jj * 32 + (lane & 31);
+      if constexpr (B8) {
+        const v4i lo = *(const LDS_PTR(v4i))(b_st + cl * BK + ((h ^ swz_a<BK>(cl)) << 4));
+        const v4i hi = *(const LDS_PTR(v4i))(b_st + cl * BK + (((2 + h) ^ swz_a<BK>(cl)) << 4));
+        bf[jj] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        sb[jj] = 127;
+      } else {
+        const v4i w = *(const LDS_PTR(v4i))(b_st + cl * B_COLB + h * 16);
+        bf[jj] = v8i{w.x, w.y, w.z, w.w, 0, 0, 0, 0};
+        sb[jj] = (int)(sSB[st][cl] >> sel);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int jj = 0; jj < FN; ++jj) acc[i][jj] = v16f{0};
-#pragma unroll 1
-    for (int kt = 0; kt < ktiles; ++kt) {
-      // stage kt complete; the stages issued after it may still be in flight
-      if (kt + STAGES - 2 < ktiles) {
-        if (lo_wave) wait_vmcnt<(STAGES - 2) * LOADS_LO>();
-        else wait_vmcnt<(STAGES - 2) * LOADS_HI>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      lds_barrier();
-      if (kt + STAGES - 1 < ktiles) issue_stage((kt + STAGES - 1) % STAGES, kt + STAGES - 1);
-      const int st = kt % STAGES;
-      const int8_t* a_st = sA + st * A_BYTES;
-      const int8_t* b_st = sB + st * B_BYTES;
-      const int sel = 8 * (2 * (kt & 1) + h);  // byte of this lane's block in the scale dword
-      v8i af[FM];
-      int sa[FM], sb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * WTM + i * 32 + (lane & 31);
-        const v4i lo = *(const LDS_PTR(v4i))(a_st + r * BK + ((h ^ swz_a<BK>(r)) << 4));
-        const v4i hi = *(const LDS_PTR(v4i))(a_st + r * BK + (((2 + h) ^ swz_a<BK>(r)) << 4));
-        af[i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        sa[i] = B8 ? 127 : (int)(sSA[B8 ? 0 : st][r] >> sel);
-      }
-      v8i bf[FN];
-#pragma unroll
-      for (int jj = 0; jj < FN; ++jj) {
-        const int cl = wn * WTN + jj * 32 + (lane & 31);
-        if constexpr (B8) {
-          const v4i lo = *(const LDS_PTR(v4i))(b_st + cl * BK + ((h ^ swz_a<BK>(cl)) << 4));
-          const v4i hi = *(const LDS_PTR(v4i))(b_st + cl * BK + (((2 + h) ^ swz_a<BK>(cl)) << 4));
-          bf[jj] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          sb[jj] = 127;
-        } else {
-          const v4i w = *(const LDS_PTR(v4i))(b_st + cl * B_COLB + h * 16);
-          bf[jj] = v8i{w.x, w.y, w.z, w.w, 0, 0, 0, 0};
-          sb[jj] = (int)(sSB[st][cl] >> sel);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int jj = 0; jj < FN; ++jj)
-          acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[jj], acc[i][jj], 0, B8 ? 0 : 4, 0,
-                                                                        sa[i], 0, sb[jj]);
-    }
-    __builtin_amdgcn_s_setprio(0);
-    if (tid < BM) {
-      s_lg[tid] = fr_lg;
-      s_pt[tid] = fr_pt;
-    }
-    __syncthreads();
-    // lane-dependent epilogue addresses are computed here (opaque indices,
-    // as in set_sources)
-    int lane = tid & 63, h = lane >> 5, wm = wave / WAVES_N, wn = wave % WAVES_N;
-    asm volatile("" : "+v"(lane), "+v"(h), "+s"(wm), "+s"(wn));
-    // epilogue: y = acc * logit (FP8: ((acc * scale) * pertokenScale) * logit),
-    // guarded by the tile's valid rows and n; the lane's four column scales
-    // are read once per tile
+      for (int jj = 0; jj < FN; ++jj)
+        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[jj], acc[i][jj], 0, B8 ? 0 : 4, 0,
+                                                                      sa[i], 0, sb[jj]);
+  };
+
+  // epilogue: y = acc * logit (FP8: ((acc * scale) * pertokenScale) * logit),
+  // guarded by the tile's valid rows and n; row factors and column scales
+  // from LDS buffer pb (no global load here: a compiler-inserted wait for one
+  // would also wait for the next tile's copies in flight).  Returns whether
+  // every lane issued all FM*FN*16 stores (an ordered full tile).
+  auto epilogue = [&](const TileCoord& cc, int pb, v16f (&acc)[FM][FN]) -> bool {
+    // tile coordinates and lane-dependent addresses are computed here
+    // (opaque indices, as in set_sources)
+    int64_t row0 = uniform64(cc.row0), col0 = uniform64(cc.col0);
+    int valid = __builtin_amdgcn_readfirstlane(cc.valid_rows);
+    int lane = threadIdx.x & 63, h = lane >> 5, wm = wave / WAVES_N, wn = wave % WAVES_N;
+    asm volatile("" : "+s"(row0), "+s"(col0), "+s"(valid), "+v"(lane), "+v"(h), "+s"(wm), "+s"(wn));
     float col_scale[FN];
 #pragma unroll
     for (int jj = 0; jj < FN; ++jj) {
-      const int64_t col = min(c.col0 + wn * WTN + jj * 32 + (lane & 31), n - 1);
+      const int cl = wn * WTN + jj * 32 + (lane & 31);
       col_scale[jj] = 1.0f;
-      if (B8 && p.scale)
-        col_scale[jj] = p.scale_bf16
-                            ? __uint_as_float((uint32_t)((const uint16_t*)p.scale)[(int64_t)c.g * n + col] << 16)
-                            : ((const float*)p.scale)[(int64_t)c.g * n + col];
+      if (B8 && p.scale) {
+        if (p.scale_bf16) {
+          const uint32_t w = s_cs[pb][cl >> 1];
+          col_scale[jj] = __uint_as_float((cl & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        } else {
+          col_scale[jj] = __uint_as_float(s_cs[pb][cl]);
+        }
+      }
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int lr = wm * WTM + i * 32 + (r / 4) * 8 + h * 4 + (r % 4);
-        if (lr >= c.valid_rows) continue;
-        const int64_t row = c.row0 + lr;
-        const float lg = s_lg[lr];
-        const float pt = s_pt[lr];
+        if (lr >= valid) continue;
+        const int64_t row = row0 + lr;
+        const float lg = s_lg[pb][lr];
+        const float pt = s_pt[pb][lr];
         int64_t d = row;
         if constexpr (COMBINE == kCombineAtomic) {
           d = dest_row(p, row);
@@ -1379,7 +1388,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
         }
 #pragma unroll
         for (int jj = 0; jj < FN; ++jj) {
-          const int64_t col = c.col0 + wn * WTN + jj * 32 + (lane & 31);
+          const int64_t col = col0 + wn * WTN + jj * 32 + (lane & 31);
           if (col >= n) continue;
           float v = acc[i][jj][r];
           if constexpr (B8) {  // ((acc * scale) * pertokenScale) * logit, each rounded
@@ -1393,6 +1402,122 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
             __hip_atomic_fetch_add(p.out + d * n + col, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
+    }
+    return COMBINE == kCombineOrdered && valid == BM && col0 + BN <= n;
+  };
+
+  const int G = gridDim.x;
+  const bool blocked = G % kTileQueues == 0;
+  const int vq = blockIdx.x % kTileQueues, lw = blockIdx.x / kTileQueues, per_q = G / kTileQueues;
+  auto tile_at = [&](int jj) -> int {
+    if (blocked) return queue_tile(vq, jj * per_q + lw, total_tiles);
+    const int64_t tt = (int64_t)jj * G + blockIdx.x;
+    return tt < total_tiles ? (int)tt : -1;
+  };
+  // The k-steps run at a raised wave priority and the epilogue at the base
+  // one (where the two workgroups of a CU share a SIMD, the one in its k-loop
+  // issues first), except in a workgroup's last two tiles.
+  auto raise_priority = [&](int jj) {
+    if (tile_at(jj + 2) >= 0) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  };
+
+  if (ktiles >= STAGES) {
+    // Continuous copy pipeline: one stream of k-steps across the workgroup's
+    // tiles.  The refill issued at a k-step fetches the k-slice STAGES-1
+    // ahead, which near a tile's end is the next tile's (with its row
+    // factors), so a tile starts without a prologue wait.  Without a next
+    // tile the last refills copy this tile's first slices again (unused).
+    int j = 0;
+    const int t0 = tile_at(0);
+    if (t0 >= 0) {
+      TileCoord cur = coord(t0);
+      int t_nxt = tile_at(1);
+      TileCoord nxt = t_nxt >= 0 ? coord(t_nxt) : cur;
+      int pb = 0;
+      dma_rows(cur, pb);
+      set_sources(cur);
+#pragma unroll
+      for (int st = 0; st < STAGES - 1; ++st) issue_stage(st, st);
+      int stage = 0;
+      bool prev_full = false;
+      // After an ordered full-tile epilogue, its FM*FN*16 stores (issued
+      // after the next tile's first slices) may stay in flight while stage 0
+      // is awaited; after any other epilogue the plain wait also drains them.
+      constexpr int FULL_STORES = FM * FN * 16;
+      constexpr int W0_LO = (STAGES - 2) * LOADS_LO + FULL_STORES < 63 ? (STAGES - 2) * LOADS_LO + FULL_STORES : 63;
+      constexpr int W0_HI = (STAGES - 2) * LOADS_HI + FULL_STORES < 63 ? (STAGES - 2) * LOADS_HI + FULL_STORES : 63;
+      while (true) {
+        raise_priority(j);
+        v16f acc[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < FN; ++jj) acc[i][jj] = v16f{0};
+#pragma unroll 1
+        for (int kt = 0; kt < ktiles; ++kt) {
+          // this k-step's slice has landed; the STAGES-2 younger ones may still be in flight
+          if (kt == 0 && prev_full) {
+            if (lo_wave) wait_vmcnt<W0_LO>();
+            else wait_vmcnt<W0_HI>();
+          } else {
+            if (lo_wave) wait_vmcnt<(STAGES - 2) * LOADS_LO>();
+            else wait_vmcnt<(STAGES - 2) * LOADS_HI>();
+          }
+          lds_barrier();
+          const int fill = kt + STAGES - 1;
+          if (fill == ktiles) {  // from here on the refills are the next tile's
+            set_sources(nxt);
+            if (t_nxt >= 0) dma_rows(nxt, pb ^ 1);
+          }
+          issue_stage(stage == 0 ? STAGES - 1 : stage - 1, fill < ktiles ? fill : fill - ktiles);
+          compute(stage, kt, acc);
+          stage = stage + 1 == STAGES ? 0 : stage + 1;
+        }
+        __builtin_amdgcn_s_setprio(0);
+        prev_full = epilogue(cur, pb, acc);
+        if (t_nxt < 0) break;
+        ++j;
+        cur = nxt;
+        pb ^= 1;
+        t_nxt = tile_at(j + 1);
+        nxt = t_nxt >= 0 ? coord(t_nxt) : cur;
+      }
+    }
+  } else {
+    // Tile by tile (k shorter than the pipeline): each tile starts with its
+    // own prologue.
+    for (int j = 0;; ++j) {
+      const int t = tile_at(j);
+      if (t < 0) break;
+      const TileCoord c = coord(t);
+      __syncthreads();  // every wave is done with the previous tile's stages and row factors
+      raise_priority(j);
+      dma_rows(c, 0);
+      set_sources(c);
+#pragma unroll
+      for (int st = 0; st < STAGES - 1; ++st)
+        if (st < ktiles) issue_stage(st, st);
+      v16f acc[FM][FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj) acc[i][jj] = v16f{0};
+#pragma unroll 1
+      for (int kt = 0; kt < ktiles; ++kt) {
+        // stage kt complete; the stages issued after it may still be in flight
+        if (kt + STAGES - 2 < ktiles) {
+          if (lo_wave) wait_vmcnt<(STAGES - 2) * LOADS_LO>();
+          else wait_vmcnt<(STAGES - 2) * LOADS_HI>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        lds_barrier();
+        if (kt + STAGES - 1 < ktiles) issue_stage((kt + STAGES - 1) % STAGES, kt + STAGES - 1);
+        compute(kt % STAGES, kt, acc);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      epilogue(c, 0, acc);
     }
   }
   wait_vmcnt<0>();  // no copy in flight when the workgroup ends
