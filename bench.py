@@ -48,7 +48,7 @@ def parse():
                     help="force the GEMM tile height (0 = the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--transpose-x2", action="store_true",
-                    help="int8 weights given transposed, (e,n,k) (the operator's transposed-x2 form)")
+                    help="int8 or FP8 weights given transposed, (e,n,k) (the operator's transposed-x2 form)")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="rows in the oracle sample (0 = auto)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (torch copy_) 5 times: the reference kernel whose "

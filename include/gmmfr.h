@@ -21,7 +21,8 @@
  *       acc[i][j] = sum_b 2^(pts[i][b]-127) * 2^(scale[g][j][b]-127) * sum_{kk in b} x1[i][kk] * x2[g][j][kk]
  *   accumulated in fp32 by the matrix core (order unspecified), then
  *       y[i][j] = acc[i][j] * logit[i].
- *   FP8 mode (x1 and x2 FLOAT8_E4M3FN, x2 given as (e,n,k)): acc is the fp32
+ *   FP8 mode (x1 and x2 FLOAT8_E4M3FN, x2 (e,k,n), or (e,n,k) when
+ *   transposed): acc is the fp32
  *   sum of the FP8 products (order unspecified), then y as in the int8 mode:
  *       y[i][j] = ((acc[i][j] * scale[g][0][j]) * pertokenScale[i]) * logit[i].
  *   The output out (outputBS,n) fp32 starts at +0.0 with rows
@@ -105,13 +106,15 @@ typedef enum {
 typedef struct {
   /* x1: INT8 (m,k), rows sorted by expert; FLOAT8_E4M3FN (m,k) selects the
    * MxA8W4 mode (Atlas 350 notes) when x2 is FP4, with the other inputs as
-   * marked MX, or the FP8 mode when x2 is FLOAT8_E4M3FN (e,n,k) with
-   * transpose_x2 = 1 (scale and pertokenScale as for INT8; rowIndex INT64). required */
+   * marked MX, or the FP8 mode when x2 is FLOAT8_E4M3FN (e,k,n), or (e,n,k)
+   * with transpose_x2 = 1 (scale and pertokenScale as for INT8; rowIndex
+   * INT64).                                                            required */
   gmmfr_tensor x1;
   /* x2: INT8 (e,k,n); or INT32 (e,k,n/8) holding eight int4 per word, column
    * 8w+t in bits [4t,4t+4); or INT4 (e,k,n), the same bytes.  With
    * transpose_x2 = 1: INT8 (e,n,k), weight column j of expert g at
    * x2[g][j][:] (parameter notes: (e,n,k) when transposed).
+   * FP8: FLOAT8_E4M3FN (e,k,n), or (e,n,k) with transpose_x2 = 1.
    * MX: FLOAT4_E2M1X2 (e,n,k/2), i.e. (e,n,k) two per byte along k, with
    * transpose_x2 = 1.                                                  required */
   gmmfr_tensor x2;

@@ -117,7 +117,10 @@ def _scaled_rows(p, rows):
 def _scaled_weights(p, g):
     """Expert g's weights with their block scales applied (MX) or as decoded (FP8), float64 (n, k)."""
     if _is_fp8(p):
-        return FP8_TABLE[np.asarray(p.x2)[g]]
+        # (e,n,k) when given transposed, else (e,k,n) ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2",
+        # full-quant notes: x2 may be transposed or not)
+        w = np.asarray(p.x2)[g]
+        return FP8_TABLE[w if getattr(p, "x2_transposed", True) else w.T]
     w = FP4_TABLE[unpack_fp4(np.asarray(p.x2)[g])]
     s = E8M0_TABLE[np.asarray(p.scale)[g]].reshape(p.n, -1)  # (n, k/32)
     return w * np.repeat(s, 32, axis=1)
@@ -269,8 +272,9 @@ def brute(p):
             for j in range(p.n):
                 total = 0.0
                 for kk in range(p.k):
-                    if _is_fp8(p):  # both operands FP8, no block scales
-                        total += fp8_e4m3_value(int(x1[i, kk])) * fp8_e4m3_value(int(x2[g, j, kk]))
+                    if _is_fp8(p):  # both operands FP8, no block scales; x2 (e,n,k) or (e,k,n)
+                        wb = x2[g, j, kk] if getattr(p, "x2_transposed", True) else x2[g, kk, j]
+                        total += fp8_e4m3_value(int(x1[i, kk])) * fp8_e4m3_value(int(wb))
                         continue
                     byte = int(x2[g, j, kk // 2])
                     wcode = byte & 0xF if kk % 2 == 0 else byte >> 4

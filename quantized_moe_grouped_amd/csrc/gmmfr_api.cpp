@@ -143,8 +143,8 @@ int validate_mx(const gmmfr_args* a, Derived* d) {
 // FP8 E4M3 x1 and x2 ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2", parameter
 // notes: rowIndex INT64 only when x1 and x2 are FLOAT8_E4M3FN; Atlas 350
 // pertoken-perchannel quantisation): scale FLOAT32/BFLOAT16 (e,1,n) and
-// pertokenScale FLOAT32 (m) as in the int8 mode.  Ours: x2 given transposed,
-// (e,n,k), the matrix core's layout (transpose_x2 = 1); k % 64 == 0.
+// pertokenScale FLOAT32 (m) as in the int8 mode; x2 (e,k,n), or (e,n,k) with
+// transpose_x2 = 1 (full-quant notes).  Ours: k % 64 == 0, n % 16 == 0.
 int validate_fp8(const gmmfr_args* a, Derived* d) {
   if (a->x2.dtype != GMMFR_DT_FLOAT8_E4M3FN) return GMMFR_ERR_DTYPE;
   if (present(a->scale) && a->scale.dtype != GMMFR_DT_FLOAT32 && a->scale.dtype != GMMFR_DT_BFLOAT16)
@@ -159,12 +159,14 @@ int validate_fp8(const gmmfr_args* a, Derived* d) {
 
   if (const int st = check_attributes(a)) return st;
   if (a->transpose_x1 != 0) return GMMFR_ERR_ATTR;
-  if (a->transpose_x2 != 1) return GMMFR_ERR_UNSUPPORTED;  // (e,k,n) FP8 weights: not built
+  // x2 (e,k,n), or (e,n,k) when transposed (full-quant notes)
+  if (a->transpose_x2 != 0 && a->transpose_x2 != 1) return GMMFR_ERR_ATTR;
+  const bool trans_b = a->transpose_x2 == 1;
 
   if (a->x1.ndim != 2 || a->x2.ndim != 3) return GMMFR_ERR_SHAPE;
   const int64_t m = a->x1.dims[0], k = a->x1.dims[1];
-  const int64_t e = a->x2.dims[0], n = a->x2.dims[1];
-  if (a->x2.dims[2] != k) return GMMFR_ERR_SHAPE;
+  const int64_t e = a->x2.dims[0], n = a->x2.dims[trans_b ? 1 : 2];
+  if (a->x2.dims[trans_b ? 2 : 1] != k) return GMMFR_ERR_SHAPE;
   if (m < 0 || m >= (int64_t(1) << 31)) return GMMFR_ERR_SHAPE;
   if (e < 1 || e > kMaxExperts) return GMMFR_ERR_SHAPE;
   if (k < 64 || k > 65536 || k % 64 != 0) return GMMFR_ERR_SHAPE;
@@ -188,7 +190,7 @@ int validate_fp8(const gmmfr_args* a, Derived* d) {
     d->bsdp = bsdp;
     d->output_bs = a->output_bs;
     d->int4 = false;
-    d->trans_b = true;
+    d->trans_b = trans_b;
     d->mx = false;
     d->fp8 = true;
     d->scale_bf16 = present(a->scale) && a->scale.dtype == GMMFR_DT_BFLOAT16;

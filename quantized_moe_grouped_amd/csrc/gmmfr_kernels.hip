@@ -1160,8 +1160,11 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // scales; the instruction's scale operands are 1.0): acc is the fp32 sum and
 // y = ((acc * scale) * pertokenScale) * logit.  Measured on the device: with
 // both operands FP8, B lane l holds column l%32 with the byte layout of A.
-template <int COMBINE, bool B8>
+template <int COMBINE, bool B8, bool BKN>
 __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
+  // BKN (FP8 only): weights given (e,k,n); a B stage then holds BK weight rows
+  // of BN bytes, laid out and read with the int8 kernel's transpose reads
+  static_assert(!BKN || B8, "the (e,k,n) weight layout is an FP8 mode");
   constexpr int BM = 128, BN = 256, BK = 64, STAGES = B8 ? 3 : 4;
   constexpr int WAVES_N = 2, WTM = 64, WTN = 128, FM = 2, FN = 4;
   constexpr int A_BYTES = BM * BK;         // fp8: one byte per k
@@ -1235,16 +1238,29 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       const int64_t row = min(c.row0 + r, p.m - 1);  // rows past the group: loaded, never stored
       a_off[q] = (uint32_t)((row - c.row0) * k + ((cpos ^ swz_a<BK>(r)) * 16));
     }
-    const int64_t colb = B8 ? k : k / 2;  // bytes of one weight column
-    b_base = (const int8_t*)uniform64((int64_t)((const int8_t*)p.x2 + ((int64_t)c.g * n + c.col0) * colb));
+    if constexpr (BKN) {
+      // LDS chunk cpos of stage row r holds global chunk cpos ^ swz_b(r) of
+      // that weight row (the int8 kernel's B layout); past n: loaded, never stored
+      b_base = (const int8_t*)uniform64((int64_t)((const int8_t*)p.x2 + (int64_t)c.g * k * n + c.col0));
 #pragma unroll
-    for (int q = 0; q < B_INSTR; ++q) {
-      const int slot = (q * 4 + wave) * 64 + lane;
-      const int64_t cpr = B_COLB / 16;  // 16-byte chunks of a column per k-step
-      const int r = slot / cpr, cpos = slot % cpr;
-      const int64_t col = min(c.col0 + r, n - 1);    // columns past n: loaded, never stored
-      // fp8 columns are stored and read like A rows (same swizzle)
-      b_off[q] = (uint32_t)((col - c.col0) * colb + (B8 ? (cpos ^ swz_a<BK>(r)) : cpos) * 16);
+      for (int q = 0; q < B_INSTR; ++q) {
+        const int slot = (q * 4 + wave) * 64 + lane;
+        const int r = slot / (BN / 16), cpos = slot % (BN / 16);
+        const int64_t colb = min(c.col0 + ((cpos ^ swz_b(r)) * 16), n - 16);
+        b_off[q] = (uint32_t)((int64_t)r * n + (colb - c.col0));
+      }
+    } else {
+      const int64_t colb = B8 ? k : k / 2;  // bytes of one weight column
+      b_base = (const int8_t*)uniform64((int64_t)((const int8_t*)p.x2 + ((int64_t)c.g * n + c.col0) * colb));
+#pragma unroll
+      for (int q = 0; q < B_INSTR; ++q) {
+        const int slot = (q * 4 + wave) * 64 + lane;
+        const int64_t cpr = B_COLB / 16;  // 16-byte chunks of a column per k-step
+        const int r = slot / cpr, cpos = slot % cpr;
+        const int64_t col = min(c.col0 + r, n - 1);    // columns past n: loaded, never stored
+        // fp8 columns are stored and read like A rows (same swizzle)
+        b_off[q] = (uint32_t)((col - c.col0) * colb + (B8 ? (cpos ^ swz_a<BK>(r)) : cpos) * 16);
+      }
     }
     sa_base = (const uint32_t*)uniform64((int64_t)(sa_words + c.row0 * kdw));
     sa_off = (uint32_t)((min(c.row0 + tid, p.m - 1) - c.row0) * kdw * 4);
@@ -1258,7 +1274,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
                    __builtin_amdgcn_readfirstlane(lds_addr(sA + st * A_BYTES + (q * 4 + wave) * 64 * 16)));
 #pragma unroll
     for (int q = 0; q < B_INSTR; ++q)
-      lds_dma16_sv(b_base + (int64_t)kt * B_COLB, b_off[q],
+      lds_dma16_sv(b_base + (int64_t)kt * (BKN ? (int64_t)BK * n : (int64_t)B_COLB), b_off[q],
                    __builtin_amdgcn_readfirstlane(lds_addr(sB + st * B_BYTES + (q * 4 + wave) * 64 * 16)));
     if constexpr (!B8) {
       // the dword holding the two block scales of k-step kt (and of its neighbour)
@@ -1327,7 +1343,22 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
 #pragma unroll
     for (int jj = 0; jj < FN; ++jj) {
       const int cl = wn * WTN + jj * 32 + (lane & 31);
-      if constexpr (B8) {
+      if constexpr (BKN) {
+        // two transpose reads per 16 k (as the int8 kernel's B fragment of one
+        // k-substep); k 16h.. and 32+16h.. of column cl make the 32 bytes
+        v4i half[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int r = kk * 32 + h * 16 + ((lane & 15) >> 1);
+          const int col = wn * WTN + jj * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+          const int8_t* a0 = b_st + r * BN + (((col >> 4) ^ swz_b(r)) << 4) + (col & 15);
+          const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0));
+          const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0 + 8 * BN));  // same swizzle
+          half[kk] = v4i{lo.x, lo.y, hi.x, hi.y};
+        }
+        bf[jj] = v8i{half[0].x, half[0].y, half[0].z, half[0].w, half[1].x, half[1].y, half[1].z, half[1].w};
+        sb[jj] = 127;
+      } else if constexpr (B8) {
         const v4i lo = *(const LDS_PTR(v4i))(b_st + cl * BK + ((h ^ swz_a<BK>(cl)) << 4));
         const v4i hi = *(const LDS_PTR(v4i))(b_st + cl * BK + (((2 + h) ^ swz_a<BK>(cl)) << 4));
         bf[jj] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -1741,7 +1772,7 @@ bool uses_continuous_pipeline(bool int4, int64_t k, int bm, int bk, int stages) 
 
 const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool mx, bool fp8) {
   if (mx) return "mx_gemm_kernel<128,256,64,2x2,s4,fp8xfp4>";
-  if (fp8) return "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8>";
+  if (fp8) return trans_b ? "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8>" : "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8,kn>";
   // per tile: i8, i4, i8 cont, i4 cont, i8 transposed weights, i8 cont transposed weights
   static const char* names[kNumTiles][6] = {
       {"gmm_kernel<256,256,64,2x2,s3,i8>", "gmm_kernel<256,256,64,2x2,s3,i4>", "gmm_kernel<256,256,64,2x2,s3,i8,cont>",
@@ -1875,14 +1906,21 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
     const size_t dyn = ((size_t)(2 * kp.e + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
     if (a.mx) {
       if (kp.combine == kCombineOrdered)
-        hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, false>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
+        hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, false, false>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
       else
-        hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, false>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
+        hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, false, false>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
     } else if (a.fp8) {
-      if (kp.combine == kCombineOrdered)
-        hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, true>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
-      else
-        hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, true>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
+      if (a.trans_b) {
+        if (kp.combine == kCombineOrdered)
+          hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, true, false>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
+        else
+          hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, true, false>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
+      } else {
+        if (kp.combine == kCombineOrdered)
+          hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, true, true>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
+        else
+          hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, true, true>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
+      }
     } else switch (plan.tile) {
       case kTile256x256: launch_gemm<256, 256, 64, 2, 2, 3, 1>(kp, a.int4, a.trans_b, plan.grid, s); break;
       case kTile128x256: launch_gemm<128, 256, 64, 2, 2, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;

@@ -282,9 +282,9 @@ def random_problem(seed: int, m: int, k: int, n: int, e: int, *,
 
 
 def with_transposed_weights(p: Problem) -> Problem:
-    """The same problem with its int8 weights given transposed, (e,n,k)."""
-    if p.x2_int4 or p.x2_transposed:
-        raise ValueError("transposed weights are taken from an untransposed int8 problem")
+    """The same problem with its int8 or FP8 weights given transposed, (e,n,k)."""
+    if p.x2_int4 or p.x2_transposed or p.mx:
+        raise ValueError("transposed weights are taken from an untransposed int8 or FP8 problem")
     return dataclasses.replace(p, x2=np.ascontiguousarray(np.transpose(p.x2, (0, 2, 1))), x2_transposed=True,
                                name=p.name + "-tb")
 
@@ -403,10 +403,19 @@ def fp8_problem(seed: int, m: int, k: int, n: int, e: int, *, scale_bf16: bool =
                    seed, counts, True, fp8=True)
 
 
+def with_untransposed_fp8_weights(p: Problem) -> Problem:
+    """The same FP8 problem with its weights given untransposed, (e,k,n)."""
+    if not p.fp8 or not p.x2_transposed:
+        raise ValueError("untransposed weights are taken from an FP8 problem with (e,n,k) weights")
+    return dataclasses.replace(p, x2=np.ascontiguousarray(np.transpose(p.x2, (0, 2, 1))), x2_transposed=False,
+                               name=p.name + "-kn")
+
+
 def make_fp8_config(name: str = "fp8", seed: int = 0) -> Problem:
     """FP8 E4M3 at the prefill shape: routing, logit, bf16 per-channel scale,
     pertokenScale and sharedInput drawn as for the prefill workload; FP8
-    activations and weights (e,n,k) drawn like the MxA8W4 activations."""
+    activations and weights drawn like the MxA8W4 activations, the weights
+    given untransposed, (e,k,n) (drawn as (e,n,k) codes and transposed)."""
     if name != "fp8":
         raise ValueError(name)
     rng = np.random.default_rng(seed)
@@ -421,8 +430,9 @@ def make_fp8_config(name: str = "fp8", seed: int = 0) -> Problem:
     scale = f32_to_bf16_bits(rng.uniform(1e-3, 1e-2, size=(e, 1, n)).astype(np.float32))
     pts = rng.uniform(1e-3, 1e-2, size=m).astype(np.float32)
     shared = f32_to_bf16_bits(rng.standard_normal((8192, n)).astype(np.float32))
-    return Problem(name, m, k, n, e, x1, x2, False, scale, True, pts, logit,
-                   _group_list(counts, 0), 0, ri, shared, 4096, obs, seed, counts, True, fp8=True)
+    p = Problem(name, m, k, n, e, x1, x2, False, scale, True, pts, logit,
+                _group_list(counts, 0), 0, ri, shared, 4096, obs, seed, counts, True, fp8=True)
+    return dataclasses.replace(with_untransposed_fp8_weights(p), name=name)
 
 
 # ---------------------------------------------------------------- activation quant + routing permute inputs

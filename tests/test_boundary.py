@@ -306,8 +306,10 @@ MX_CASES = [
     ("fp8_per_tensor_pertoken", _fp8_args, dict(pertoken_scale=_fake(B.DT_FLOAT32, 1)), B.OK),
     ("fp8_pertoken_len", _fp8_args, dict(pertoken_scale=_fake(B.DT_FLOAT32, 2)), B.ERR_SHAPE),
     ("fp8_bf16_scale", _fp8_args, dict(scale=_fake(B.DT_BFLOAT16, 8, 1, 7168)), B.OK),
-    ("fp8_untransposed", _fp8_args, dict(transpose_x2=0, x2=_fake(B.DT_FLOAT8_E4M3FN, 8, 2048, 7168)),
-     B.ERR_UNSUPPORTED),
+    ("fp8_untransposed", _fp8_args, dict(transpose_x2=0, x2=_fake(B.DT_FLOAT8_E4M3FN, 8, 2048, 7168)), B.OK),
+    ("fp8_untransposed_k_mismatch", _fp8_args, dict(transpose_x2=0, x2=_fake(B.DT_FLOAT8_E4M3FN, 8, 7168, 2048)),
+     B.ERR_SHAPE),
+    ("fp8_transpose_value", _fp8_args, dict(transpose_x2=2), B.ERR_ATTR),
     ("fp8_row_index_i32", _fp8_args, dict(row_index=_fake(B.DT_INT32, 512)), B.ERR_DTYPE),
     ("fp8_acc_dump", _fp8_args, dict(acc_out=_fake(B.DT_INT32, 512, 7168)), B.ERR_UNSUPPORTED),
     ("fp8_x2_int8", _fp8_args, dict(x2=_fake(B.DT_INT8, 8, 7168, 2048)), B.ERR_DTYPE),

@@ -92,6 +92,39 @@ def test_fp8_random_case_all_elements(name):
 
 
 
+@pytest.mark.parametrize("name", list(FP8_CASES), ids=list(FP8_CASES))
+def test_fp8_untransposed_weights(name):
+    """FP8 weights given (e,k,n) (full-quant notes: x2 transposed or not)."""
+    p = W.with_untransposed_fp8_weights(W.fp8_problem(**FP8_CASES[name]))
+    ref, bound, _ = MX.run(p)
+    d = G.to_device(p)
+    for det, combine in ((True, "auto"), (False, "atomic")):
+        out, _ = G.run_gpu(p, d, deterministic=det, combine=combine)
+        _check(p, out.cpu().numpy(), ref, bound)
+
+
+def test_fp8_untransposed_ordered_is_run_to_run_identical():
+    """The ordered combine is run-to-run identical with (e,k,n) weights."""
+    p = W.with_untransposed_fp8_weights(W.fp8_problem(**FP8_CASES["long_k"]))
+    d = G.to_device(p)
+    a, _ = G.run_gpu(p, d, deterministic=True)
+    b, _ = G.run_gpu(p, d, deterministic=True)
+    G.assert_bitexact(b.cpu().numpy(), a.cpu().numpy())
+
+
+def test_fp8_transposed_workload_sampled_rows():
+    """The FP8 workload (weights (e,k,n)) with its weights given transposed, (e,n,k)."""
+    p = W.with_transposed_weights(W.make_fp8_config("fp8", 0))
+    assert p.x2_transposed and p.x2.shape == (p.e, p.n, p.k)
+    rng = np.random.default_rng(102)
+    dsel = np.array(sorted(set(rng.choice(p.output_bs, size=24, replace=False).tolist())
+                           | {0, p.output_bs - 1, 4095, 4096, 12287, 12288}), dtype=np.int64)
+    ref, bound = MX.out_rows(p, dsel)
+    d = G.to_device(p)
+    out, _ = G.run_gpu(p, d, deterministic=True)
+    _check(p, out.cpu().numpy()[dsel], ref, bound)
+
+
 @pytest.mark.parametrize("name", ["ragged_bf16_shared", "many_empty"])
 def test_fp8_per_tensor_scale(name):
     """pertokenScale of shape (1): one static per-tensor activation scale."""

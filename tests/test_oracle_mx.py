@@ -273,3 +273,23 @@ def test_fp8_per_tensor_scale_is_every_rows_scale():
     on, _, _ = MX.run(none)
     o8, _, _ = MX.run(W.with_per_tensor_scale(p, 8.0))
     assert np.array_equal(o8, on * 8.0)
+
+
+def test_fp8_untransposed_weights_equal_transposed():
+    """FP8 weights given (e,k,n) instead of (e,n,k) ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2",
+    full-quant notes: x2 transposed or not) compute the same result; the brute
+    force indexes the (e,k,n) array directly; reading the bytes with the other
+    layout changes the result."""
+    p = W.fp8_problem(27, 30, 64, 32, 3, output_bs=20, bsdp=3, shared_offset=2)
+    q = W.with_untransposed_fp8_weights(p)
+    assert q.x2.shape == (p.e, p.k, p.n) and not q.x2_transposed
+    op, bp, ap = MX.run(p)
+    oq, bq, aq = MX.run(q)
+    assert np.array_equal(op, oq) and np.array_equal(bp, bq) and np.array_equal(ap, aq)
+    small = W.with_untransposed_fp8_weights(W.fp8_problem(28, 7, 64, 6, 2, output_bs=4))
+    _, _, acc = MX.run(small)
+    assert np.allclose(acc, MX.brute(small), rtol=1e-12, atol=0.0)
+    wrong = copy.deepcopy(q)
+    wrong.x2_transposed = True
+    wrong.x2 = np.ascontiguousarray(q.x2.reshape(p.e, p.n, p.k))  # (e,k,n) bytes read as (e,n,k)
+    assert not np.array_equal(MX.run(wrong)[0], op)
