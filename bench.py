@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="prefill",
-                    choices=["tiny", "decode", "skewed", "prefill", "int4", "mxa8w4", "fp8", "dispatch"])
+                    choices=["tiny", "decode", "skewed", "prefill", "int4", "mxa8w4", "fp8", "dispatch", "layer"])
     ap.add_argument("--combine", default="auto", choices=["auto", "atomic", "ordered"])
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
@@ -239,6 +239,76 @@ def bench_dispatch(args):
     del keep
 
 
+def bench_layer(args):
+    """Both entry points in sequence at the prefill shape: bf16 hidden states of
+    16384 tokens and their top-8 of 32 router choices -> quantise and permute
+    -> grouped int8 GEMM with dequant and the combine by token.  int8 TOPS of
+    the whole layer (the GEMM's 2*m*k*n over the time of both calls)."""
+    import numpy as np
+    import torch
+    from quantized_moe_grouped_amd import binding as B
+    from quantized_moe_grouped_amd import workloads as W
+
+    rp = W.make_route_config("dispatch", args.seed)
+    pw = W.make_config("prefill", args.seed)  # weights, scales and sharedInput of the prefill workload
+    dev = "cuda"
+    m, n = rp.T * rp.K, pw.n
+    hidden = torch.from_numpy(rp.hidden.view(np.int16)).to(dev).view(torch.bfloat16)
+    ids = torch.from_numpy(rp.expert_ids).to(dev)
+    w = torch.from_numpy(rp.topk_weights).to(dev)
+    x1 = torch.empty((m, rp.k), dtype=torch.int8, device=dev)
+    pts = torch.empty(m, dtype=torch.float32, device=dev)
+    logit = torch.empty(m, dtype=torch.float32, device=dev)
+    ri = torch.empty(m, dtype=torch.int64, device=dev)
+    gl = torch.empty(rp.e, dtype=torch.int64, device=dev)
+    qargs, qkeep = B.make_qp_args(hidden, ids, x1, pts, ri, gl, topk_weights=w, logit=logit, group_list_type=1)
+    qws = torch.empty(max(B.qp_workspace_size(qargs), 1), dtype=torch.uint8, device=dev)
+    x2 = torch.from_numpy(pw.x2).to(dev)
+    scale = torch.from_numpy(np.ascontiguousarray(pw.scale).view(np.int16)).to(dev).view(torch.bfloat16)
+    shared = torch.from_numpy(np.ascontiguousarray(pw.shared_input).view(np.int16)).to(dev).view(torch.bfloat16)
+    out = torch.empty((rp.T, n), dtype=torch.float32, device=dev)
+    gargs, gkeep = B.make_args(x1, x2, gl, out, scale=scale, pertoken_scale=pts, logit=logit, row_index=ri,
+                               shared_input=shared, shared_input_offset=pw.shared_input_offset, group_list_type=1,
+                               deterministic=args.deterministic, combine=args.combine,
+                               tuning_config=[m // rp.e])  # expected rows per expert (the tiling hint)
+    plan = B.plan(gargs)
+    gws = torch.empty(max(B.workspace_size(gargs), 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = Hip()
+    ev = (hip.event(), hip.event())
+
+    def step():
+        st = B.lib().gmm_quant_permute(ctypes.byref(qargs), ctypes.c_void_p(qws.data_ptr()),
+                                       ctypes.c_size_t(qws.numel()), ctypes.c_void_p(stream))
+        if st != 0:
+            raise B.GmmfrError(st, "gmm_quant_permute")
+        B.run(gargs, gws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    hip.record(ev[0], stream)
+    for _ in range(args.steps):
+        step()
+    hip.record(ev[1], stream)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(*ev) / args.steps
+    ops = 2.0 * m * rp.k * n
+    res = {
+        "metric": "int8 TOPS of a whole MoE expert layer (quantise + permute + GMM + finalize-routing) at 1 GPU",
+        "value": round(ops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic (seeded bf16 hidden states and top-8 router choices; the prefill workload's weights)",
+        "config": {"workload": "layer", "tokens": rp.T, "top_k": rp.K, "m": m, "e": rp.e, "k": rp.k, "n": n,
+                   "combine": plan["combine"], "gemm_kernel": plan["gemm_kernel"], "seed": args.seed,
+                   "ops_per_step": ops},
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+    del qkeep, gkeep
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -268,6 +338,9 @@ def main():
         return
     if args.config == "dispatch":
         bench_dispatch(args)
+        return
+    if args.config == "layer":
+        bench_layer(args)
         return
     print(f"[bench] generating {args.config} seed {args.seed}", file=sys.stderr, flush=True)
     if args.config == "mxa8w4":
