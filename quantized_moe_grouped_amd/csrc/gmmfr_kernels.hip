@@ -421,7 +421,8 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   int64_t b4_col0 = 0;
   uint4 b4reg[REGB4 ? B4_PER : 1];
   auto set_sources = [&](const TileCoord& c) {
-    a_base = p.x1 + c.row0 * k;
+    // copy bases are wave-uniform (SGPRs: the copies' saddr operand)
+    a_base = (const int8_t*)uniform64((int64_t)(p.x1 + c.row0 * k));
 #pragma unroll
     for (int q = 0; q < A_INSTR; ++q) {
       const int slot = (q * NWAVES + wave) * 64 + lane;
@@ -431,7 +432,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     }
     if constexpr (TB) {
       // weight column col is k contiguous bytes; columns past n: loaded, never stored
-      b_base = (const int8_t*)p.x2 + ((int64_t)c.g * n + c.col0) * k;
+      b_base = (const int8_t*)uniform64((int64_t)((const int8_t*)p.x2 + ((int64_t)c.g * n + c.col0) * k));
 #pragma unroll
       for (int q = 0; q < B_INSTR; ++q) {
         const int slot = (q * NWAVES + wave) * 64 + lane;
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     } else if constexpr (!REGB4) {
       // bytes of one weight row, and the tile's first byte in it
       const int64_t rowb = PACKED ? n / 2 : n, col0b = PACKED ? c.col0 / 2 : c.col0;
-      b_base = (const int8_t*)p.x2 + (int64_t)c.g * k * rowb + col0b;
+      b_base = (const int8_t*)uniform64((int64_t)((const int8_t*)p.x2 + (int64_t)c.g * k * rowb + col0b));
 #pragma unroll
       for (int q = 0; q < B_INSTR; ++q) {
         const int slot = (q * NWAVES + wave) * 64 + lane;
