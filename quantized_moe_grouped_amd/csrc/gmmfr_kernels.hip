@@ -10,8 +10,10 @@
 //
 // Kernels
 //   seed_kernel        out := 0, rows [off, off+bsdp) := widened sharedInput
-//   gmm_kernel<...>    persistent grouped GEMM; epilogue adds into out with
-//                      fp32 atomics, or stores y for the ordered combine
+//   gmm_kernel<...>    persistent grouped int8 / int4 GEMM; epilogue adds into
+//                      out with fp32 atomics, or stores y for the ordered combine
+//   mx_gemm_kernel<..> the same for FP8 x FP4 (MxA8W4, E8M0 block scales) and
+//                      FP8 x FP8 weights, on the block-scaled MFMA
 //   hist/scan/scatter  rows bucketed by destination (ordered combine)
 //   reduce_kernel      per destination: sort its rows ascending, fold
 //                      seed + y[rows] in that order, write out once
@@ -1156,11 +1158,12 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// FP8 (B8 = true): the same kernel for FP8 E4M3 weights given (e,n,k) with
-// per-channel scale and per-token pertokenScale as in the int8 mode (no block
-// scales; the instruction's scale operands are 1.0): acc is the fp32 sum and
-// y = ((acc * scale) * pertokenScale) * logit.  Measured on the device: with
-// both operands FP8, B lane l holds column l%32 with the byte layout of A.
+// FP8 (B8 = true): the same kernel for FP8 E4M3 weights, given (e,n,k) or,
+// with BKN, (e,k,n), with per-channel scale and per-token pertokenScale as in
+// the int8 mode (no block scales; the instruction's scale operands are 1.0):
+// acc is the fp32 sum and y = ((acc * scale) * pertokenScale) * logit.
+// Measured on the device: with both operands FP8, B lane l holds column l%32
+// with the byte layout of A.
 template <int COMBINE, bool B8, bool BKN>
 __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   // BKN (FP8 only): weights given (e,k,n); a B stage then holds BK weight rows
