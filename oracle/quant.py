@@ -30,6 +30,18 @@ matmul then takes: int8 x with one float perTokenScale per row.  Readings taken
 
 Rows at and past sum(counts) are not defined (the grouped matmul never reads
 them).  Hidden values must be finite.
+
+FP8 outputs (for the FP8 and MxA8W4 grouped matmuls; readings, the pages
+giving only the mode names and the multiply by an inverse scale):
+  fp8 per token:  scale_t = fl(amax_t / 448), inv = fl(448 / amax_t) (0 when
+                  amax_t = 0), code = E4M3(fl(x * inv)), 448 being the
+                  largest finite E4M3 value;
+  mx (per 32 k):  the OCP MX v1.0 conversion: for each block of 32 values of a
+                  token, shared exponent s = floor(log2(amax_b)) - 8 (8 = the
+                  largest E4M3 exponent), clamped to [-127, 127] (-127 for an
+                  all-zero block), E8M0 code s + 127, element code
+                  E4M3(clamp(x * 2^-s, -448, 448)).
+E4M3(v) rounds to the nearest E4M3 value, ties to the even code.
 """
 from __future__ import annotations
 
@@ -58,6 +70,61 @@ def quantize(hidden_bits):
     return q, scale
 
 
+_E4M3_CODES = np.arange(0x00, 0x7F)  # non-negative finite codes (0x7F is NaN)
+
+
+def _e4m3_values():
+    from .mx import FP8_TABLE  # decoded from the format definition
+    return FP8_TABLE[_E4M3_CODES]
+
+
+def e4m3_encode(v):
+    """FP8 E4M3 codes (uint8) of finite values with |v| <= 448: nearest
+    representable value, ties to the even code; the sign bit from v."""
+    vals = _e4m3_values()
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    if (a > 448.0).any():
+        raise ValueError("E4M3 encode: value beyond 448")
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 1, len(vals) - 1)
+    lo = hi - 1
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    pick = np.where(dhi < dlo, hi, np.where(dlo < dhi, lo, np.where(_E4M3_CODES[lo] % 2 == 0, lo, hi)))
+    code = _E4M3_CODES[pick].astype(np.uint8)
+    return code | (np.signbit(v).astype(np.uint8) << 7)
+
+
+def quantize_fp8(hidden_bits):
+    """FP8 per token: (codes uint8 (T,k), scale float32 (T))."""
+    x = bf16_to_f32(hidden_bits)
+    amax = np.abs(x).max(axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    if not np.isfinite(amax).all():
+        raise ValueError("hidden values must be finite")
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    inv = np.zeros_like(amax)
+    nz = amax > 0
+    inv[nz] = np.float32(448.0) / amax[nz]
+    prod = (x * inv[:, None]).astype(np.float32)
+    return e4m3_encode(np.clip(prod, -448.0, 448.0)), scale
+
+
+def quantize_mx(hidden_bits):
+    """MX per 32 values: (codes uint8 (T,k), E8M0 codes uint8 (T, k/32))."""
+    x = bf16_to_f32(hidden_bits).astype(np.float64)
+    T, k = x.shape
+    if k % 32:
+        raise ValueError("k must be a multiple of 32")
+    xb = x.reshape(T, k // 32, 32)
+    amax = np.abs(xb).max(axis=2)
+    if not np.isfinite(amax).all():
+        raise ValueError("hidden values must be finite")
+    _, ex = np.frexp(amax)                      # amax = f * 2^ex, f in [0.5, 1)
+    s = np.where(amax > 0, ex - 1 - 8, -127)    # floor(log2(amax)) - 8
+    s = np.clip(s, -127, 127)
+    v = np.clip(xb * np.exp2(-s)[:, :, None], -448.0, 448.0)  # exact: a power-of-two scaling
+    return e4m3_encode(v).reshape(T, k), (s + 127).astype(np.uint8)
+
+
 def permute(expert_ids, e: int, expert_offset: int = 0):
     """Steps 2-3 on the indices: (order of flat entries f, counts (e))."""
     ids = np.asarray(expert_ids).astype(np.int64).reshape(-1)
@@ -69,7 +136,8 @@ def permute(expert_ids, e: int, expert_offset: int = 0):
 
 
 def run(rp):
-    """All four steps.  Returns a dict: x1 (m,k) int8, pertoken_scale (m),
+    """All four steps.  Returns a dict: x1 (m,k) int8 (FP8 modes: uint8 E4M3
+    codes), pertoken_scale (m) float32 (mx: uint8 E8M0 codes (m, k/32)),
     logit (m) or None, row_index (m) int64, group_list (e) int64, and
     ``rows`` = sum(counts); entries at and past ``rows`` are zero here and
     undefined in the operator."""
@@ -78,14 +146,22 @@ def run(rp):
         raise ValueError("shapes")
     if rp.group_list_type not in (0, 1):
         raise ValueError("groupListType")
-    q, scale = quantize(rp.hidden)
+    mode = getattr(rp, "mode", "int8")
+    if mode == "int8":
+        q, scale = quantize(rp.hidden)
+    elif mode == "fp8":
+        q, scale = quantize_fp8(rp.hidden)
+    elif mode == "mx":
+        q, scale = quantize_mx(rp.hidden)
+    else:
+        raise ValueError(mode)
     order, counts = permute(rp.expert_ids, e, rp.expert_offset)
     m = T * K
     rows = len(order)
     tok = order // K if K > 0 else order
-    x1 = np.zeros((m, k), dtype=np.int8)
+    x1 = np.zeros((m, k), dtype=q.dtype)
     x1[:rows] = q[tok]
-    pts = np.zeros(m, dtype=np.float32)
+    pts = np.zeros((m,) + scale.shape[1:], dtype=scale.dtype)
     pts[:rows] = scale[tok]
     ri = np.zeros(m, dtype=np.int64)
     ri[:rows] = tok

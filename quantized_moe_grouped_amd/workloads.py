@@ -460,6 +460,7 @@ class RouteProblem:
     expert_offset: int = 0
     group_list_type: int = 1
     seed: int = 0
+    mode: str = "int8"   # x1 as int8 per token, "fp8" per token, or "mx" (FP8 with E8M0 per 32 k)
 
     @property
     def m(self) -> int:

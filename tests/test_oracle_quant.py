@@ -2,6 +2,8 @@
 exactly representable rows, round-half-to-even ties, zero rows, the rounding
 bound, power-of-two scaling, a pure-Python permute, groupList types, and the
 composition with the grouped matmul oracle against a float64 MoE layer."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -144,3 +146,112 @@ def test_dispatch_config_shapes():
     assert (rp.T, rp.k, rp.K, rp.e) == (16384, 2048, 8, 32)
     _, counts = Q.permute(rp.expert_ids, rp.e)
     assert counts.sum() == 131072 and counts.min() > 3500 and counts.max() < 4700
+
+
+# ---------------------------------------------------------------- FP8 outputs (per token; MX per 32 k)
+
+def test_e4m3_encoder_matches_torch_and_rounds_ties_to_even():
+    """The encoder against torch's float8_e4m3fn conversion (a library
+    routine) on fp32 values over the whole range, and on values exactly
+    half-way between codes (ties go to the even code)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(41)
+    v = np.concatenate([np.linspace(-448, 448, 20001),
+                        rng.uniform(-1, 1, 20000) * np.exp2(rng.integers(-12, 9, 20000))]).astype(np.float32)
+    v = np.clip(v, -448, 448)
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (Q.e4m3_encode(v) == want).all()
+    # 84 lies half-way between 80 (mantissa 010) and 88 (011): the even one;
+    # 2^-9 * 1.5 half-way between the subnormals 1 and 2 (x 2^-9): code 2
+    assert Q.e4m3_encode(np.array([84.0, 92.0, -84.0, 1.5 * 2.0 ** -9], np.float32)).tolist() == \
+        [0x6A, 0x6C, 0xEA, 0x02]
+
+
+def _decode(codes):
+    from oracle.mx import FP8_TABLE
+    return FP8_TABLE[np.asarray(codes)]
+
+
+def test_fp8_per_token_exact_rows_and_bound():
+    """x = s * v with v on the E4M3 grid and max|v| = 448: amax = 448 s, so
+    scale = s, inv = 1/s (s a power of two) and the codes decode to v exactly;
+    random rows decode within half an E4M3 step (relative 2^-4) of x/scale."""
+    rng = np.random.default_rng(42)
+    from oracle.mx import FP8_TABLE
+    grid = FP8_TABLE[np.arange(0, 0x7F)]
+    v = rng.choice(grid, size=(5, 64)) * rng.choice([-1.0, 1.0], size=(5, 64))
+    v[:, 7] = 448.0
+    s = np.exp2(rng.integers(-10, 4, size=(5, 1)))
+    x = (v * s).astype(np.float32)
+    assert np.array_equal(W.bf16_bits_to_f32(W.f32_to_bf16_bits(x)), x)
+    codes, scale = Q.quantize_fp8(W.f32_to_bf16_bits(x))
+    assert np.array_equal(scale, s[:, 0].astype(np.float32))
+    assert np.array_equal(_decode(codes), v)
+    rp = W.route_problem(43, 40, 256, 2, 3)
+    codes, scale = Q.quantize_fp8(rp.hidden)
+    xr = W.bf16_bits_to_f32(rp.hidden).astype(np.float64)
+    dq = _decode(codes) * scale[:, None]
+    assert (np.abs(dq - xr) <= np.abs(xr) * 2.0 ** -4 + scale[:, None] * 2.0 ** -9 * 1.01).all()
+
+
+def test_mx_block_scales_follow_the_block_maximum():
+    """Each 32-value block gets E8M0 code floor(log2(amax)) - 8 + 127: a block
+    whose largest magnitude is 2^e * 1.x gets code e + 119; values scaled by
+    2^p shift the code by p; an all-zero block gets code 0 and zero elements;
+    values in [448, 512) after scaling saturate to 448; blocks are independent."""
+    x = np.zeros((2, 96), np.float32)
+    x[0, :32] = np.linspace(-3.0, 3.0, 32)        # amax 3 = 1.5 * 2^1 -> code 120
+    x[0, 32:64] = 0.0                              # zero block -> code 0
+    x[0, 64:96] = 2.0 ** -20                       # amax 2^-20 -> code 99
+    x[1, :32] = 1.96875 * 2.0 ** 5                 # amax 63 -> 63 / 2^-3 = 504 -> saturates to 448
+    x[1, 32:64] = np.linspace(0.0, 1.0, 32) * 2.0 ** 7
+    x[1, 64:96] = -(2.0 ** 100)
+    codes, sc = Q.quantize_mx(W.f32_to_bf16_bits(x))
+    assert sc.tolist() == [[120, 0, 99], [124, 126, 219]]
+    assert (codes[0, 32:64] == 0).all()
+    assert (_decode(codes[1, :32]) == 448.0).all()
+    assert (codes[1, 64:96] == Q.e4m3_encode(np.float32(-256.0))).all()
+    two = Q.quantize_mx(W.f32_to_bf16_bits(x * np.float32(2.0 ** 3)))
+    assert (two[0] == codes).all() and (two[1][sc > 0] == sc[sc > 0] + 3).all()
+
+
+def test_fp8_modes_permute_like_int8():
+    """The FP8 and MX modes route rows exactly as the int8 mode; only x1 and
+    pertokenScale change, to the per-token codes and scales."""
+    rp = W.route_problem(44, 50, 128, 4, 5, expert_offset=1, n_gate=7)
+    r8 = Q.run(rp)
+    for mode, qf in (("fp8", Q.quantize_fp8), ("mx", Q.quantize_mx)):
+        rp.mode = mode
+        r = Q.run(rp)
+        rows = r["rows"]
+        assert rows == r8["rows"] and (r["row_index"] == r8["row_index"]).all()
+        assert (r["group_list"] == r8["group_list"]).all() and np.array_equal(r["logit"], r8["logit"])
+        q, s = qf(rp.hidden)
+        t = r["row_index"][:rows]
+        assert (r["x1"][:rows] == q[t]).all() and np.array_equal(r["pertoken_scale"][:rows], s[t])
+    rp.mode = "int8"
+
+
+def test_mx_composition_with_the_mx_matmul_oracle():
+    """MX producer -> MxA8W4 grouped-matmul oracle (FP4 weights) equals the
+    float64 layer built from the decoded codes and block scales."""
+    from oracle import mx as MX
+    T, k, n, K, e = 20, 128, 32, 2, 3
+    rp = W.route_problem(45, T, k, K, e, group_list_type=0)
+    rp.mode = "mx"
+    r = Q.run(rp)
+    m = T * K
+    base = W.mx_problem(46, m, k, n, e, output_bs=T)
+    p = dataclasses.replace(base, x1=r["x1"], pertoken_scale=r["pertoken_scale"].reshape(m, k // 64, 2),
+                            logit=r["logit"], group_list=r["group_list"], group_list_type=0,
+                            row_index=r["row_index"], shared_input=None, counts=np.diff(np.r_[0, r["group_list"]]))
+    out, bound, _ = MX.run(p)
+    a = _decode(r["x1"]).reshape(m, k // 32, 32) * MX.E8M0_TABLE[r["pertoken_scale"]][:, :, None]
+    ref = np.zeros((T, n))
+    ends = r["group_list"]
+    for g in range(e):
+        s0 = 0 if g == 0 else ends[g - 1]
+        wg = MX._scaled_weights(p, g)  # (n, k) with its block scales
+        for i in range(s0, ends[g]):
+            ref[r["row_index"][i]] += r["logit"][i] * (a[i].reshape(k) @ wg.T)
+    assert (np.abs(out - ref) <= bound + 1e-12).all()
