@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--config", default="prefill",
                     choices=["tiny", "decode", "skewed", "prefill", "int4", "mxa8w4", "fp8", "dispatch", "layer"])
     ap.add_argument("--combine", default="auto", choices=["auto", "atomic", "ordered"])
+    ap.add_argument("--quant", default="int8", choices=["int8", "fp8", "mx"],
+                    help="dispatch workload: x1 encoding of the producer step")
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--tile-m", type=int, default=0, choices=[0, 32, 64, 128, 256],
@@ -154,9 +156,10 @@ def dispatch_bytes(rp):
     map and writes x1 and pertokenScale; the step adds the router outputs read
     and rowIndex, logit and groupList written."""
     m = rp.T * rp.K
-    kern = rp.T * rp.k * 2 + m * 4 + m * rp.k + m * 4
+    sbytes = m * (rp.k // 32) if getattr(rp, "mode", "int8") == "mx" else m * 4  # pertokenScale written
+    kern = rp.T * rp.k * 2 + m * 4 + m * rp.k + sbytes
     step = (rp.T * rp.k * 2 + m * rp.expert_ids.itemsize + (0 if rp.topk_weights is None else m * 4)
-            + m * rp.k + m * 4 + (0 if rp.topk_weights is None else m * 4) + m * 8 + rp.e * 8)
+            + m * rp.k + sbytes + (0 if rp.topk_weights is None else m * 4) + m * 8 + rp.e * 8)
     return step, kern
 
 
@@ -170,13 +173,17 @@ def bench_dispatch(args):
     from quantized_moe_grouped_amd import workloads as W
 
     rp = W.make_route_config("dispatch", args.seed)
+    rp.mode = args.quant
     dev = "cuda"
     hidden = torch.from_numpy(rp.hidden.view(np.int16)).to(dev).view(torch.bfloat16)
     ids = torch.from_numpy(rp.expert_ids).to(dev)
     w = torch.from_numpy(rp.topk_weights).to(dev)
     m = rp.T * rp.K
-    x1 = torch.empty((m, rp.k), dtype=torch.int8, device=dev)
-    pts = torch.empty(m, dtype=torch.float32, device=dev)
+    x1 = torch.empty((m, rp.k), dtype=torch.int8 if rp.mode == "int8" else torch.float8_e4m3fn, device=dev)
+    if rp.mode == "mx":
+        pts = torch.empty((m, rp.k // 64, 2), dtype=torch.float8_e8m0fnu, device=dev)
+    else:
+        pts = torch.empty(m, dtype=torch.float32, device=dev)
     logit = torch.empty(m, dtype=torch.float32, device=dev)
     ri = torch.empty(m, dtype=torch.int64, device=dev)
     gl = torch.empty(rp.e, dtype=torch.int64, device=dev)
@@ -213,9 +220,10 @@ def bench_dispatch(args):
         "metric": "GB/s (and % of HBM roofline) of per-token int8 quantisation + routing permute at 1 GPU",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16->int8",
+        "dtype": {"int8": "bf16->int8", "fp8": "bf16->fp8", "mx": "bf16->fp8+e8m0"}[rp.mode],
         "data": "synthetic (seeded generator; bf16 hidden states, top-8 of 32 router choices with softmax weights)",
-        "config": {"workload": "dispatch", "tokens": rp.T, "k": rp.k, "top_k": rp.K, "e": rp.e, "m": m,
+        "config": {"workload": "dispatch" if rp.mode == "int8" else "dispatch-" + rp.mode, "tokens": rp.T,
+                   "k": rp.k, "top_k": rp.K, "e": rp.e, "m": m, "quant": rp.mode,
                    "ids": str(rp.expert_ids.dtype), "group_list_type": rp.group_list_type, "seed": args.seed,
                    "algorithmic_bytes_per_step": step_bytes,
                    "path_roofline_frac": round(gbs / PEAK_HBM_GBS, 4)},

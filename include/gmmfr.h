@@ -237,6 +237,15 @@ int gmm_finalize_routing_plan(const gmmfr_args* args, gmmfr_plan_info* info);
  *   logit = topk_weights[t][j], rowIndex = t;
  *   groupList[g] = rows of expert g (type 1) or their cumulative end (type 0).
  *
+ * FP8 x1 (readings; 448 is the largest E4M3 value, E4M3(v) rounds to nearest,
+ * ties to even):
+ *   with FLOAT32 pertokenScale: scale_t = fl(amax / 448), codes of
+ *     E4M3(clamp(fl(x * fl(448 / amax)), -448, 448));
+ *   with FLOAT8_E8M0 pertokenScale (the OCP MX conversion, per 32 values of a
+ *     token): shared exponent s = floor(log2(block amax)) - 8, clamped to
+ *     [-127, 127] (-127 for an all-zero block), E8M0 code s + 127, codes of
+ *     E4M3(clamp(x * 2^-s, -448, 448)).
+ *
  * Rows at and past sum(groupList counts) are not written (the grouped matmul
  * never reads them).  Hidden values must be finite; expert ids are device data
  * and are not validated beyond routing the out-of-range ones nowhere.
@@ -245,8 +254,10 @@ typedef struct {
   gmmfr_tensor hidden;         /* BFLOAT16 (T,k)                                required */
   gmmfr_tensor expert_ids;     /* INT32 or INT64 (T,K): global expert per slot  required */
   gmmfr_tensor topk_weights;   /* FLOAT32 (T,K) routing weights; given iff logit is given */
-  gmmfr_tensor x1;             /* out INT8 (T*K,k)                              required */
-  gmmfr_tensor pertoken_scale; /* out FLOAT32 (T*K)                             required */
+  gmmfr_tensor x1;             /* out INT8 (T*K,k), or FLOAT8_E4M3FN (T*K,k)    required */
+  gmmfr_tensor pertoken_scale; /* out FLOAT32 (T*K); with FP8 x1 FLOAT32 (T*K), or
+                                * FLOAT8_E8M0 (T*K, k/64, 2): one scale per 32
+                                * values (MX; k % 64 == 0)                     required */
   gmmfr_tensor logit;          /* out FLOAT32 (T*K); given iff topk_weights is given      */
   gmmfr_tensor row_index;      /* out INT64 or INT32 (T*K)                      required */
   gmmfr_tensor group_list;     /* out INT64 (e)                                 required */

@@ -254,16 +254,30 @@ def qp_workspace_size(args: QpArgs) -> int:
 
 
 def quant_permute(hidden, expert_ids, num_experts: int, *, topk_weights=None, expert_offset: int = 0,
-                  group_list_type: int = 1, row_index_dtype=None, workspace=None, stream=None) -> dict:
+                  group_list_type: int = 1, row_index_dtype=None, mode: str = "int8", workspace=None,
+                  stream=None) -> dict:
     """Allocate the outputs with torch and enqueue gmm_quant_permute on `stream`
-    (default: the current stream).  Returns the output tensors by name."""
+    (default: the current stream).  mode: "int8" (int8 x1, fp32 per-token
+    scale), "fp8" (FP8 E4M3 x1, fp32 per-token scale) or "mx" (FP8 E4M3 x1,
+    E8M0 scale per 32 values, (m, k/64, 2)).  Returns the output tensors by name."""
     import torch
     dev = hidden.device
     T, k = hidden.shape
     K = expert_ids.shape[1]
     m = T * K
-    out = dict(x1=torch.empty((m, k), dtype=torch.int8, device=dev),
-               pertoken_scale=torch.empty(m, dtype=torch.float32, device=dev),
+    if mode == "int8":
+        x1 = torch.empty((m, k), dtype=torch.int8, device=dev)
+        pts = torch.empty(m, dtype=torch.float32, device=dev)
+    elif mode == "fp8":
+        x1 = torch.empty((m, k), dtype=torch.float8_e4m3fn, device=dev)
+        pts = torch.empty(m, dtype=torch.float32, device=dev)
+    elif mode == "mx":
+        x1 = torch.empty((m, k), dtype=torch.float8_e4m3fn, device=dev)
+        pts = torch.empty((m, k // 64, 2), dtype=torch.float8_e8m0fnu, device=dev)
+    else:
+        raise ValueError(f"unknown mode {mode!r}")
+    out = dict(x1=x1,
+               pertoken_scale=pts,
                row_index=torch.empty(m, dtype=row_index_dtype or torch.int64, device=dev),
                group_list=torch.empty(num_experts, dtype=torch.int64, device=dev),
                logit=None if topk_weights is None else torch.empty(m, dtype=torch.float32, device=dev))

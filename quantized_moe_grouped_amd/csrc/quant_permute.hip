@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "../../include/gmmfr.h"
 
@@ -54,6 +55,11 @@ struct QpParams {
   int64_t T, k, nflat, offset;
   int32_t K, e, nchunks, ids_i32, ri_i32, glt;
 };
+
+// x1 encodings of the quantisation step
+constexpr int kQInt8 = 0;  // int8 per token, pertokenScale fp32 (m)
+constexpr int kQFp8 = 1;   // FP8 E4M3 per token, pertokenScale fp32 (m)
+constexpr int kQMx = 2;    // FP8 E4M3 with one E8M0 scale per 32 values, pertokenScale (m, k/64, 2)
 
 // Local expert of entry f, or -1 when its id lies outside [offset, offset+e)
 // (unsigned difference: no overflow for any id).
@@ -215,10 +221,31 @@ __device__ __forceinline__ uint32_t quant4(uint32_t lo2, uint32_t hi2, float inv
   return out;
 }
 
+// fp32 -> FP8 E4M3 code for |v| <= 448 (the caller saturates): round to
+// nearest, ties to even.  Normal range: keep 3 mantissa bits of the binary32
+// pattern, rounding the 20 dropped ones to nearest even (a carry moves into
+// the exponent), and rebias the exponent from 127 to 7; below 2^-6 the
+// subnormal grid of 2^-9.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t bits = __float_as_uint(v);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8; 8 is the smallest normal's code
+  } else {
+    const uint32_t ab = bits & 0x7FFFFFFFu;
+    const uint32_t r = ab + 0x7FFFFu + ((ab >> 20) & 1u);
+    code = (r >> 20) - ((127u - 7u) << 3);
+  }
+  return sign | code;
+}
+
 // One wave per token.  NI > 0: the row has at most NI*1024 values and stays in
 // registers between the amax pass and the quantisation; NI = 0: any k, the
-// second pass reads the row again (from cache).
-template <int NI>
+// second pass reads the row again (from cache).  QM: the x1 encoding.  For MX
+// the two lanes holding a 32-value block (16 values each) share its maximum.
+template <int NI, int QM>
 __global__ __launch_bounds__(kQpThreads) void quant_rows_kernel(QpParams q) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int kStep = 64 * kQuantCols;
@@ -251,16 +278,60 @@ __global__ __launch_bounds__(kQpThreads) void quant_rows_kernel(QpParams q) {
       for (int64_t c = (int64_t)lane * kQuantCols; c < q.k; c += kStep)
         fold(*(const uint4*)(row + c), *(const uint4*)(row + c + 8));
     }
+    float inv = 0.0f;
+    if constexpr (QM != kQMx) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, off));
-    const float amax = bf16f(mag);
-    const float scale = __fdiv_rn(amax, 127.0f);
-    const float inv = amax > 0.0f ? __fdiv_rn(127.0f, amax) : 0.0f;
-    if (dst >= 0) q.pts[dst] = scale;
+      for (int off = 32; off >= 1; off >>= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, off));
+      const float amax = bf16f(mag);
+      const float top = QM == kQInt8 ? 127.0f : 448.0f;  // the largest code magnitude
+      const float scale = __fdiv_rn(amax, top);
+      inv = amax > 0.0f ? __fdiv_rn(top, amax) : 0.0f;
+      if (dst >= 0) q.pts[dst] = scale;
+    }
     // x1 rows are written once and not read again here: nontemporal stores
     // (measured 16% faster for the whole step than plain stores)
     auto emit = [&](int64_t c, const uint4& u, const uint4& v) {
-      const u32x4 o = {quant4(u.x, u.y, inv), quant4(u.z, u.w, inv), quant4(v.x, v.y, inv), quant4(v.z, v.w, inv)};
+      u32x4 o;
+      if constexpr (QM == kQInt8) {
+        o = u32x4{quant4(u.x, u.y, inv), quant4(u.z, u.w, inv), quant4(v.x, v.y, inv), quant4(v.z, v.w, inv)};
+      } else {
+        // FP8 per token: codes of fl(x * inv), saturated to +-448.  MX: the
+        // block's shared exponent from its largest magnitude's bf16 exponent
+        // field E (floor(log2) - 8, clamped at -127: E8M0 code max(E - 8, 0)),
+        // codes of x * 2^(127 - code), saturated.
+        int shift = 0;
+        uint32_t bcode = 0;
+        if constexpr (QM == kQMx) {
+          uint32_t bm = 0;
+          const uint32_t wv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) bm = max(bm, max(wv[i] & 0x7FFFu, (wv[i] >> 16) & 0x7FFFu));
+          bm = max(bm, (uint32_t)__shfl_xor((int)bm, 1));
+          const uint32_t ex = bm >> 7;
+          bcode = ex >= 8 ? ex - 8 : 0;
+          shift = 127 - (int)bcode;
+        }
+        auto enc4 = [&](uint32_t lo2, uint32_t hi2) {
+          const float x[4] = {bf16f(lo2 & 0xFFFFu), bf16f(lo2 >> 16), bf16f(hi2 & 0xFFFFu), bf16f(hi2 >> 16)};
+          uint32_t w = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float t = QM == kQMx ? ldexpf(x[i], shift) : __fmul_rn(x[i], inv);
+            w |= e4m3_code(fminf(fmaxf(t, -448.0f), 448.0f)) << (8 * i);
+          }
+          return w;
+        };
+        o = u32x4{enc4(u.x, u.y), enc4(u.z, u.w), enc4(v.x, v.y), enc4(v.z, v.w)};
+        if constexpr (QM == kQMx) {
+          // the even lane of the pair writes the block's E8M0 code to each row
+          if ((lane & 1) == 0) {
+            for (int j = 0; j < q.K; ++j) {
+              const int32_t d = __builtin_amdgcn_readlane(dst, j);
+              if (d >= 0) ((uint8_t*)q.pts)[(int64_t)d * (q.k / 32) + c / 32] = (uint8_t)bcode;
+            }
+          }
+        }
+      }
       for (int j = 0; j < q.K; ++j) {
         const int32_t d = __builtin_amdgcn_readlane(dst, j);
         if (d >= 0) __builtin_nontemporal_store(o, (u32x4*)(q.x1 + (int64_t)d * q.k + c));
@@ -298,7 +369,7 @@ size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct QpPlan {
   int64_t T, k, nflat;
-  int32_t K, e, nchunks;
+  int32_t K, e, nchunks, qmode;
   size_t base_off, tot_off, pos_off, total;
 };
 
@@ -311,7 +382,13 @@ int qp_validate(const gmmqp_args* a, QpPlan* p) {
   if (a->hidden.dtype != GMMFR_DT_BFLOAT16) return GMMFR_ERR_DTYPE;
   if (a->expert_ids.dtype != GMMFR_DT_INT32 && a->expert_ids.dtype != GMMFR_DT_INT64) return GMMFR_ERR_DTYPE;
   if (given(a->topk_weights) && a->topk_weights.dtype != GMMFR_DT_FLOAT32) return GMMFR_ERR_DTYPE;
-  if (a->x1.dtype != GMMFR_DT_INT8 || a->pertoken_scale.dtype != GMMFR_DT_FLOAT32) return GMMFR_ERR_DTYPE;
+  // x1 INT8 with FLOAT32 per-token scales; FLOAT8_E4M3FN with FLOAT32 per-token
+  // scales, or with FLOAT8_E8M0 scales per 32 values (MX)
+  int qmode;
+  if (a->x1.dtype == GMMFR_DT_INT8 && a->pertoken_scale.dtype == GMMFR_DT_FLOAT32) qmode = kQInt8;
+  else if (a->x1.dtype == GMMFR_DT_FLOAT8_E4M3FN && a->pertoken_scale.dtype == GMMFR_DT_FLOAT32) qmode = kQFp8;
+  else if (a->x1.dtype == GMMFR_DT_FLOAT8_E4M3FN && a->pertoken_scale.dtype == GMMFR_DT_FLOAT8_E8M0) qmode = kQMx;
+  else return GMMFR_ERR_DTYPE;
   if (given(a->logit) && a->logit.dtype != GMMFR_DT_FLOAT32) return GMMFR_ERR_DTYPE;
   if (a->row_index.dtype != GMMFR_DT_INT32 && a->row_index.dtype != GMMFR_DT_INT64) return GMMFR_ERR_DTYPE;
   if (a->group_list.dtype != GMMFR_DT_INT64) return GMMFR_ERR_DTYPE;
@@ -328,8 +405,13 @@ int qp_validate(const gmmqp_args* a, QpPlan* p) {
   const int64_t e = a->group_list.dims[0];
   if (e < 1 || e > kMaxLocalExperts) return GMMFR_ERR_SHAPE;
   if (given(a->topk_weights) && !shape_is(a->topk_weights, 2, T, K)) return GMMFR_ERR_SHAPE;
-  if (!shape_is(a->x1, 2, m, k) || !shape_is(a->pertoken_scale, 1, m) || !shape_is(a->row_index, 1, m))
+  if (!shape_is(a->x1, 2, m, k) || !shape_is(a->row_index, 1, m)) return GMMFR_ERR_SHAPE;
+  if (qmode == kQMx) {
+    const gmmfr_tensor& t = a->pertoken_scale;  // (m, k/64, 2): one E8M0 per 32 values
+    if (k % 64 != 0 || t.ndim != 3 || t.dims[0] != m || t.dims[1] != k / 64 || t.dims[2] != 2) return GMMFR_ERR_SHAPE;
+  } else if (!shape_is(a->pertoken_scale, 1, m)) {
     return GMMFR_ERR_SHAPE;
+  }
   if (given(a->logit) && !shape_is(a->logit, 1, m)) return GMMFR_ERR_SHAPE;
   const gmmfr_tensor* all[] = {&a->hidden, &a->expert_ids, &a->topk_weights, &a->x1, &a->pertoken_scale,
                                &a->logit, &a->row_index, &a->group_list};
@@ -341,6 +423,7 @@ int qp_validate(const gmmqp_args* a, QpPlan* p) {
     p->K = (int32_t)K;
     p->e = (int32_t)e;
     p->nflat = m;
+    p->qmode = qmode;
     p->nchunks = (int32_t)((m + kRouteChunk - 1) / kRouteChunk);
     p->base_off = 0;
     p->tot_off = round256((size_t)e * p->nchunks * 4);
@@ -388,10 +471,16 @@ int qp_run(const gmmqp_args* a, void* workspace, size_t workspace_bytes, void* s
     const int64_t want = (p.T + kQpWaves - 1) / kQpWaves;
     const int qgrid = (int)(want < 65536 ? want : 65536);
     if (events && events[0] && hipEventRecord((hipEvent_t)events[0], s) != hipSuccess) return GMMFR_ERR_HIP;
-    if (p.k <= 1024) hipLaunchKernelGGL(quant_rows_kernel<1>, dim3(qgrid), dim3(kQpThreads), 0, s, q);
-    else if (p.k <= 2048) hipLaunchKernelGGL(quant_rows_kernel<2>, dim3(qgrid), dim3(kQpThreads), 0, s, q);
-    else if (p.k <= 4096) hipLaunchKernelGGL(quant_rows_kernel<4>, dim3(qgrid), dim3(kQpThreads), 0, s, q);
-    else hipLaunchKernelGGL(quant_rows_kernel<0>, dim3(qgrid), dim3(kQpThreads), 0, s, q);
+    auto launch = [&](auto qm_) {
+      constexpr int QM = decltype(qm_)::value;
+      if (p.k <= 1024) hipLaunchKernelGGL((quant_rows_kernel<1, QM>), dim3(qgrid), dim3(kQpThreads), 0, s, q);
+      else if (p.k <= 2048) hipLaunchKernelGGL((quant_rows_kernel<2, QM>), dim3(qgrid), dim3(kQpThreads), 0, s, q);
+      else if (p.k <= 4096) hipLaunchKernelGGL((quant_rows_kernel<4, QM>), dim3(qgrid), dim3(kQpThreads), 0, s, q);
+      else hipLaunchKernelGGL((quant_rows_kernel<0, QM>), dim3(qgrid), dim3(kQpThreads), 0, s, q);
+    };
+    if (p.qmode == kQMx) launch(std::integral_constant<int, kQMx>{});
+    else if (p.qmode == kQFp8) launch(std::integral_constant<int, kQFp8>{});
+    else launch(std::integral_constant<int, kQInt8>{});
     if (events && events[1] && hipEventRecord((hipEvent_t)events[1], s) != hipSuccess) return GMMFR_ERR_HIP;
   }
   return hipGetLastError() == hipSuccess ? GMMFR_OK : GMMFR_ERR_HIP;

@@ -364,7 +364,13 @@ QP_CASES = [
     ("no_hidden", dict(hidden=B.Tensor()), B.ERR_NULLPTR),
     ("hidden_f32", dict(hidden=_fake(B.DT_FLOAT32, 512, 2048)), B.ERR_DTYPE),
     ("ids_f32", dict(expert_ids=_fake(B.DT_FLOAT32, 512, 8)), B.ERR_DTYPE),
-    ("x1_fp8", dict(x1=_fake(B.DT_FLOAT8_E4M3FN, 4096, 2048)), B.ERR_DTYPE),
+    ("x1_fp8_per_token", dict(x1=_fake(B.DT_FLOAT8_E4M3FN, 4096, 2048)), B.OK),
+    ("x1_fp8_mx", dict(x1=_fake(B.DT_FLOAT8_E4M3FN, 4096, 2048),
+                       pertoken_scale=_fake(B.DT_FLOAT8_E8M0, 4096, 32, 2)), B.OK),
+    ("x1_fp8_mx_scale_shape", dict(x1=_fake(B.DT_FLOAT8_E4M3FN, 4096, 2048),
+                                   pertoken_scale=_fake(B.DT_FLOAT8_E8M0, 4096, 64)), B.ERR_SHAPE),
+    ("x1_int8_e8m0_scale", dict(pertoken_scale=_fake(B.DT_FLOAT8_E8M0, 4096, 32, 2)), B.ERR_DTYPE),
+    ("x1_fp4", dict(x1=_fake(B.DT_FLOAT4_E2M1X2, 4096, 1024)), B.ERR_DTYPE),
     ("group_list_i32", dict(group_list=_fake(B.DT_INT32, 32)), B.ERR_DTYPE),
     ("group_list_type", dict(group_list_type=2), B.ERR_ATTR),
     ("k_not_mult_16", dict(hidden=_fake(B.DT_BFLOAT16, 512, 2040), x1=_fake(B.DT_INT8, 4096, 2040)), B.ERR_SHAPE),

@@ -31,22 +31,34 @@ CASES = {
 }
 
 
+def _host(v):
+    if v is None:
+        return None
+    if v.dtype in (torch.float8_e4m3fn, torch.float8_e8m0fnu):
+        v = v.view(torch.uint8)
+    return v.cpu().numpy()
+
+
 def _run_gpu(rp, ri_dtype=torch.int64):
     dev = torch.device("cuda:0")
     hidden = torch.from_numpy(rp.hidden.view(np.int16)).to(dev).view(torch.bfloat16)
     ids = torch.from_numpy(np.ascontiguousarray(rp.expert_ids)).to(dev)
     w = None if rp.topk_weights is None else torch.from_numpy(rp.topk_weights).to(dev)
     out = B.quant_permute(hidden, ids, rp.e, topk_weights=w, expert_offset=rp.expert_offset,
-                          group_list_type=rp.group_list_type, row_index_dtype=ri_dtype)
+                          group_list_type=rp.group_list_type, row_index_dtype=ri_dtype, mode=rp.mode)
     torch.cuda.synchronize()
-    return {k: (None if v is None else v.cpu().numpy()) for k, v in out.items() if k != "workspace"}
+    return {k: _host(v) for k, v in out.items() if k != "workspace"}
 
 
 def _compare(rp, got, ref):
     rows = ref["rows"]
     assert (got["group_list"] == ref["group_list"]).all()
     assert (got["x1"][:rows] == ref["x1"][:rows]).all()
-    assert np.array_equal(got["pertoken_scale"][:rows].view(np.uint32), ref["pertoken_scale"][:rows].view(np.uint32))
+    if rp.mode == "mx":
+        assert (got["pertoken_scale"].reshape(len(got["pertoken_scale"]), -1)[:rows] == ref["pertoken_scale"][:rows]).all()
+    else:
+        assert np.array_equal(got["pertoken_scale"][:rows].view(np.uint32),
+                              ref["pertoken_scale"][:rows].view(np.uint32))
     assert (got["row_index"][:rows].astype(np.int64) == ref["row_index"][:rows]).all()
     if ref["logit"] is not None:
         assert np.array_equal(got["logit"][:rows].view(np.uint32), ref["logit"][:rows].view(np.uint32))
@@ -101,3 +113,56 @@ def test_composition_with_the_grouped_matmul():
                            logit=qp["logit"], row_index=qp["row_index"], group_list_type=1, deterministic=True)
     torch.cuda.synchronize()
     G.assert_bitexact(out.cpu().numpy(), want)
+
+
+# ---------------------------------------------------------------- FP8 outputs
+
+FP8_CASES = ["small", "ep_offset_i32", "zero_tokens_repeats", "single", "many_chunks", "k_4096", "k_8208_reread"]
+
+
+@pytest.mark.parametrize("mode", ["fp8", "mx"])
+@pytest.mark.parametrize("name", FP8_CASES, ids=FP8_CASES)
+def test_quant_permute_fp8_bitexact(name, mode):
+    kw = dict(CASES[name])
+    if mode == "mx" and kw["k"] % 64:
+        kw["k"] = kw["k"] // 64 * 64 + 64
+    rp = W.route_problem(**kw)
+    rp.mode = mode
+    _compare(rp, _run_gpu(rp), Q.run(rp))
+
+
+@pytest.mark.parametrize("mode", ["fp8", "mx"])
+def test_dispatch_workload_fp8_bitexact(mode):
+    rp = W.make_route_config("dispatch", 0)
+    rp.mode = mode
+    _compare(rp, _run_gpu(rp), Q.run(rp))
+
+
+def test_mx_producer_feeds_the_mx_matmul():
+    """MX producer on the device feeding the MxA8W4 grouped matmul on the
+    device: within the MxA8W4 oracle's bound of the oracles chained."""
+    import dataclasses
+    from oracle import mx as MX
+    T, k, n, K, e = 200, 256, 288, 4, 5
+    rp = W.route_problem(34, T, k, K, e, group_list_type=0)
+    rp.mode = "mx"
+    r = Q.run(rp)
+    m = T * K
+    base = W.mx_problem(35, m, k, n, e, output_bs=T)
+    p = dataclasses.replace(base, x1=r["x1"], pertoken_scale=r["pertoken_scale"].reshape(m, k // 64, 2),
+                            logit=r["logit"], group_list=r["group_list"], group_list_type=0,
+                            row_index=r["row_index"], shared_input=None,
+                            counts=np.diff(np.r_[0, r["group_list"]]))
+    ref, bound, _ = MX.run(p)
+    dev = torch.device("cuda:0")
+    hidden = torch.from_numpy(rp.hidden.view(np.int16)).to(dev).view(torch.bfloat16)
+    qp = B.quant_permute(hidden, torch.from_numpy(rp.expert_ids).to(dev), e,
+                         topk_weights=torch.from_numpy(rp.topk_weights).to(dev), group_list_type=0, mode="mx")
+    d = G.to_device(p)
+    out = torch.empty((T, n), dtype=torch.float32, device=dev)
+    B.gmm_finalize_routing(qp["x1"], d["x2"], qp["group_list"], out, scale=d["scale"],
+                           pertoken_scale=qp["pertoken_scale"], logit=qp["logit"], row_index=qp["row_index"],
+                           group_list_type=0, deterministic=True, transpose_x2=True)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert (np.abs(got - ref) <= bound).all()
