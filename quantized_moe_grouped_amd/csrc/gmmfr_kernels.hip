@@ -1176,14 +1176,22 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   constexpr int B_BYTES = BN * B_COLB;
   constexpr int A_INSTR = A_BYTES / 16 / kThreads, B_INSTR = B_BYTES / 16 / kThreads;
   static_assert(A_INSTR == 2 && B_INSTR == (B8 ? 4 : 2) && BN == kThreads && BM == kThreads / 2, "copy split");
-  // copies per thread and stage: A, B and (MX) one B-scale dword; waves 0-1 add an A-scale dword
-  constexpr int LOADS_LO = A_INSTR + B_INSTR + (B8 ? 0 : 2), LOADS_HI = A_INSTR + B_INSTR + (B8 ? 0 : 1);
-  constexpr int SC_STAGES = B8 ? 1 : STAGES;  // block-scale staging (MX only)
+  // Copies per thread and k-slice: A and B.  MX: a scale dword holds the
+  // block scales of two k-slices, so even slices add one B-scale dword copy
+  // per thread (waves 0-1 also an A-scale dword) into a ring of SC_SLOTS slots
+  // of its own, indexed by the running count of slices.  A wait for a slice
+  // allows the fewest copies its STAGES-2 younger slices can have issued.
+  constexpr int LOADS_AB = A_INSTR + B_INSTR;
+  constexpr int SC_LO = B8 ? 0 : 2, SC_HI = B8 ? 0 : 1;
+  constexpr int LOADS_LO = (STAGES - 2) * LOADS_AB + (STAGES - 2) / 2 * SC_LO;
+  constexpr int LOADS_HI = (STAGES - 2) * LOADS_AB + (STAGES - 2) / 2 * SC_HI;
+  constexpr int SC_SLOTS = B8 ? 1 : 4;
+  static_assert(B8 || STAGES <= 5, "a scale slot is refilled only after its two k-slices are read");
 
   __shared__ __attribute__((aligned(16))) int8_t sA[STAGES * A_BYTES];
   __shared__ __attribute__((aligned(16))) int8_t sB[STAGES * B_BYTES];
-  __shared__ __attribute__((aligned(16))) uint32_t sSA[SC_STAGES][BM];  // the scale dword of each row
-  __shared__ __attribute__((aligned(16))) uint32_t sSB[SC_STAGES][BN];  // and of each column
+  __shared__ __attribute__((aligned(16))) uint32_t sSA[SC_SLOTS][BM];  // the scale dword of each row
+  __shared__ __attribute__((aligned(16))) uint32_t sSB[SC_SLOTS][BN];  // and of each column
   // per-row logit and (FP8) pertokenScale of a tile for its epilogue, as raw
   // words copied by the DMA path, double-buffered across consecutive tiles
   __shared__ __attribute__((aligned(16))) float s_lg[2][BM];
@@ -1271,7 +1279,9 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
     sb_base = (const uint32_t*)uniform64((int64_t)(sb_words + ((int64_t)c.g * n + c.col0) * kdw));
     sb_off = (uint32_t)((min(c.col0 + tid, n - 1) - c.col0) * kdw * 4);
   };
-  auto issue_stage = [&](int st, int kt) {
+  // copies of k-slice kt (tile-local) into stage st; gs: the slice's running
+  // count (its scale dword goes to slot gs/2 of the ring)
+  auto issue_stage = [&](int st, int kt, int gs) {
 #pragma unroll
     for (int q = 0; q < A_INSTR; ++q)
       lds_dma16_sv(a_base + (int64_t)kt * BK, a_off[q],
@@ -1281,10 +1291,12 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       lds_dma16_sv(b_base + (int64_t)kt * (BKN ? (int64_t)BK * n : (int64_t)B_COLB), b_off[q],
                    __builtin_amdgcn_readfirstlane(lds_addr(sB + st * B_BYTES + (q * 4 + wave) * 64 * 16)));
     if constexpr (!B8) {
-      // the dword holding the two block scales of k-step kt (and of its neighbour)
-      lds_dma4_sv(sb_base + kt / 2, sb_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSB[st][wave * 64])));
-      if (lo_wave)
-        lds_dma4_sv(sa_base + kt / 2, sa_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSA[st][wave * 64])));
+      if ((kt & 1) == 0) {  // the dword holding the block scales of slices kt and kt + 1
+        const int slot = (gs >> 1) % SC_SLOTS;
+        lds_dma4_sv(sb_base + kt / 2, sb_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSB[slot][wave * 64])));
+        if (lo_wave)
+          lds_dma4_sv(sa_base + kt / 2, sa_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSA[slot][wave * 64])));
+      }
     }
   };
 
@@ -1329,7 +1341,8 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   };
 
   // one k-step on stage st (tile-local k-step kt): fragment reads, 8 MFMAs
-  auto compute = [&](int st, int kt, v16f (&acc)[FM][FN]) {
+  auto compute = [&](int st, int kt, int gs, v16f (&acc)[FM][FN]) {
+    const int slot = B8 ? 0 : (gs >> 1) % SC_SLOTS;
     const int8_t* a_st = sA + st * A_BYTES;
     const int8_t* b_st = sB + st * B_BYTES;
     const int sel = 8 * (2 * (kt & 1) + h);  // byte of this lane's block in the scale dword
@@ -1341,7 +1354,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       const v4i lo = *(const LDS_PTR(v4i))(a_st + r * BK + ((h ^ swz_a<BK>(r)) << 4));
       const v4i hi = *(const LDS_PTR(v4i))(a_st + r * BK + (((2 + h) ^ swz_a<BK>(r)) << 4));
       af[i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      sa[i] = B8 ? 127 : (int)(sSA[B8 ? 0 : st][r] >> sel);
+      sa[i] = B8 ? 127 : (int)(sSA[slot][r] >> sel);
     }
     v8i bf[FN];
 #pragma unroll
@@ -1370,7 +1383,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       } else {
         const v4i w = *(const LDS_PTR(v4i))(b_st + cl * B_COLB + h * 16);
         bf[jj] = v8i{w.x, w.y, w.z, w.w, 0, 0, 0, 0};
-        sb[jj] = (int)(sSB[st][cl] >> sel);
+        sb[jj] = (int)(sSB[slot][cl] >> sel);
       }
     }
 #pragma unroll
@@ -1473,15 +1486,16 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       dma_rows(cur, pb);
       set_sources(cur);
 #pragma unroll
-      for (int st = 0; st < STAGES - 1; ++st) issue_stage(st, st);
+      for (int st = 0; st < STAGES - 1; ++st) issue_stage(st, st, st);
+      int gfill = STAGES - 1, gstep = 0;  // running counts of slices issued and consumed
       int stage = 0;
       bool prev_full = false;
       // After an ordered full-tile epilogue, its FM*FN*16 stores (issued
       // after the next tile's first slices) may stay in flight while stage 0
       // is awaited; after any other epilogue the plain wait also drains them.
       constexpr int FULL_STORES = FM * FN * 16;
-      constexpr int W0_LO = (STAGES - 2) * LOADS_LO + FULL_STORES < 63 ? (STAGES - 2) * LOADS_LO + FULL_STORES : 63;
-      constexpr int W0_HI = (STAGES - 2) * LOADS_HI + FULL_STORES < 63 ? (STAGES - 2) * LOADS_HI + FULL_STORES : 63;
+      constexpr int W0_LO = LOADS_LO + FULL_STORES < 63 ? LOADS_LO + FULL_STORES : 63;
+      constexpr int W0_HI = LOADS_HI + FULL_STORES < 63 ? LOADS_HI + FULL_STORES : 63;
       while (true) {
         raise_priority(j);
         v16f acc[FM][FN];
@@ -1496,8 +1510,8 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
             if (lo_wave) wait_vmcnt<W0_LO>();
             else wait_vmcnt<W0_HI>();
           } else {
-            if (lo_wave) wait_vmcnt<(STAGES - 2) * LOADS_LO>();
-            else wait_vmcnt<(STAGES - 2) * LOADS_HI>();
+            if (lo_wave) wait_vmcnt<LOADS_LO>();
+            else wait_vmcnt<LOADS_HI>();
           }
           lds_barrier();
           const int fill = kt + STAGES - 1;
@@ -1505,8 +1519,10 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
             set_sources(nxt);
             if (t_nxt >= 0) dma_rows(nxt, pb ^ 1);
           }
-          issue_stage(stage == 0 ? STAGES - 1 : stage - 1, fill < ktiles ? fill : fill - ktiles);
-          compute(stage, kt, acc);
+          issue_stage(stage == 0 ? STAGES - 1 : stage - 1, fill < ktiles ? fill : fill - ktiles, gfill);
+          ++gfill;
+          compute(stage, kt, gstep, acc);
+          ++gstep;
           stage = stage + 1 == STAGES ? 0 : stage + 1;
         }
         __builtin_amdgcn_s_setprio(0);
@@ -1532,7 +1548,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       set_sources(c);
 #pragma unroll
       for (int st = 0; st < STAGES - 1; ++st)
-        if (st < ktiles) issue_stage(st, st);
+        if (st < ktiles) issue_stage(st, st, st);
       v16f acc[FM][FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -1542,14 +1558,14 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       for (int kt = 0; kt < ktiles; ++kt) {
         // stage kt complete; the stages issued after it may still be in flight
         if (kt + STAGES - 2 < ktiles) {
-          if (lo_wave) wait_vmcnt<(STAGES - 2) * LOADS_LO>();
-          else wait_vmcnt<(STAGES - 2) * LOADS_HI>();
+          if (lo_wave) wait_vmcnt<LOADS_LO>();
+          else wait_vmcnt<LOADS_HI>();
         } else {
           wait_vmcnt<0>();
         }
         lds_barrier();
-        if (kt + STAGES - 1 < ktiles) issue_stage((kt + STAGES - 1) % STAGES, kt + STAGES - 1);
-        compute(kt % STAGES, kt, acc);
+        if (kt + STAGES - 1 < ktiles) issue_stage((kt + STAGES - 1) % STAGES, kt + STAGES - 1, kt + STAGES - 1);
+        compute(kt % STAGES, kt, kt, acc);
       }
       __builtin_amdgcn_s_setprio(0);
       epilogue(c, 0, acc);
