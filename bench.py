@@ -451,10 +451,10 @@ def main():
     if not args.no_cpu_baseline:
         rows = args.cpu_sample_rows
         if not rows:
-            # size the sample for about 15 s of oracle time from a short calibration run
+            # size the sample for about 20 s of oracle time from a short calibration run
             cal = cpu_baseline(p, min(p.covered_rows, 256))
             rate_rows = min(p.covered_rows, 256) / max(cal["seconds"], 1e-3)
-            rows = int(max(256, min(p.covered_rows, 15.0 * rate_rows)))
+            rows = int(max(256, min(p.covered_rows, 20.0 * rate_rows)))
         print(f"[bench] cpu oracle on a {rows}-row sample", file=sys.stderr, flush=True)
         cb = cpu_baseline(p, rows)
         cb.pop("seconds")
