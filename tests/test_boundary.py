@@ -390,3 +390,25 @@ def test_quant_permute_stage_one(name, over, code):
     assert st == code, (B.STATUS_NAMES.get(st), B.STATUS_NAMES.get(code))
     if code != B.OK:
         assert ws == 12345
+
+
+# ---------------------------------------------------------------- no fallback, bench contract
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    """The product path has no CPU fallback: without the built library every
+    entry point raises."""
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libgmmfr.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        B.workspace_size(_args())
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 exits with a message."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
