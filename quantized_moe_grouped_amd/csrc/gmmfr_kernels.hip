@@ -1187,11 +1187,19 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   constexpr int LOADS_HI = (STAGES - 2) * LOADS_AB + (STAGES - 2) / 2 * SC_HI;
   constexpr int SC_SLOTS = B8 ? 1 : 4;
   static_assert(B8 || STAGES <= 5, "a scale slot is refilled only after its two k-slices are read");
+  // When k is a multiple of 512 (a whole number of 8-slice groups), the four
+  // scale dwords of 8 slices are copied at once, 16 bytes per row and per
+  // column, with the group's first slice, into 2 slots of [row][4 dwords]; a
+  // slot is refilled 6 slices after the group that used it ends.  Waits then
+  // allow no scale copy among the younger slices.
+  constexpr int G8_SLOTS = 2;
+  constexpr int SC_WORDS = B8 ? 1 : (G8_SLOTS * 4 > SC_SLOTS ? G8_SLOTS * 4 : SC_SLOTS);
+  constexpr int LOADS_G8 = (STAGES - 2) * LOADS_AB;
 
   __shared__ __attribute__((aligned(16))) int8_t sA[STAGES * A_BYTES];
   __shared__ __attribute__((aligned(16))) int8_t sB[STAGES * B_BYTES];
-  __shared__ __attribute__((aligned(16))) uint32_t sSA[SC_SLOTS][BM];  // the scale dword of each row
-  __shared__ __attribute__((aligned(16))) uint32_t sSB[SC_SLOTS][BN];  // and of each column
+  __shared__ __attribute__((aligned(16))) uint32_t sSA[SC_WORDS][BM];  // the scale dwords of each row
+  __shared__ __attribute__((aligned(16))) uint32_t sSB[SC_WORDS][BN];  // and of each column
   // per-row logit and (FP8) pertokenScale of a tile for its epilogue, as raw
   // words copied by the DMA path, double-buffered across consecutive tiles
   __shared__ __attribute__((aligned(16))) float s_lg[2][BM];
@@ -1225,6 +1233,8 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int64_t k = p.k, n = p.n;
   const int ktiles = (int)(k / BK);
+  const bool grp8 = !B8 && k % 512 == 0 && ktiles >= STAGES;  // (always the continuous pipeline)
+  static_assert(B8 || STAGES <= 9, "a group's slot is refilled only after the group two before it is read");
   const int64_t kdw = k / 128;         // MX: scale dwords per row or column (k % 128 == 0)
   const bool lo_wave = wave < 2;       // waves that copy the A-scale dwords (rows 0..127)
   const uint32_t* sa_words = (const uint32_t*)p.pertoken;
@@ -1291,7 +1301,16 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       lds_dma16_sv(b_base + (int64_t)kt * (BKN ? (int64_t)BK * n : (int64_t)B_COLB), b_off[q],
                    __builtin_amdgcn_readfirstlane(lds_addr(sB + st * B_BYTES + (q * 4 + wave) * 64 * 16)));
     if constexpr (!B8) {
-      if ((kt & 1) == 0) {  // the dword holding the block scales of slices kt and kt + 1
+      if (grp8) {
+        if ((kt & 7) == 0) {  // the four dwords of slices kt .. kt + 7, [row][4 dwords]
+          const int slot = (gs >> 3) % G8_SLOTS;
+          lds_dma16_sv(sb_base + kt / 2, sb_off,
+                       __builtin_amdgcn_readfirstlane(lds_addr(&sSB[0][0] + (slot * BN + wave * 64) * 4)));
+          if (lo_wave)
+            lds_dma16_sv(sa_base + kt / 2, sa_off,
+                         __builtin_amdgcn_readfirstlane(lds_addr(&sSA[0][0] + (slot * BM + wave * 64) * 4)));
+        }
+      } else if ((kt & 1) == 0) {  // the dword holding the block scales of slices kt and kt + 1
         const int slot = (gs >> 1) % SC_SLOTS;
         lds_dma4_sv(sb_base + kt / 2, sb_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSB[slot][wave * 64])));
         if (lo_wave)
@@ -1342,7 +1361,14 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
 
   // one k-step on stage st (tile-local k-step kt): fragment reads, 8 MFMAs
   auto compute = [&](int st, int kt, int gs, v16f (&acc)[FM][FN]) {
-    const int slot = B8 ? 0 : (gs >> 1) % SC_SLOTS;
+    // scale dword of row or column q: ring slot of this slice's pair, or (8-slice
+    // groups) word (kt/2)%4 of the group's slot
+    const uint32_t* sca = &sSA[0][0];
+    const uint32_t* scb = &sSB[0][0];
+    auto sc_word = [&](const uint32_t* base, int rows, int q) -> uint32_t {
+      if (grp8) return base[(((gs >> 3) % G8_SLOTS) * rows + q) * 4 + ((kt >> 1) & 3)];
+      return base[((gs >> 1) % SC_SLOTS) * rows + q];
+    };
     const int8_t* a_st = sA + st * A_BYTES;
     const int8_t* b_st = sB + st * B_BYTES;
     const int sel = 8 * (2 * (kt & 1) + h);  // byte of this lane's block in the scale dword
@@ -1354,7 +1380,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       const v4i lo = *(const LDS_PTR(v4i))(a_st + r * BK + ((h ^ swz_a<BK>(r)) << 4));
       const v4i hi = *(const LDS_PTR(v4i))(a_st + r * BK + (((2 + h) ^ swz_a<BK>(r)) << 4));
       af[i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      sa[i] = B8 ? 127 : (int)(sSA[slot][r] >> sel);
+      sa[i] = B8 ? 127 : (int)(sc_word(sca, BM, r) >> sel);
     }
     v8i bf[FN];
 #pragma unroll
@@ -1383,7 +1409,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       } else {
         const v4i w = *(const LDS_PTR(v4i))(b_st + cl * B_COLB + h * 16);
         bf[jj] = v8i{w.x, w.y, w.z, w.w, 0, 0, 0, 0};
-        sb[jj] = (int)(sSB[slot][cl] >> sel);
+        sb[jj] = (int)(sc_word(scb, BN, cl) >> sel);
       }
     }
 #pragma unroll
@@ -1496,6 +1522,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       constexpr int FULL_STORES = FM * FN * 16;
       constexpr int W0_LO = LOADS_LO + FULL_STORES < 63 ? LOADS_LO + FULL_STORES : 63;
       constexpr int W0_HI = LOADS_HI + FULL_STORES < 63 ? LOADS_HI + FULL_STORES : 63;
+      constexpr int W0_G8 = LOADS_G8 + FULL_STORES < 63 ? LOADS_G8 + FULL_STORES : 63;
       while (true) {
         raise_priority(j);
         v16f acc[FM][FN];
@@ -1507,8 +1534,11 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
         for (int kt = 0; kt < ktiles; ++kt) {
           // this k-step's slice has landed; the STAGES-2 younger ones may still be in flight
           if (kt == 0 && prev_full) {
-            if (lo_wave) wait_vmcnt<W0_LO>();
+            if (grp8) wait_vmcnt<W0_G8>();
+            else if (lo_wave) wait_vmcnt<W0_LO>();
             else wait_vmcnt<W0_HI>();
+          } else if (grp8) {
+            wait_vmcnt<LOADS_G8>();
           } else {
             if (lo_wave) wait_vmcnt<LOADS_LO>();
             else wait_vmcnt<LOADS_HI>();
