@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--transpose-x2", action="store_true",
                     help="int8 or FP8 weights given transposed, (e,n,k) (the operator's transposed-x2 form)")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="rows in the oracle sample (0 = auto)")
+    ap.add_argument("--timing-detail", action="store_true",
+                    help="after the timed steps, add a 'timing' object: per-call median/min/p90 with warm caches "
+                         "and with 1 GiB written before each call (L2 and MALL evicted), and both combine modes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (torch copy_) 5 times: the reference kernel whose "
                          "FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic figures")
@@ -82,6 +85,45 @@ class Hip:
         ms = ctypes.c_float()
         assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
         return float(ms.value)
+
+
+def _stats(ms):
+    t = sorted(ms)
+    return {"median": round(t[len(t) // 2], 5), "min": round(t[0], 5), "p90": round(t[int(0.9 * (len(t) - 1))], 5),
+            "calls": len(t)}
+
+
+def timing_detail(p, d, args, stream, hip, chosen, calls=20):
+    """Whole-call times from events around each call: warm (back to back) and
+    cold (a 1 GiB buffer written before each call, which evicts the L2s and
+    the 256 MB MALL), for the combine mode the library chose and the other."""
+    import torch
+    from quantized_moe_grouped_amd import binding as B
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    out = {}
+    for mode in ("atomic", "ordered"):
+        cargs, keep = B.make_args(d["x1"], d["x2"], d["gl"], d["out"], scale=d["scale"], pertoken_scale=d["pts"],
+                                  logit=d["logit"], row_index=d["ri"], shared_input=d["shared"],
+                                  shared_input_offset=p.shared_input_offset, group_list_type=p.group_list_type,
+                                  combine=mode, transpose_x2=p.x2_transposed)
+        ws = torch.empty(max(B.workspace_size(cargs), 1), dtype=torch.uint8, device="cuda")
+        for _ in range(args.warmup):
+            B.run(cargs, ws, stream)
+        res = {}
+        for kind in ("warm", "cold"):
+            evs = [(hip.event(), hip.event()) for _ in range(calls)]
+            for i, (a, b) in enumerate(evs):
+                if kind == "cold":
+                    flush.fill_(float(i))
+                hip.record(a, stream)
+                B.run(cargs, ws, stream)
+                hip.record(b, stream)
+            torch.cuda.synchronize()
+            res[kind + "_ms"] = _stats([hip.elapsed_ms(a, b) for a, b in evs])
+        out[mode] = res
+        del ws, keep
+    out["chosen"] = chosen
+    return out
 
 
 def algorithmic_bytes(p):
@@ -458,6 +500,9 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if args.timing_detail:
+        res["timing"] = timing_detail(p, dict(x1=x1, x2=x2, gl=gl, out=out, scale=scale, pts=pts, logit=logit, ri=ri,
+                                              shared=shared), args, stream, hip, plan["combine"])
     if not args.no_cpu_baseline:
         rows = args.cpu_sample_rows
         if not rows:
