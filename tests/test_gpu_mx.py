@@ -25,6 +25,7 @@ CASES = {
     # k a multiple of 512: block scales copied 8 k-slices at a time
     "k_512_one_scale_group": dict(seed=7, m=1000, k=512, n=512, e=4, output_bs=500),
     "k_1536_many_tiles": dict(seed=8, m=2000, k=1536, n=768, e=3, output_bs=700, bsdp=30, shared_offset=5),
+    "k_512_many_empty": dict(seed=10, m=900, k=512, n=256, e=40, empty_frac=0.7, output_bs=300),
     # one group past 512 plus 128: the dword-per-pair path
     "k_640_dword_path": dict(seed=9, m=600, k=640, n=288, e=3, output_bs=300),
 }
