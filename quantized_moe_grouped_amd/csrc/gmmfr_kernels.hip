@@ -1671,47 +1671,74 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(KParams p, int32_t* coun
 }
 
 // Single workgroup of 1024 threads: exclusive scan of counts into offsets
-// (output_bs + 1 entries) and cursor := offsets.  Chunks of kScanChunk counts
-// are staged in LDS with coalesced loads, each thread scans a contiguous run
-// of the chunk, the 1024 run totals are scanned across the block, and the
-// chunk goes back out coalesced.
-constexpr int kScanChunk = 32768;  // 128 KiB of LDS
+// (nbins + 1 entries) and cursor := offsets, in chunks of 16384 counts.  Each
+// thread takes 16 consecutive counts (four 16-byte loads when whole), scans
+// them in registers, a shuffle scan over the wave and one LDS pass over the 16
+// wave totals give its starting offset, and its 16 results go out as four
+// 16-byte stores to each output.  (Sections of the workspace are 256-byte
+// aligned and chunks start at multiples of 16 counts.)
+constexpr int kScanPer = 16, kScanChunk = 1024 * kScanPer;
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* counts, int32_t* offsets, int32_t* cursor, int64_t nbins) {
-  __shared__ int32_t s_buf[kScanChunk];
-  __shared__ int32_t s[1024];
-  const int tid = threadIdx.x;
+  __shared__ int32_t s_wave[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int32_t carry = 0;
   for (int64_t base = 0; base < nbins; base += kScanChunk) {
-    const int len = (int)min((int64_t)kScanChunk, nbins - base);
-#pragma unroll 8
-    for (int i = tid; i < len; i += 1024) s_buf[i] = counts[base + i];
-    __syncthreads();
-    const int per = (len + 1023) / 1024;
-    const int b0 = min(tid * per, len), b1 = min(b0 + per, len);
-    int32_t local = 0;
-    for (int b = b0; b < b1; ++b) local += s_buf[b];
-    s[tid] = local;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int32_t t = tid >= off ? s[tid - off] : 0;
-      __syncthreads();
-      s[tid] += t;
-      __syncthreads();
+    const int64_t b0 = base + (int64_t)tid * kScanPer;
+    const bool whole = b0 + kScanPer <= nbins;
+    int32_t v[kScanPer];
+    if (whole) {
+#pragma unroll
+      for (int q = 0; q < kScanPer / 4; ++q) {
+        const int4 x = ((const int4*)(counts + b0))[q];
+        v[4 * q] = x.x;
+        v[4 * q + 1] = x.y;
+        v[4 * q + 2] = x.z;
+        v[4 * q + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kScanPer; ++i) v[i] = b0 + i < nbins ? counts[b0 + i] : 0;
     }
-    int32_t run = carry + (tid > 0 ? s[tid - 1] : 0);
-    for (int b = b0; b < b1; ++b) {
-      const int32_t c = s_buf[b];
-      s_buf[b] = run;
-      run += c;
+    int32_t local = 0;  // exclusive scan within the thread
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+      const int32_t c = v[i];
+      v[i] = local;
+      local += c;
     }
-    const int32_t total = s[1023];
+    int32_t incl = local;  // inclusive scan of the thread totals over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    if (lane == 63) s_wave[wv] = incl;
     __syncthreads();
-    for (int i = tid; i < len; i += 1024) {
-      offsets[base + i] = s_buf[i];
-      cursor[base + i] = s_buf[i];
+    int32_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int32_t t = s_wave[w];
+      before += w < wv ? t : 0;
+      total += t;
+    }
+    const int32_t start = carry + before + incl - local;
+    if (whole) {
+#pragma unroll
+      for (int q = 0; q < kScanPer / 4; ++q) {
+        const int4 x = make_int4(start + v[4 * q], start + v[4 * q + 1], start + v[4 * q + 2], start + v[4 * q + 3]);
+        ((int4*)(offsets + b0))[q] = x;
+        ((int4*)(cursor + b0))[q] = x;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kScanPer; ++i)
+        if (b0 + i < nbins) {
+          offsets[b0 + i] = start + v[i];
+          cursor[b0 + i] = start + v[i];
+        }
     }
     carry += total;
-    __syncthreads();
+    __syncthreads();  // s_wave is rewritten by the next chunk
   }
   if (tid == 0) offsets[nbins] = carry;
 }
