@@ -140,6 +140,20 @@ def algorithmic_bytes(p):
             + p.e * 8 + p.bsdp * p.n * 2 + p.output_bs * p.n * 4)
 
 
+def host_cpu() -> str:
+    """The host CPU's model name and logical CPU count, as the kernel reports them."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} logical CPUs"
+
+
 def cpu_baseline(p, rows_wanted: int):
     """Time the oracle (whole computation) on a sample: the first rows of every
     expert group, all k and n, same destinations and output size."""
@@ -170,7 +184,7 @@ def cpu_baseline(p, rows_wanted: int):
         dt = time.perf_counter() - t0
     ops = 2.0 * q.m * q.k * q.n
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle", "host": host_cpu(),
             "sample": f"{q.m} of {p.covered_rows} rows (first rows of each of the {p.e} experts), full k={p.k}, "
                       f"n={p.n}, seed + combine into outputBS={p.output_bs}; {dt:.2f} s wall",
             "seconds": dt}
@@ -283,7 +297,7 @@ def bench_dispatch(args):
             reps += 1
         dt = (time.perf_counter() - t0) / reps
         res["cpu_baseline"] = {"value": round(step_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
-                               "kind": "oracle",
+                               "kind": "oracle", "host": host_cpu(),
                                "sample": f"the whole workload ({rp.T} tokens), {reps} runs, {dt:.2f} s each"}
     print(json.dumps(res), flush=True)
     del keep
