@@ -1779,10 +1779,35 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p, const int32
       }
       __syncthreads();
       // Rows in batches of kBatch: the batch's loads are issued together
-      // (independent, streamed once), then folded in ascending order.
+      // (independent, streamed once), then folded in ascending order; two
+      // float4 columns per pass while both exist (16 loads in flight).
       constexpr int kBatch = 8;
       typedef float v4f __attribute__((ext_vector_type(4)));
-      for (int64_t j4 = tid; j4 < n4; j4 += kThreads) {
+      int64_t j4 = tid;
+      for (; j4 + kThreads < n4; j4 += 2 * kThreads) {
+        const int64_t j4b = j4 + kThreads;
+        const float4 sa = seed4(p, d, j4), sb = seed4(p, d, j4b);
+        v4f va = {sa.x, sa.y, sa.z, sa.w}, vb = {sb.x, sb.y, sb.z, sb.w};
+        for (int s0 = 0; s0 < len; s0 += kBatch) {
+          v4f ya[kBatch], yb[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u)
+            if (s0 + u < len) {
+              const v4f* r = (const v4f*)(p.y + (int64_t)s_sorted[s0 + u] * n);
+              ya[u] = __builtin_nontemporal_load(r + j4);
+              yb[u] = __builtin_nontemporal_load(r + j4b);
+            }
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u)
+            if (s0 + u < len) {
+              va = va + ya[u];
+              vb = vb + yb[u];
+            }
+        }
+        __builtin_nontemporal_store(va, (v4f*)(p.out + d * n) + j4);
+        __builtin_nontemporal_store(vb, (v4f*)(p.out + d * n) + j4b);
+      }
+      for (; j4 < n4; j4 += kThreads) {
         const float4 seed = seed4(p, d, j4);
         v4f v = {seed.x, seed.y, seed.z, seed.w};
         for (int s0 = 0; s0 < len; s0 += kBatch) {
