@@ -1779,47 +1779,41 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p, const int32
       }
       __syncthreads();
       // Rows in batches of kBatch: the batch's loads are issued together
-      // (independent, streamed once), then folded in ascending order; two
-      // float4 columns per pass while both exist (16 loads in flight).
+      // (independent, streamed once), then folded in ascending order; four
+      // float4 columns a kThreads apart per pass (32 loads in flight).
       constexpr int kBatch = 8;
       typedef float v4f __attribute__((ext_vector_type(4)));
-      int64_t j4 = tid;
-      for (; j4 + kThreads < n4; j4 += 2 * kThreads) {
-        const int64_t j4b = j4 + kThreads;
-        const float4 sa = seed4(p, d, j4), sb = seed4(p, d, j4b);
-        v4f va = {sa.x, sa.y, sa.z, sa.w}, vb = {sb.x, sb.y, sb.z, sb.w};
+      constexpr int kCols = 4;
+      for (int64_t j0 = tid; j0 < n4; j0 += kCols * kThreads) {
+        v4f v[kCols];
+        bool ok[kCols];
+#pragma unroll
+        for (int c = 0; c < kCols; ++c) {
+          ok[c] = j0 + c * kThreads < n4;
+          const float4 sd = ok[c] ? seed4(p, d, j0 + c * kThreads) : make_float4(0.f, 0.f, 0.f, 0.f);
+          v[c] = v4f{sd.x, sd.y, sd.z, sd.w};
+        }
         for (int s0 = 0; s0 < len; s0 += kBatch) {
-          v4f ya[kBatch], yb[kBatch];
+          v4f yb[kBatch][kCols];
 #pragma unroll
           for (int u = 0; u < kBatch; ++u)
             if (s0 + u < len) {
               const v4f* r = (const v4f*)(p.y + (int64_t)s_sorted[s0 + u] * n);
-              ya[u] = __builtin_nontemporal_load(r + j4);
-              yb[u] = __builtin_nontemporal_load(r + j4b);
+#pragma unroll
+              for (int c = 0; c < kCols; ++c)
+                if (ok[c]) yb[u][c] = __builtin_nontemporal_load(r + j0 + c * kThreads);
             }
 #pragma unroll
           for (int u = 0; u < kBatch; ++u)
             if (s0 + u < len) {
-              va = va + ya[u];
-              vb = vb + yb[u];
+#pragma unroll
+              for (int c = 0; c < kCols; ++c)
+                if (ok[c]) v[c] = v[c] + yb[u][c];
             }
         }
-        __builtin_nontemporal_store(va, (v4f*)(p.out + d * n) + j4);
-        __builtin_nontemporal_store(vb, (v4f*)(p.out + d * n) + j4b);
-      }
-      for (; j4 < n4; j4 += kThreads) {
-        const float4 seed = seed4(p, d, j4);
-        v4f v = {seed.x, seed.y, seed.z, seed.w};
-        for (int s0 = 0; s0 < len; s0 += kBatch) {
-          v4f yb[kBatch];
 #pragma unroll
-          for (int u = 0; u < kBatch; ++u)
-            if (s0 + u < len) yb[u] = __builtin_nontemporal_load((const v4f*)(p.y + (int64_t)s_sorted[s0 + u] * n) + j4);
-#pragma unroll
-          for (int u = 0; u < kBatch; ++u)
-            if (s0 + u < len) v = v + yb[u];
-        }
-        __builtin_nontemporal_store(v, (v4f*)(p.out + d * n) + j4);
+        for (int c = 0; c < kCols; ++c)
+          if (ok[c]) __builtin_nontemporal_store(v[c], (v4f*)(p.out + d * n) + j0 + c * kThreads);
       }
       __syncthreads();
     } else {
