@@ -163,8 +163,13 @@ typedef struct {
    * description: the first value is the expected token count per expert and
    * the tiling follows it).  Element 1 (an extension of this library), if
    * present and non-zero, forces the tile height: 32, 64, 128 or 256; any
-   * other value is rejected (ATTR).  Results never depend on it.  May be
-   * NULL.                                                                     */
+   * other value is rejected (ATTR).  Element 2 (also ours, meant for tests),
+   * if present and non-zero, caps the number of workgroups of the persistent
+   * GEMM launch, so that each runs many tiles in a row; negative values are
+   * rejected (ATTR).  Results never depend on elements 0-2: the int32
+   * accumulators and the ordered combine are bit-identical for any value,
+   * the unordered combine differs only in the order of its additions.  May
+   * be NULL.                                                                  */
   const int64_t* tuning_config;
   int64_t tuning_config_len;
 } gmmfr_args;

@@ -176,3 +176,41 @@ def group_ranges(p):
     if st != 0:
         raise OracleError(st)
     return s, e
+
+
+def clamped_ends(group_list, group_list_type: int, m: int):
+    """End row of every group under the library's reading of a groupList that
+    breaks the operator's rule ("aclnnGroupedMatmulFinalizeRoutingWeightNzV2",
+    common constraints: type 0 lists non-negative, non-decreasing cumulative
+    ends; type 1 non-negative counts; and the rows they cover lie in x1).  The
+    library header states the reading for device data it cannot check: each
+    entry is clamped to [0, m]; type 0 ends are the running maximum of the
+    clamped entries, type 1 ends the running sum of the clamped counts, capped
+    at m.  For a list that keeps the rule this is the plain reading."""
+    ends = []
+    end = 0
+    for x in (int(v) for v in group_list):
+        c = min(max(x, 0), int(m))
+        end = max(end, c) if int(group_list_type) == 0 else min(end + c, int(m))
+        ends.append(end)
+    return np.array(ends, dtype=np.int64)
+
+
+def clamped_problem(p):
+    """A problem that keeps every rule and computes what the library computes
+    for ``p`` under the clamped reading of its device data: groups end at
+    ``clamped_ends`` (given as a type-0 list), and a row whose rowIndex lies
+    outside [0, outputBS) contributes nothing -- it is sent to one extra
+    destination row outputBS, which the caller drops from the result.
+    Returns (problem, rows of the real output)."""
+    import copy
+    q = copy.copy(p)
+    q.group_list = clamped_ends(p.group_list, p.group_list_type, p.m)
+    q.group_list_type = 0
+    if p.row_index is not None:
+        ri = np.asarray(p.row_index).astype(np.int64)
+        bad = (ri < 0) | (ri >= int(p.output_bs))
+        ri = np.where(bad, int(p.output_bs), ri)
+        q.row_index = ri.astype(np.asarray(p.row_index).dtype)
+    q.output_bs = int(p.output_bs) + 1
+    return q, int(p.output_bs)

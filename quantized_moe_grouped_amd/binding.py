@@ -195,6 +195,17 @@ def plan(args: Args) -> dict:
             "workspace_bytes": int(info.workspace_bytes), "gemm_kernel": info.gemm_kernel.decode()}
 
 
+def _torch_stream(stream):
+    """The torch stream object for `stream`: None (the current stream), a
+    torch.cuda.Stream, or a raw hipStream_t handle."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
 def run(args: Args, workspace=None, stream=None) -> None:
     """Enqueue on `stream` (default: torch's current stream on the current device)."""
     import torch
@@ -212,13 +223,21 @@ def run(args: Args, workspace=None, stream=None) -> None:
 
 def gmm_finalize_routing(x1, x2, group_list, out, *, workspace=None, stream=None, **kw) -> None:
     """One call: validate, size the workspace, allocate it with torch if none
-    is given, enqueue.  Keyword arguments are those of make_args."""
+    is given, enqueue.  Keyword arguments are those of make_args.
+
+    A workspace allocated here is taken from the pool of the stream the kernels
+    run on, so when it is released on return the caching allocator hands the
+    block out again only to work ordered after them on that stream (a block
+    from another stream's pool could be reused, and overwritten, while the
+    kernels still run)."""
     import torch
     args, keep = make_args(x1, x2, group_list, out, **kw)
     need = workspace_size(args)
+    ts = _torch_stream(stream)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=out.device)
-    run(args, workspace, stream)
+        with torch.cuda.stream(ts):
+            workspace = torch.empty(need, dtype=torch.uint8, device=out.device)
+    run(args, workspace, ts)
     del keep
 
 
@@ -265,6 +284,15 @@ def quant_permute(hidden, expert_ids, num_experts: int, *, topk_weights=None, ex
     T, k = hidden.shape
     K = expert_ids.shape[1]
     m = T * K
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):  # outputs and workspace from the pool of the stream that writes them
+        return _quant_permute_on(hidden, expert_ids, num_experts, topk_weights, expert_offset, group_list_type,
+                                 row_index_dtype, mode, workspace, ts, dev, T, k, m)
+
+
+def _quant_permute_on(hidden, expert_ids, num_experts, topk_weights, expert_offset, group_list_type,
+                      row_index_dtype, mode, workspace, ts, dev, T, k, m):
+    import torch
     if mode == "int8":
         x1 = torch.empty((m, k), dtype=torch.int8, device=dev)
         pts = torch.empty(m, dtype=torch.float32, device=dev)
@@ -287,10 +315,7 @@ def quant_permute(hidden, expert_ids, num_experts: int, *, topk_weights=None, ex
     need = qp_workspace_size(args)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    if stream is None:
-        stream = torch.cuda.current_stream().cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
+    stream = ts.cuda_stream
     ws_ptr = 0 if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().gmm_quant_permute(ctypes.byref(args), ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes),

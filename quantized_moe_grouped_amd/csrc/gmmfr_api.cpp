@@ -59,6 +59,9 @@ int check_attributes(const gmmfr_args* a) {
   if (a->tuning_config_len > 1 && a->tuning_config[1] != 0 && a->tuning_config[1] != 32 &&
       a->tuning_config[1] != 64 && a->tuning_config[1] != 128 && a->tuning_config[1] != 256)
     return GMMFR_ERR_ATTR;
+  // element 2: cap on the persistent GEMM's workgroups (0 = none)
+  if (a->tuning_config_len > 2 && (a->tuning_config[2] < 0 || a->tuning_config[2] >= (int64_t(1) << 31)))
+    return GMMFR_ERR_ATTR;
   return GMMFR_OK;
 }
 
@@ -333,6 +336,9 @@ int make_plan(const gmmfr_args* a, const Derived& d, int cu_count, Plan* plan) {
   const int64_t resident = (int64_t)std::max(cu_count, 1) * tile_occupancy(plan->tile);
   int64_t grid = std::min(max_tiles, resident);
   if (grid > 8) grid -= grid % 8;  // whole XCD rounds: workgroups are dealt to the 8 XCDs in turn
+  // An explicit cap (tuningConfig[2], for tests: it makes every workgroup
+  // run many tiles in a row) is taken as given, rounded or not.
+  if (a->tuning_config_len > 2 && a->tuning_config[2] > 0) grid = std::min(grid, a->tuning_config[2]);
   plan->grid = d.m > 0 ? (int32_t)grid : 0;
   plan->workspace_bytes = workspace_layout(d.m, d.n, d.output_bs, plan->combine == kCombineOrdered).total;
   return GMMFR_OK;

@@ -134,6 +134,31 @@ def test_plan_does_not_depend_on_data_and_follows_hint():
     assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.ERR_ATTR
 
 
+@pytest.mark.parametrize("cap", [1, 3, 8, 16, 100000])
+def test_grid_cap_limits_the_gemm_launch(cap):
+    """tuningConfig[2] caps the persistent GEMM's workgroups (a test hook:
+    results do not depend on it); 0 means no cap, negative is rejected."""
+    a = _args(m=131072, n=7168, obs=16384, e=32)
+    info = B.PlanInfo()
+    assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
+    full = info.grid
+    ws_full = info.workspace_bytes
+    hint = (ctypes.c_int64 * 3)(0, 0, cap)
+    a.tuning_config = ctypes.cast(hint, ctypes.POINTER(ctypes.c_int64))
+    a.tuning_config_len = 3
+    assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
+    assert info.grid == min(cap, full)
+    assert info.workspace_bytes == ws_full
+    for bad in (-1, -100):
+        hint = (ctypes.c_int64 * 3)(0, 0, bad)
+        a.tuning_config = ctypes.cast(hint, ctypes.POINTER(ctypes.c_int64))
+        assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.ERR_ATTR
+    hint = (ctypes.c_int64 * 3)(0, 0, 0)
+    a.tuning_config = ctypes.cast(hint, ctypes.POINTER(ctypes.c_int64))
+    assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
+    assert info.grid == full
+
+
 CASES = [
     ("nullptr_x1", dict(x1=B.Tensor()), B.ERR_NULLPTR),
     ("nullptr_group_list", dict(group_list=B.Tensor()), B.ERR_NULLPTR),

@@ -2,9 +2,10 @@
 
 Bars: int32 accumulators bit-exact; the ordered (deterministic) combine
 bit-exact; the unordered combine within max|err| <= 1e-5 * max|ref|.
-Small cases compare every element and span several tiles with ragged tails;
-the five named workloads run at full size and are checked on sampled rows
-that the oracle evaluates one by one.
+Small cases compare every element and span several tiles with ragged tails,
+also with the GEMM's grid capped so that each workgroup runs many tiles; the
+five named workloads run at full size and are compared on every output
+element (the int32 accumulators on sampled rows).
 """
 import copy
 import json
@@ -14,6 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
+from quantized_moe_grouped_amd import binding as B
 from quantized_moe_grouped_amd import workloads as W
 from tests import gpu_util as G
 
@@ -119,6 +121,53 @@ def test_per_tensor_scale_transposed_weights():
     p = W.with_per_tensor_scale(W.with_transposed_weights(W.random_problem(**CASES["long_k_no_factors"])), 0.75)
     _check_full(p, hints=(None, 8, (0, 256)))
 
+# ---------------------------------------------------------------- many tiles per workgroup
+
+def _check_grid_capped(p, caps=(3, 8, 16), tiles=(0, 32, 64, 128, 256)):
+    """The persistent GEMM with its grid capped (tuningConfig[2]): every
+    workgroup runs many tiles in a row, through the continuous pipeline's
+    tile-to-tile handoff (next tile's k-slices and row factors copied under
+    this tile's last k-steps, epilogue stores still in flight at the next
+    tile's first wait) or the dynamic queues.  Outputs are compared without
+    the accumulator dump, so the guard-free epilogue is the one checked:
+    ordered bit-exact, atomic within the tolerance; the int32 accumulators
+    in a separate run with the dump."""
+    ref, ref_acc = oracle.run(p)
+    cov = G.covered_mask(p)
+    d = G.to_device(p)
+    for cap in caps:
+        for tile in tiles:
+            tc = [0, tile, cap]
+            out, _ = G.run_gpu(p, d, deterministic=True, tuning_config=tc)
+            G.assert_bitexact(out.cpu().numpy(), ref)
+            out, _ = G.run_gpu(p, d, deterministic=False, combine="atomic", tuning_config=tc)
+            G.assert_close_atomic(out.cpu().numpy(), ref)
+            out, acc = G.run_gpu(p, d, deterministic=True, want_acc=True, tuning_config=tc)
+            acc = acc.cpu().numpy()
+            assert (acc[cov] == ref_acc[cov]).all(), f"acc mismatch (tile {tile}, grid cap {cap})"
+            assert (acc[~cov] == -0x55555556).all()
+            G.assert_bitexact(out.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("name", list(CASES), ids=list(CASES))
+def test_grid_capped_all_elements(name):
+    _check_grid_capped(W.random_problem(**CASES[name]))
+
+
+@pytest.mark.parametrize("name", TB_CASES, ids=TB_CASES)
+def test_grid_capped_transposed_weights(name):
+    _check_grid_capped(W.with_transposed_weights(W.random_problem(**CASES[name])))
+
+
+def test_grid_capped_single_workgroup():
+    """One workgroup runs every tile of a case with a ragged n tail, an empty
+    expert and two group tails, in both loop structures."""
+    p = W.random_problem(18, 700, 256, 528, 5, output_bs=300, bsdp=50, shared_offset=100, empty_frac=0.3)
+    _check_grid_capped(p, caps=(1,), tiles=(0, 32, 64, 128))
+    q = W.random_problem(19, 600, 256, 544, 4, int4=True, output_bs=200)
+    _check_grid_capped(q, caps=(1,), tiles=(0, 64, 128))
+
+
 def test_zero_rows_gives_seed():
     p = W.random_problem(9, 0, 64, 64, 2, output_bs=20, bsdp=6, shared_offset=3)
     ref, _ = oracle.run(p)
@@ -196,15 +245,6 @@ def test_gpu_empty_experts_with_nan_scale():
 
 # ---------------------------------------------------------------- named workloads at full size
 
-def _sample_rows(p, rng, count=48):
-    d = set(rng.choice(p.output_bs, size=min(count, p.output_bs), replace=False).tolist())
-    d |= {0, p.output_bs - 1}
-    if p.shared_input is not None:
-        o, b = p.shared_input_offset, p.bsdp
-        d |= {x for x in (o - 1, o, o + b - 1, o + b) if 0 <= x < p.output_bs}
-    return np.array(sorted(d), dtype=np.int64)
-
-
 def _sample_src(p, rng, count=48):
     s, e = oracle.group_ranges(p)
     rows = set(rng.choice(max(int(e[-1]), 1), size=min(count, max(int(e[-1]), 1)), replace=False).tolist())
@@ -214,40 +254,64 @@ def _sample_src(p, rng, count=48):
     return np.array(sorted(rows), dtype=np.int64)
 
 
+_NAMED_REF = {}
+
+
+def _named_ref(name, p):
+    """The oracle's whole output of a named workload (computed once per
+    session; the transposed-weights form of a workload has the same)."""
+    if name not in _NAMED_REF:
+        _NAMED_REF[name] = oracle.run(p, want_acc=False)[0]
+    return _NAMED_REF[name]
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["tiny", "decode", "skewed", "int4", "prefill"])
 def test_named_workload(name):
     _check_named(W.make_config(name, 0), name)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["decode", "prefill"])
 def test_named_workload_transposed_weights(name):
     _check_named(W.with_transposed_weights(W.make_config(name, 0)), name)
 
 
 def _check_named(p, name):
+    """A named workload at full size, every output element against the
+    oracle: the ordered combine (deterministic = 1) and the library's own
+    choice without the accumulator dump -- the launch the benchmark times --
+    bit-exact when that choice is the ordered combine, and the atomic
+    combine within the tolerance; the int32 accumulators of sampled rows from
+    a run with the dump (whose output must be bit-exact too)."""
     import torch
-    rng = np.random.default_rng(100)
+    ref = _named_ref(name, p)
     d = G.to_device(p)
-    if name == "tiny":
-        ref, ref_acc = oracle.run(p)
-        dsel = np.arange(p.output_bs)
-        isel = np.arange(p.m)
+    args, keep = B.make_args(d["x1"], d["x2"], d["group_list"], torch.empty((p.output_bs, p.n), device="cuda"),
+                             scale=d["scale"], pertoken_scale=d["pertoken_scale"], logit=d["logit"],
+                             row_index=d["row_index"], shared_input=d["shared_input"],
+                             shared_input_offset=p.shared_input_offset if p.shared_input is not None else 0,
+                             group_list_type=p.group_list_type, transpose_x2=p.x2_transposed)
+    auto_plan = B.plan(args)
+    del keep
+    out, _ = G.run_gpu(p, d, deterministic=True)
+    G.assert_bitexact(out.cpu().numpy(), ref)
+    del out
+    out, _ = G.run_gpu(p, d, deterministic=False, combine="auto")
+    if auto_plan["combine"] == "ordered":
+        G.assert_bitexact(out.cpu().numpy(), ref)
     else:
-        dsel = _sample_rows(p, rng)
-        isel = _sample_src(p, rng)
-        ref = oracle.out_rows(p, dsel)
-        ref_acc = oracle.acc_rows(p, isel)
-        ref_full = None
-    # int32 accumulators (the dump is written by the same launch as the output)
+        G.assert_close_atomic(out.cpu().numpy(), ref)
+    del out
+    out, _ = G.run_gpu(p, d, deterministic=False, combine="atomic")
+    G.assert_close_atomic(out.cpu().numpy(), ref)
+    del out
+    isel = np.arange(p.m) if name == "tiny" else _sample_src(p, np.random.default_rng(100))
     out, acc = G.run_gpu(p, d, deterministic=True, want_acc=True)
     got_acc = acc[torch.from_numpy(isel).cuda()].cpu().numpy()
     del acc
-    assert (got_acc == (ref_acc if name != "tiny" else ref_acc[isel])).all()
-    G.assert_bitexact(out.cpu().numpy()[dsel], ref if name != "tiny" else ref[dsel])
-    out2, _ = G.run_gpu(p, d, deterministic=False, combine="atomic")
-    G.assert_close_atomic(out2.cpu().numpy()[dsel], ref if name != "tiny" else ref[dsel])
-    out3, _ = G.run_gpu(p, d, deterministic=False, combine="auto")
-    G.assert_close_atomic(out3.cpu().numpy()[dsel], ref if name != "tiny" else ref[dsel])
+    assert (got_acc == oracle.acc_rows(p, isel)).all()
+    G.assert_bitexact(out.cpu().numpy(), ref)
 
 
 def test_ordered_mode_is_run_to_run_identical():

@@ -403,3 +403,63 @@ def test_named_configs_shapes(name):
     # every token gets the same number of rows
     cnt = np.bincount(p.row_index.astype(np.int64), minlength=p.output_bs)
     assert (cnt == p.m // p.output_bs).all()
+
+
+# ---------------------------------------------------------------- the clamped reading of broken device data
+
+@pytest.mark.parametrize("gl,glt,m,want", [
+    ([3, 2, 7], 0, 5, [3, 3, 5]),          # decreasing entry kept at the running maximum; past m clamped
+    ([-4, 2, 1, 9], 0, 6, [0, 2, 2, 6]),   # negative entry read as 0
+    ([3, 4, 2], 1, 5, [3, 5, 5]),          # counts past m: the running sum stops at m
+    ([-2, 2, 1], 1, 10, [0, 2, 3]),        # negative count read as 0
+    ([2, 5, 5, 9], 0, 9, [2, 5, 5, 9]),    # a list that keeps the rule is read plainly
+    ([2, 3, 0, 4], 1, 9, [2, 5, 5, 9]),
+])
+def test_clamped_group_ends_hand_derived(gl, glt, m, want):
+    """Ends under the library's reading of a broken groupList (entries clamped
+    to [0, m]; running maximum for type 0, running sum capped at m for type
+    1), against values worked out by hand."""
+    assert oracle.clamped_ends(np.array(gl, dtype=np.int64), glt, m).tolist() == want
+
+
+def test_clamped_problem_of_a_valid_problem_is_the_problem():
+    p = W.random_problem(31, 120, 64, 48, 4, output_bs=40, bsdp=10, shared_offset=5, group_list_type=1)
+    q, rows = oracle.clamped_problem(p)
+    ref, _ = oracle.run(p)
+    got, _ = oracle.run(q)
+    assert rows == p.output_bs
+    assert np.array_equal(got[:rows], ref)
+    assert not got[rows:].any()
+
+
+def test_clamped_problem_drops_rows_sent_outside_the_output():
+    """Rows whose rowIndex lies outside [0, outputBS) contribute nothing: the
+    clamped problem equals the same problem with those rows sent to row 0
+    with a zero routing weight (their products are then +-0)."""
+    p = W.random_problem(32, 150, 64, 32, 3, output_bs=30)
+    bad = np.array([3, 77, 149])
+    p.row_index[bad[:2]] = -1
+    p.row_index[bad[2]] = p.output_bs
+    q, rows = oracle.clamped_problem(p)
+    got, _ = oracle.run(q)
+    z = copy.deepcopy(p)
+    z.row_index[bad] = 0
+    z.logit[bad] = 0.0
+    ref, _ = oracle.run(z)
+    assert np.array_equal(got[:rows], ref)
+
+
+def test_clamped_problem_reads_a_broken_group_list():
+    """A type-0 list with a decreasing entry and an end past m equals the
+    list of its clamped ends; rows past the last end contribute nothing."""
+    p = W.random_problem(33, 100, 64, 32, 4, output_bs=25)
+    p.group_list = np.array([40, 30, 70, 500], dtype=np.int64)
+    q, rows = oracle.clamped_problem(p)
+    assert q.group_list.tolist() == [40, 40, 70, 100]
+    r = copy.deepcopy(p)
+    r.group_list = np.array([40, 40, 70, 100], dtype=np.int64)
+    ref, _ = oracle.run(r)
+    got, _ = oracle.run(q)
+    assert np.array_equal(got[:rows], ref)
+    with pytest.raises(oracle.OracleError):
+        oracle.run(p)  # the oracle itself keeps the rule strictly
