@@ -209,6 +209,25 @@ int gmm_finalize_routing(const gmmfr_args* args, void* workspace, size_t workspa
 int gmm_finalize_routing_profiled(const gmmfr_args* args, void* workspace, size_t workspace_bytes, void* stream,
                                   void* gemm_start, void* gemm_stop);
 
+/* Allocation-free variant of stage 2, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Identical work and results to
+ * gmm_finalize_routing, but the workspace is a device array inside the
+ * library, GMMFR_NOALLOC_SCRATCH_BYTES long, which each GPU the library runs
+ * on holds from its first use until the process ends; the call itself
+ * allocates and frees nothing.  The caller still passes every input and
+ * output.  A plan that needs more workspace than the array holds is rejected
+ * with GMMFR_ERR_WORKSPACE before any device work (the ordered combine needs
+ * about m*n*4 bytes: force combine = GMMFR_COMBINE_ATOMIC, whose plan needs
+ * 1 KiB, or use gmm_finalize_routing).  Every call on one GPU shares that
+ * GPU's array and the kernels re-initialise what they use, so calls that
+ * overlap on one GPU (on different streams, or from different host threads
+ * without ordering) race and give wrong results; calls ordered on one stream
+ * are safe.  Returns as gmm_finalize_routing; GMMFR_ERR_HIP also when the
+ * array's device address cannot be obtained. */
+#define GMMFR_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int gmm_finalize_routing_noalloc(const gmmfr_args* args, void* stream);
+
 /* Description of the plan stage 2 would use for `args` (host only). */
 typedef struct {
   int32_t combine;          /* gmmfr_combine actually used (ATOMIC or ORDERED) */

@@ -24,7 +24,8 @@ COMBINE = {"auto": 0, "atomic": 1, "ordered": 2}
 
 EXPORTED = ("gmm_finalize_routing_workspace", "gmm_finalize_routing", "gmm_finalize_routing_profiled",
             "gmm_finalize_routing_plan", "gmmfr_status_string", "gmm_quant_permute_workspace",
-            "gmm_quant_permute", "gmm_quant_permute_profiled")
+            "gmm_quant_permute", "gmm_quant_permute_profiled", "gmm_finalize_routing_noalloc")
+NOALLOC_SCRATCH_BYTES = 128 << 20  # GMMFR_NOALLOC_SCRATCH_BYTES
 
 
 class GmmfrError(RuntimeError):
@@ -83,6 +84,8 @@ def lib():
         L.gmm_finalize_routing_profiled.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p, ctypes.c_size_t,
                                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.gmm_finalize_routing_profiled.restype = ctypes.c_int
+        L.gmm_finalize_routing_noalloc.argtypes = [ctypes.POINTER(Args), ctypes.c_void_p]
+        L.gmm_finalize_routing_noalloc.restype = ctypes.c_int
         L.gmm_finalize_routing_plan.argtypes = [ctypes.POINTER(Args), ctypes.POINTER(PlanInfo)]
         L.gmm_finalize_routing_plan.restype = ctypes.c_int
         L.gmm_quant_permute_workspace.argtypes = [ctypes.POINTER(QpArgs), ctypes.POINTER(ctypes.c_size_t)]
@@ -238,6 +241,28 @@ def gmm_finalize_routing(x1, x2, group_list, out, *, workspace=None, stream=None
         with torch.cuda.stream(ts):
             workspace = torch.empty(need, dtype=torch.uint8, device=out.device)
     run(args, workspace, ts)
+    del keep
+
+
+def run_noalloc(args: Args, stream=None) -> None:
+    """Enqueue through the allocation-free entry point (the library's own
+    scratch array; nothing is allocated) on `stream` (default: the current
+    stream)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    st = lib().gmm_finalize_routing_noalloc(ctypes.byref(args), ctypes.c_void_p(stream))
+    if st != OK:
+        raise GmmfrError(st, "gmm_finalize_routing_noalloc")
+
+
+def gmm_finalize_routing_noalloc(x1, x2, group_list, out, *, stream=None, **kw) -> None:
+    """gmm_finalize_routing without any allocation (see run_noalloc).
+    Keyword arguments are those of make_args."""
+    args, keep = make_args(x1, x2, group_list, out, **kw)
+    run_noalloc(args, stream)
     del keep
 
 

@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/gmmfr.h"
 #include "gmmfr_internal.h"
@@ -386,6 +387,35 @@ bool log_enabled() {
   return v && v[0] == '1';
 }
 
+// ---------------------------------------------------------------------------
+// Scratch memory of the allocation-free entry point: one file-scope device
+// array, GMMFR_NOALLOC_SCRATCH_BYTES long, which every GPU the library runs on
+// holds until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is looked up once per
+// device with hipGetSymbolAddress (with that device current) and only that
+// address is handed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[GMMFR_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on its
+// first use there).  Returns GMMFR_OK or GMMFR_ERR_HIP.
+int scratch_of_current_device(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GMMFR_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GMMFR_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return GMMFR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -432,6 +462,22 @@ int gmm_finalize_routing_profiled(const gmmfr_args* args, void* workspace, size_
                                   void* gemm_start, void* gemm_stop) {
   void* ev[2] = {gemm_start, gemm_stop};
   return run_stage2(args, workspace, workspace_bytes, stream, ev);
+}
+
+int gmm_finalize_routing_noalloc(const gmmfr_args* args, void* stream) {
+  // Validate and size on the host first: a plan that needs more scratch than
+  // the array holds is rejected before any device is touched.
+  Derived d;
+  int st = validate(args, &d);
+  if (st != GMMFR_OK) return st;
+  Plan plan;
+  st = make_plan(args, d, 1, &plan);
+  if (st != GMMFR_OK) return st;
+  if (plan.workspace_bytes > (size_t)GMMFR_NOALLOC_SCRATCH_BYTES) return GMMFR_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != GMMFR_OK) return st;
+  return run_stage2(args, ws, (size_t)GMMFR_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int gmm_finalize_routing_plan(const gmmfr_args* args, gmmfr_plan_info* info) {

@@ -437,3 +437,22 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+# ---------------------------------------------------------------- allocation-free entry point
+
+def test_noalloc_rejects_plans_larger_than_its_scratch_before_device_work():
+    """The allocation-free entry point validates and sizes on the host and
+    rejects a plan whose workspace exceeds its fixed scratch array (here the
+    ordered combine's m*n*4 bytes of contributions) before touching a device,
+    so this runs without one; validation errors come first."""
+    a = _args(m=8192, n=7168, obs=1024, e=8)  # fake pointers, never dereferenced
+    a.combine = B.COMBINE["ordered"]
+    assert 8192 * 7168 * 4 > B.NOALLOC_SCRATCH_BYTES
+    assert B.lib().gmm_finalize_routing_noalloc(ctypes.byref(a), None) == B.ERR_WORKSPACE
+    a.deterministic = 1
+    a.combine = B.COMBINE["auto"]
+    assert B.lib().gmm_finalize_routing_noalloc(ctypes.byref(a), None) == B.ERR_WORKSPACE
+    a.x1 = B.Tensor()
+    assert B.lib().gmm_finalize_routing_noalloc(ctypes.byref(a), None) == B.ERR_NULLPTR
+    assert B.lib().gmm_finalize_routing_noalloc(None, None) == B.ERR_NULLPTR
