@@ -166,7 +166,10 @@ typedef struct {
    * other value is rejected (ATTR).  Element 2 (also ours, meant for tests),
    * if present and non-zero, caps the number of workgroups of the persistent
    * GEMM launch, so that each runs many tiles in a row; negative values are
-   * rejected (ATTR).  Results never depend on elements 0-2: the int32
+   * rejected (ATTR).  Element 3 (ours, for tests) picks how the ordered
+   * combine finds each destination's rows: 0 by problem size, 1 a bucket
+   * index, 2 a scan of rowIndex per destination; other values are rejected
+   * (ATTR).  Results never depend on elements 0-3: the int32
    * accumulators and the ordered combine are bit-identical for any value,
    * the unordered combine differs only in the order of its additions.  May
    * be NULL.                                                                  */

@@ -63,6 +63,8 @@ int check_attributes(const gmmfr_args* a) {
   // element 2: cap on the persistent GEMM's workgroups (0 = none)
   if (a->tuning_config_len > 2 && (a->tuning_config[2] < 0 || a->tuning_config[2] >= (int64_t(1) << 31)))
     return GMMFR_ERR_ATTR;
+  // element 3: the ordered combine's row lookup (0 = by size, 1 = bucket index, 2 = scan)
+  if (a->tuning_config_len > 3 && (a->tuning_config[3] < 0 || a->tuning_config[3] > 2)) return GMMFR_ERR_ATTR;
   return GMMFR_OK;
 }
 
@@ -341,6 +343,9 @@ int make_plan(const gmmfr_args* a, const Derived& d, int cu_count, Plan* plan) {
   // run many tiles in a row) is taken as given, rounded or not.
   if (a->tuning_config_len > 2 && a->tuning_config[2] > 0) grid = std::min(grid, a->tuning_config[2]);
   plan->grid = d.m > 0 ? (int32_t)grid : 0;
+  const int64_t lookup = a->tuning_config_len > 3 ? a->tuning_config[3] : 0;
+  plan->scan_reduce = plan->combine == kCombineOrdered &&
+                      (lookup == 2 || (lookup == 0 && d.m * d.output_bs <= kScanReduceMax));
   plan->workspace_bytes = workspace_layout(d.m, d.n, d.output_bs, plan->combine == kCombineOrdered).total;
   return GMMFR_OK;
 }

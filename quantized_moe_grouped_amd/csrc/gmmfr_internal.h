@@ -61,8 +61,13 @@ struct Plan {
   Combine combine;
   TileId tile;
   int32_t grid;             // GEMM workgroups (persistent)
+  bool scan_reduce;         // ordered combine without the bucket index (small m * outputBS)
   size_t workspace_bytes;
 };
+
+// The ordered combine scans rowIndex once per destination instead of
+// building a bucket index when m * outputBS is at most this.
+constexpr int64_t kScanReduceMax = int64_t(1) << 23;
 
 // Enqueue the whole computation.  Returns 0 or a hipError_t value.
 // gemm_events: optional {start, stop} hipEvent_t recorded around the GEMM.

@@ -1754,6 +1754,78 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(KParams p, int32_t* c
 
 constexpr int kSegMax = 1024;  // longer segments take the scanning path
 
+// out[d] = seed[d] + y[rows[0]] + y[rows[1]] + ... (left to right), rows in
+// LDS in ascending order.  Rows in batches of kBatch: the batch's loads are
+// issued together (independent, streamed once), then folded in ascending
+// order; four float4 columns a kThreads apart per pass (32 loads in flight).
+__device__ void fold_sorted_rows(const KParams& p, int64_t d, const int32_t* s_sorted, int len) {
+  const int tid = threadIdx.x;
+  const int64_t n = p.n, n4 = n / 4;
+  constexpr int kBatch = 8;
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  constexpr int kCols = 4;
+  for (int64_t j0 = tid; j0 < n4; j0 += kCols * kThreads) {
+    v4f v[kCols];
+    bool ok[kCols];
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) {
+      ok[c] = j0 + c * kThreads < n4;
+      const float4 sd = ok[c] ? seed4(p, d, j0 + c * kThreads) : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[c] = v4f{sd.x, sd.y, sd.z, sd.w};
+    }
+    for (int s0 = 0; s0 < len; s0 += kBatch) {
+      v4f yb[kBatch][kCols];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (s0 + u < len) {
+          const v4f* r = (const v4f*)(p.y + (int64_t)s_sorted[s0 + u] * n);
+#pragma unroll
+          for (int c = 0; c < kCols; ++c)
+            if (ok[c]) yb[u][c] = __builtin_nontemporal_load(r + j0 + c * kThreads);
+        }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (s0 + u < len) {
+#pragma unroll
+          for (int c = 0; c < kCols; ++c)
+            if (ok[c]) v[c] = v[c] + yb[u][c];
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < kCols; ++c)
+      if (ok[c]) __builtin_nontemporal_store(v[c], (v4f*)(p.out + d * n) + j0 + c * kThreads);
+  }
+}
+
+// The same fold for a destination with more than kSegMax rows: walk all
+// covered rows in ascending order, kThreads at a time, per column block.
+__device__ void fold_long_segment(const KParams& p, int64_t d, int64_t covered, int32_t* s_dst) {
+  const int tid = threadIdx.x;
+  const int64_t n = p.n, n4 = n / 4;
+  for (int64_t j4b = 0; j4b < n4; j4b += kThreads) {
+    const int64_t j4 = j4b + tid;
+    float4 v = j4 < n4 ? seed4(p, d, j4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t i0 = 0; i0 < covered; i0 += kThreads) {
+      const int64_t i = i0 + tid;
+      s_dst[tid] = i < covered ? (int32_t)dest_row(p, i) : -1;
+      __syncthreads();
+      const int cnt = (int)min((int64_t)kThreads, covered - i0);
+      if (j4 < n4) {
+        for (int c = 0; c < cnt; ++c) {
+          if (s_dst[c] != d) continue;
+          const float4 y = *(const float4*)(p.y + (i0 + c) * n + j4 * 4);
+          v.x = v.x + y.x;
+          v.y = v.y + y.y;
+          v.z = v.z + y.z;
+          v.w = v.w + y.w;
+        }
+      }
+      __syncthreads();
+    }
+    if (j4 < n4) *(float4*)(p.out + d * n + j4 * 4) = v;
+  }
+}
+
 // One workgroup per destination row (grid-stride).  The destination's rows
 // (unordered after the scatter) are ranked in LDS -- ranks are unique because
 // row ids are -- then every column folds seed + y[rows] in ascending order.
@@ -1763,7 +1835,6 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p, const int32
   __shared__ int32_t s_dst[kThreads];
   __shared__ int64_t s_red[kThreads];
   const int tid = threadIdx.x;
-  const int64_t n = p.n, n4 = n / 4;
   int64_t covered = -1;
   for (int64_t d = blockIdx.x; d < p.output_bs; d += gridDim.x) {
     const int32_t beg = offsets[d];
@@ -1778,70 +1849,92 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p, const int32
         s_sorted[rank] = x;
       }
       __syncthreads();
-      // Rows in batches of kBatch: the batch's loads are issued together
-      // (independent, streamed once), then folded in ascending order; four
-      // float4 columns a kThreads apart per pass (32 loads in flight).
-      constexpr int kBatch = 8;
-      typedef float v4f __attribute__((ext_vector_type(4)));
-      constexpr int kCols = 4;
-      for (int64_t j0 = tid; j0 < n4; j0 += kCols * kThreads) {
-        v4f v[kCols];
-        bool ok[kCols];
-#pragma unroll
-        for (int c = 0; c < kCols; ++c) {
-          ok[c] = j0 + c * kThreads < n4;
-          const float4 sd = ok[c] ? seed4(p, d, j0 + c * kThreads) : make_float4(0.f, 0.f, 0.f, 0.f);
-          v[c] = v4f{sd.x, sd.y, sd.z, sd.w};
-        }
-        for (int s0 = 0; s0 < len; s0 += kBatch) {
-          v4f yb[kBatch][kCols];
-#pragma unroll
-          for (int u = 0; u < kBatch; ++u)
-            if (s0 + u < len) {
-              const v4f* r = (const v4f*)(p.y + (int64_t)s_sorted[s0 + u] * n);
-#pragma unroll
-              for (int c = 0; c < kCols; ++c)
-                if (ok[c]) yb[u][c] = __builtin_nontemporal_load(r + j0 + c * kThreads);
-            }
-#pragma unroll
-          for (int u = 0; u < kBatch; ++u)
-            if (s0 + u < len) {
-#pragma unroll
-              for (int c = 0; c < kCols; ++c)
-                if (ok[c]) v[c] = v[c] + yb[u][c];
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < kCols; ++c)
-          if (ok[c]) __builtin_nontemporal_store(v[c], (v4f*)(p.out + d * n) + j0 + c * kThreads);
-      }
+      fold_sorted_rows(p, d, s_sorted, len);
       __syncthreads();
     } else {
-      // Long segment: walk all covered rows in ascending order.
       if (covered < 0) covered = block_covered_rows(p, s_red);
-      for (int64_t j4b = 0; j4b < n4; j4b += kThreads) {
-        const int64_t j4 = j4b + tid;
-        float4 v = j4 < n4 ? seed4(p, d, j4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int64_t i0 = 0; i0 < covered; i0 += kThreads) {
-          const int64_t i = i0 + tid;
-          s_dst[tid] = i < covered ? (int32_t)dest_row(p, i) : -1;
-          __syncthreads();
-          const int cnt = (int)min((int64_t)kThreads, covered - i0);
-          if (j4 < n4) {
-            for (int c = 0; c < cnt; ++c) {
-              if (s_dst[c] != d) continue;
-              const float4 y = *(const float4*)(p.y + (i0 + c) * n + j4 * 4);
-              v.x = v.x + y.x;
-              v.y = v.y + y.y;
-              v.z = v.z + y.z;
-              v.w = v.w + y.w;
-            }
-          }
-          __syncthreads();
-        }
-        if (j4 < n4) *(float4*)(p.out + d * n + j4 * 4) = v;
-      }
+      fold_long_segment(p, d, covered, s_dst);
     }
+  }
+}
+
+// Ordered combine without a bucket index, for problems where every
+// workgroup reading all of rowIndex is cheap (m * outputBS small): one
+// workgroup per destination row (grid-stride) scans the covered rows in
+// ascending order, kScanRows at a time (16 consecutive rows per thread, a
+// count per thread, a block-wide exclusive scan of the counts), collects the
+// rows sent to it -- already ascending -- and folds them like reduce_kernel.
+constexpr int kScanPerThread = 16, kScanRows = kThreads * kScanPerThread;
+__global__ __launch_bounds__(kThreads) void reduce_scan_kernel(KParams p) {
+  __shared__ int32_t s_rows[kSegMax];
+  __shared__ int32_t s_dst[kThreads];
+  __shared__ int32_t s_wave[kThreads / 64];
+  __shared__ int64_t s_red[kThreads];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t covered = block_covered_rows(p, s_red);
+  for (int64_t d = blockIdx.x; d < p.output_bs; d += gridDim.x) {
+    int len = 0;  // rows found so far (the same in every thread)
+    for (int64_t c0 = 0; c0 < covered; c0 += kScanRows) {
+      const int64_t i0 = c0 + (int64_t)tid * kScanPerThread;
+      uint32_t hits = 0;  // bit u: row i0 + u goes to d
+      if (p.row_index && i0 + kScanPerThread <= covered) {
+        // whole run of 16 rows: 16-byte loads, all issued before any compare
+        // (i0 is a multiple of 16 and the base 16-byte aligned)
+        if (p.row_index_i32) {
+          uint4 w[kScanPerThread / 4];
+#pragma unroll
+          for (int q = 0; q < kScanPerThread / 4; ++q) w[q] = ((const uint4*)((const int32_t*)p.row_index + i0))[q];
+#pragma unroll
+          for (int q = 0; q < kScanPerThread / 4; ++q) {
+            const uint32_t v[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) hits |= (uint32_t)((int64_t)(int32_t)v[t] == d) << (4 * q + t);
+          }
+        } else {
+          uint4 w[kScanPerThread / 2];
+#pragma unroll
+          for (int q = 0; q < kScanPerThread / 2; ++q) w[q] = ((const uint4*)((const int64_t*)p.row_index + i0))[q];
+#pragma unroll
+          for (int q = 0; q < kScanPerThread / 2; ++q) {
+            const int64_t lo = (int64_t)(((uint64_t)w[q].y << 32) | w[q].x);
+            const int64_t hi = (int64_t)(((uint64_t)w[q].w << 32) | w[q].z);
+            hits |= ((uint32_t)(lo == d) << (2 * q)) | ((uint32_t)(hi == d) << (2 * q + 1));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kScanPerThread; ++u)
+          if (i0 + u < covered && dest_row(p, i0 + u) == d) hits |= 1u << u;
+      }
+      const int mine = __popc(hits);
+      int incl = mine;  // inclusive scan over the wave
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      if (lane == 63) s_wave[wv] = incl;
+      __syncthreads();
+      int before = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) {
+        const int t = s_wave[w];
+        before += w < wv ? t : 0;
+        total += t;
+      }
+      int pos = len + before + incl - mine;
+#pragma unroll
+      for (int u = 0; u < kScanPerThread; ++u)
+        if ((hits >> u) & 1u) {
+          if (pos < kSegMax) s_rows[pos] = (int32_t)(i0 + u);
+          ++pos;
+        }
+      len += total;
+      __syncthreads();  // s_wave is rewritten by the next chunk
+    }
+    if (len <= kSegMax) fold_sorted_rows(p, d, s_rows, len);
+    else fold_long_segment(p, d, covered, s_dst);
+    __syncthreads();  // s_rows is rewritten for the next destination
   }
 }
 
@@ -1974,7 +2067,15 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
   kp.tile_ctr = (int32_t*)(ws + w.ctrl_off);
 
   const int64_t n4 = a.n / 4;
-  if (plan.combine == kCombineOrdered) {
+  // the tile-by-tile loop of the int8/int4 kernel takes its tiles from
+  // queues whose counters start at zero; the other loops use a static order
+  const bool dynamic_queues =
+      !a.mx && !a.fp8 && !(ts.bm >= 64 && uses_continuous_pipeline(a.int4, a.k, ts.bm, ts.bk, 3));
+  if (plan.combine == kCombineOrdered && plan.scan_reduce) {
+    kp.y = (float*)(ws + w.y_off);
+    if (dynamic_queues)
+      hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(kThreads), 0, s, (int32_t*)nullptr, (int64_t)0, kp.tile_ctr);
+  } else if (plan.combine == kCombineOrdered) {
     kp.y = (float*)(ws + w.y_off);
     int32_t* counts = (int32_t*)(ws + w.counts_off);
     int32_t* cursor = (int32_t*)(ws + w.cursor_off);
@@ -2030,8 +2131,11 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
   }
   if (plan.combine == kCombineOrdered) {
     const int gr = (int)std::min<int64_t>(65535, a.output_bs);
-    hipLaunchKernelGGL(reduce_kernel, dim3(gr > 0 ? gr : 1), dim3(kThreads), 0, s, kp,
-                       (const int32_t*)(ws + w.offsets_off), (const int32_t*)(ws + w.list_off));
+    if (plan.scan_reduce)
+      hipLaunchKernelGGL(reduce_scan_kernel, dim3(gr > 0 ? gr : 1), dim3(kThreads), 0, s, kp);
+    else
+      hipLaunchKernelGGL(reduce_kernel, dim3(gr > 0 ? gr : 1), dim3(kThreads), 0, s, kp,
+                         (const int32_t*)(ws + w.offsets_off), (const int32_t*)(ws + w.list_off));
   }
   return (int)hipGetLastError();
 }

@@ -456,3 +456,14 @@ def test_noalloc_rejects_plans_larger_than_its_scratch_before_device_work():
     a.x1 = B.Tensor()
     assert B.lib().gmm_finalize_routing_noalloc(ctypes.byref(a), None) == B.ERR_NULLPTR
     assert B.lib().gmm_finalize_routing_noalloc(None, None) == B.ERR_NULLPTR
+
+
+def test_row_lookup_hint_is_checked():
+    """tuningConfig[3] picks the ordered combine's row lookup: 0, 1 or 2."""
+    a = _args(m=4096, n=7168, obs=512, e=8)
+    info = B.PlanInfo()
+    for v, want in ((0, B.OK), (1, B.OK), (2, B.OK), (3, B.ERR_ATTR), (-1, B.ERR_ATTR)):
+        hint = (ctypes.c_int64 * 4)(0, 0, 0, v)
+        a.tuning_config = ctypes.cast(hint, ctypes.POINTER(ctypes.c_int64))
+        a.tuning_config_len = 4
+        assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == want

@@ -88,10 +88,15 @@ CASES = {
 }
 
 
+# tile hints covering every tile variant, and the ordered combine's two row
+# lookups (tuningConfig[3]: 1 bucket index, 2 scan of rowIndex)
+HINTS = (None, 8, 100, 300, (0, 256), (0, 0, 0, 1), (0, 0, 0, 2), (0, 64, 0, 1), (8, 0, 0, 1))
+
+
 @pytest.mark.parametrize("name", list(CASES), ids=list(CASES))
 def test_random_case_all_elements(name):
     p = W.random_problem(**CASES[name])
-    _check_full(p, hints=(None, 8, 100, 300, (0, 256)))  # every tile variant
+    _check_full(p, hints=HINTS)
 
 
 # int8 weights given transposed, (e,n,k) (parameter notes: transposed x2)
@@ -102,7 +107,7 @@ TB_CASES = ["ragged_n_shared", "counts_i32_bf16_uncovered", "many_empty_experts"
 @pytest.mark.parametrize("name", TB_CASES, ids=TB_CASES)
 def test_random_case_transposed_weights(name):
     p = W.with_transposed_weights(W.random_problem(**CASES[name]))
-    _check_full(p, hints=(None, 8, 100, 300, (0, 256)))
+    _check_full(p, hints=HINTS)
 
 
 
@@ -137,7 +142,7 @@ def _check_grid_capped(p, caps=(3, 8, 16), tiles=(0, 32, 64, 128, 256)):
     d = G.to_device(p)
     for cap in caps:
         for tile in tiles:
-            tc = [0, tile, cap]
+            tc = [0, tile, cap, 1 + (caps.index(cap) + tiles.index(tile)) % 2]  # both row lookups
             out, _ = G.run_gpu(p, d, deterministic=True, tuning_config=tc)
             G.assert_bitexact(out.cpu().numpy(), ref)
             out, _ = G.run_gpu(p, d, deterministic=False, combine="atomic", tuning_config=tc)
@@ -177,18 +182,19 @@ def test_zero_rows_gives_seed():
 
 
 def test_long_segment_path():
-    """More than 1024 rows into one destination takes the reducer's scanning path."""
+    """More than 1024 rows into one destination take the reducer's long-segment
+    path, with either row lookup."""
     p = W.random_problem(10, 1500, 64, 64, 3, output_bs=3, bsdp=3, shared_offset=0)
     p.row_index[:] = 0
     p.row_index[::7] = 2
-    _check_full(p, hints=(None,))
+    _check_full(p, hints=(None, (0, 0, 0, 1), (0, 0, 0, 2)))
 
 
 def test_many_destinations_scan_in_chunks():
     """output_bs above the index scan's LDS chunk (32768 destinations): the
     offsets are built over several chunks with a carry."""
     p = W.random_problem(14, 3000, 64, 16, 3, output_bs=70001, bsdp=5000, shared_offset=60000)
-    _check_full(p, hints=(None,))
+    _check_full(p, hints=(None, (0, 0, 0, 2)))
 
 
 def test_extreme_accumulators_round_like_the_oracle():
