@@ -7,7 +7,9 @@ notes on the MxA8W4 quantisation: x2 given as (e,n,k) with transposeX2 fixed
 true, pertokenScale of shape (m, ceil(k/64), 2) required, scale of shape
 (e, n, ceil(k/64), 2); the page's dtype table is lost, and the reading taken is
 x1 FLOAT8_E4M3FN, x2 FLOAT4_E2M1 two per byte along k, both scales
-FLOAT8_E8M0, one scale per 32 consecutive k):
+FLOAT8_E8M0, one scale per 32 consecutive k; the page asks k % 32 == 0, so
+when k % 64 == 32 the second byte of each row's last scale pair stands for no
+block and is not read):
 
     acc[i][j] = sum_kk x1[i][kk] * 2^(pts[i][kk//32] - 127) * w[g][j][kk] * 2^(scale[g][j][kk//32] - 127)
     y[i][j]   = acc[i][j] * logit[i]
@@ -110,7 +112,9 @@ def _scaled_rows(p, rows):
     x = FP8_TABLE[np.asarray(p.x1)[rows]]
     if _is_fp8(p):
         return x
-    s = E8M0_TABLE[np.asarray(p.pertoken_scale)[rows]].reshape(len(rows), -1)  # (rows, k/32)
+    # (rows, ceil(k/64)*2) bytes; the first k/32 are the blocks' scales (when
+    # k % 64 == 32 the last pair's second byte stands for no block)
+    s = E8M0_TABLE[np.asarray(p.pertoken_scale)[rows]].reshape(len(rows), -1)[:, :p.k // 32]
     return x * np.repeat(s, 32, axis=1)
 
 
@@ -122,7 +126,7 @@ def _scaled_weights(p, g):
         w = np.asarray(p.x2)[g]
         return FP8_TABLE[w if getattr(p, "x2_transposed", True) else w.T]
     w = FP4_TABLE[unpack_fp4(np.asarray(p.x2)[g])]
-    s = E8M0_TABLE[np.asarray(p.scale)[g]].reshape(p.n, -1)  # (n, k/32)
+    s = E8M0_TABLE[np.asarray(p.scale)[g]].reshape(p.n, -1)[:, :p.k // 32]  # (n, k/32), as for the rows
     return w * np.repeat(s, 32, axis=1)
 
 

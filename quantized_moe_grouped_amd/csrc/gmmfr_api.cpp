@@ -96,7 +96,8 @@ int check_output_and_alignment(const gmmfr_args* a, int64_t n, int64_t* bsdp) {
 // pertokenScale required with shape (m, ceil(k/64), 2), scale shape
 // (e, n, ceil(k/64), 2), k % 32 == 0, n % 32 == 0; rowIndex INT64 only).
 // Reading of the lost dtype table: x1 FLOAT8_E4M3FN, x2 FLOAT4_E2M1 two per
-// byte along k, both scales FLOAT8_E8M0 (one per 32 k).  Ours: k % 128 == 0.
+// byte along k, both scales FLOAT8_E8M0 (one per 32 k; when k % 64 == 32 the
+// second byte of each row's last pair stands for no block and is ignored).
 int validate_mx(const gmmfr_args* a, Derived* d) {
   if (!present(a->pertoken_scale) || !present(a->scale)) return GMMFR_ERR_NULLPTR;
   if (a->x2.dtype != GMMFR_DT_FLOAT4_E2M1X2) return GMMFR_ERR_DTYPE;
@@ -118,11 +119,11 @@ int validate_mx(const gmmfr_args* a, Derived* d) {
   if (a->x2.dims[2] * 2 != k) return GMMFR_ERR_SHAPE;
   if (m < 0 || m >= (int64_t(1) << 31)) return GMMFR_ERR_SHAPE;
   if (e < 1 || e > kMaxExperts) return GMMFR_ERR_SHAPE;
-  if (k < 128 || k > 65536 || k % 128 != 0) return GMMFR_ERR_SHAPE;
+  if (k < 32 || k > 65536 || k % 32 != 0) return GMMFR_ERR_SHAPE;
   if (n < 32 || n % 32 != 0) return GMMFR_ERR_SHAPE;
   if (n > (int64_t(1) << 24) || m * n >= (int64_t(1) << 40)) return GMMFR_ERR_SHAPE;
-  if (!dims_are(a->pertoken_scale, 3, m, k / 64, 2)) return GMMFR_ERR_SHAPE;
-  if (!dims_are(a->scale, 4, e, n, k / 64, 2)) return GMMFR_ERR_SHAPE;
+  if (!dims_are(a->pertoken_scale, 3, m, (k + 63) / 64, 2)) return GMMFR_ERR_SHAPE;
+  if (!dims_are(a->scale, 4, e, n, (k + 63) / 64, 2)) return GMMFR_ERR_SHAPE;
   if (!dims_are(a->group_list, 1, e)) return GMMFR_ERR_SHAPE;
   if (present(a->logit) && !dims_are(a->logit, 1, m)) return GMMFR_ERR_SHAPE;
   if (present(a->row_index) && !dims_are(a->row_index, 1, m)) return GMMFR_ERR_SHAPE;
@@ -346,7 +347,9 @@ int make_plan(const gmmfr_args* a, const Derived& d, int cu_count, Plan* plan) {
   const int64_t lookup = a->tuning_config_len > 3 ? a->tuning_config[3] : 0;
   plan->scan_reduce = plan->combine == kCombineOrdered &&
                       (lookup == 2 || (lookup == 0 && d.m * d.output_bs <= kScanReduceMax));
-  plan->workspace_bytes = workspace_layout(d.m, d.n, d.output_bs, plan->combine == kCombineOrdered).total;
+  const MxPad mp = mx_pad(d.mx, d.m, d.k, d.n, d.e);
+  plan->workspace_bytes =
+      workspace_layout(d.m, d.n, d.output_bs, plan->combine == kCombineOrdered, mp.a_bytes, mp.b_bytes).total;
   return GMMFR_OK;
 }
 

@@ -53,9 +53,21 @@ struct LaunchArgs {
 // block (GEMM tile-queue counters); the ordered combine adds the rest.
 constexpr size_t kCtrlBytes = 1024;
 struct Workspace {
-  size_t ctrl_off, y_off, counts_off, cursor_off, offsets_off, list_off, total;
+  size_t ctrl_off, mx_sa_off, mx_sb_off, y_off, counts_off, cursor_off, offsets_off, list_off, total;
 };
-Workspace workspace_layout(int64_t m, int64_t n, int64_t output_bs, bool ordered);
+// MxA8W4 with k % 128 != 0: the block scales are copied into the workspace,
+// each row padded to k rounded up to 128 (whole dwords of four block scales).
+struct MxPad {
+  int64_t row_bytes;        // bytes per padded row (0 when no padding)
+  int64_t a_bytes, b_bytes; // padded copies of pertokenScale (m rows) and scale (e*n rows)
+};
+inline MxPad mx_pad(bool mx, int64_t m, int64_t k, int64_t n, int64_t e) {
+  if (!mx || k % 128 == 0) return MxPad{0, 0, 0};
+  const int64_t row = (k + 127) / 128 * 4;
+  return MxPad{row, m * row, e * n * row};
+}
+Workspace workspace_layout(int64_t m, int64_t n, int64_t output_bs, bool ordered, int64_t mx_pad_a = 0,
+                           int64_t mx_pad_b = 0);
 
 struct Plan {
   Combine combine;

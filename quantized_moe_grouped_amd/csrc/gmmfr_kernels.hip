@@ -1232,10 +1232,15 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   const int lane = tid & 63, h = lane >> 5;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int64_t k = p.k, n = p.n;
-  const int ktiles = (int)(k / BK);
+  // MX with k % 64 == 32: the last k-step holds 32 valid k (its other half,
+  // and that block's scale, read as zero products with a unit scale)
+  const bool half_tail = !B8 && (k % BK) != 0;
+  const int ktiles = (int)((k + BK - 1) / BK);
   const bool grp8 = !B8 && k % 512 == 0 && ktiles >= STAGES;  // (always the continuous pipeline)
   static_assert(B8 || STAGES <= 9, "a group's slot is refilled only after the group two before it is read");
-  const int64_t kdw = k / 128;         // MX: scale dwords per row or column (k % 128 == 0)
+  // MX: scale dwords per row or column; when k % 128 != 0 the block scales
+  // come from copies padded to a whole dword (unit scales appended)
+  const int64_t kdw = (k + 127) / 128;
   const bool lo_wave = wave < 2;       // waves that copy the A-scale dwords (rows 0..127)
   const uint32_t* sa_words = (const uint32_t*)p.pertoken;
   const uint32_t* sb_words = (const uint32_t*)p.scale;
@@ -1246,6 +1251,10 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   const uint32_t* sa_base = sa_words;
   const uint32_t* sb_base = sb_words;
   uint32_t a_off[A_INSTR], b_off[B_INSTR], sa_off = 0, sb_off = 0;
+  // half-filled last k-step: per copy, whether this lane's chunk lies in the
+  // missing half (it then fetches the chunk 32 k lower -- in bounds; its
+  // products are cancelled by zeroed A bytes)
+  uint32_t a_tail_mask = 0, b_tail_mask = 0;
   auto set_sources = [&](const TileCoord& c) {
     // The lane and wave indices pass through an opaque point: the per-lane
     // offsets are computed here for each tile, not hoisted out of the tile
@@ -1253,12 +1262,14 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
     int lane = tid & 63, wave = tid >> 6, tid = threadIdx.x;
     asm volatile("" : "+v"(lane), "+v"(wave), "+v"(tid));
     a_base = (const int8_t*)uniform64((int64_t)(p.x1 + c.row0 * k));
+    a_tail_mask = 0;
 #pragma unroll
     for (int q = 0; q < A_INSTR; ++q) {
       const int slot = (q * 4 + wave) * 64 + lane;
       const int r = slot / 4, cpos = slot % 4;
       const int64_t row = min(c.row0 + r, p.m - 1);  // rows past the group: loaded, never stored
       a_off[q] = (uint32_t)((row - c.row0) * k + ((cpos ^ swz_a<BK>(r)) * 16));
+      if ((cpos ^ swz_a<BK>(r)) >= 2) a_tail_mask |= 1u << q;
     }
     if constexpr (BKN) {
       // LDS chunk cpos of stage row r holds global chunk cpos ^ swz_b(r) of
@@ -1274,6 +1285,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
     } else {
       const int64_t colb = B8 ? k : k / 2;  // bytes of one weight column
       b_base = (const int8_t*)uniform64((int64_t)((const int8_t*)p.x2 + ((int64_t)c.g * n + c.col0) * colb));
+      b_tail_mask = 0;
 #pragma unroll
       for (int q = 0; q < B_INSTR; ++q) {
         const int slot = (q * 4 + wave) * 64 + lane;
@@ -1282,6 +1294,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
         const int64_t col = min(c.col0 + r, n - 1);    // columns past n: loaded, never stored
         // fp8 columns are stored and read like A rows (same swizzle)
         b_off[q] = (uint32_t)((col - c.col0) * colb + (B8 ? (cpos ^ swz_a<BK>(r)) : cpos) * 16);
+        if (!B8 && cpos == 1) b_tail_mask |= 1u << q;  // fp4: nibbles of k 32..63 of the step
       }
     }
     sa_base = (const uint32_t*)uniform64((int64_t)(sa_words + c.row0 * kdw));
@@ -1290,15 +1303,22 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
     sb_off = (uint32_t)((min(c.col0 + tid, n - 1) - c.col0) * kdw * 4);
   };
   // copies of k-slice kt (tile-local) into stage st; gs: the slice's running
-  // count (its scale dword goes to slot gs/2 of the ring)
-  auto issue_stage = [&](int st, int kt, int gs) {
+  // count (8-slice groups: slot gs/8); pr: the running count of the scale
+  // dwords issued before this slice's pair (its dword goes to ring slot pr --
+  // counted per pair, not as gs/2, since a tile may hold an odd number of
+  // slices)
+  auto issue_stage = [&](int st, int kt, int gs, int pr) {
+    // the half-filled last step: chunks of its missing half re-fetch the
+    // valid half (every lane still issues its copy, so the waits' counts hold)
+    const bool tail = half_tail && kt == ktiles - 1;  // wave-uniform
 #pragma unroll
     for (int q = 0; q < A_INSTR; ++q)
-      lds_dma16_sv(a_base + (int64_t)kt * BK, a_off[q],
+      lds_dma16_sv(a_base + (int64_t)kt * BK, a_off[q] - ((tail && ((a_tail_mask >> q) & 1u)) ? 32u : 0u),
                    __builtin_amdgcn_readfirstlane(lds_addr(sA + st * A_BYTES + (q * 4 + wave) * 64 * 16)));
 #pragma unroll
     for (int q = 0; q < B_INSTR; ++q)
-      lds_dma16_sv(b_base + (int64_t)kt * (BKN ? (int64_t)BK * n : (int64_t)B_COLB), b_off[q],
+      lds_dma16_sv(b_base + (int64_t)kt * (BKN ? (int64_t)BK * n : (int64_t)B_COLB),
+                   b_off[q] - ((tail && ((b_tail_mask >> q) & 1u)) ? 16u : 0u),
                    __builtin_amdgcn_readfirstlane(lds_addr(sB + st * B_BYTES + (q * 4 + wave) * 64 * 16)));
     if constexpr (!B8) {
       if (grp8) {
@@ -1311,7 +1331,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
                          __builtin_amdgcn_readfirstlane(lds_addr(&sSA[0][0] + (slot * BM + wave * 64) * 4)));
         }
       } else if ((kt & 1) == 0) {  // the dword holding the block scales of slices kt and kt + 1
-        const int slot = (gs >> 1) % SC_SLOTS;
+        const int slot = pr % SC_SLOTS;
         lds_dma4_sv(sb_base + kt / 2, sb_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSB[slot][wave * 64])));
         if (lo_wave)
           lds_dma4_sv(sa_base + kt / 2, sa_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSA[slot][wave * 64])));
@@ -1360,25 +1380,27 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   };
 
   // one k-step on stage st (tile-local k-step kt): fragment reads, 8 MFMAs
-  auto compute = [&](int st, int kt, int gs, v16f (&acc)[FM][FN]) {
+  auto compute = [&](int st, int kt, int gs, int pr, v16f (&acc)[FM][FN]) {
     // scale dword of row or column q: ring slot of this slice's pair, or (8-slice
     // groups) word (kt/2)%4 of the group's slot
     const uint32_t* sca = &sSA[0][0];
     const uint32_t* scb = &sSB[0][0];
     auto sc_word = [&](const uint32_t* base, int rows, int q) -> uint32_t {
       if (grp8) return base[(((gs >> 3) % G8_SLOTS) * rows + q) * 4 + ((kt >> 1) & 3)];
-      return base[((gs >> 1) % SC_SLOTS) * rows + q];
+      return base[(pr % SC_SLOTS) * rows + q];
     };
     const int8_t* a_st = sA + st * A_BYTES;
     const int8_t* b_st = sB + st * B_BYTES;
     const int sel = 8 * (2 * (kt & 1) + h);  // byte of this lane's block in the scale dword
     v8i af[FM];
     int sa[FM], sb[FN];
+    const bool tail = half_tail && kt == ktiles - 1;  // k 32..63 of this step lie past k: zero A there
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = wm * WTM + i * 32 + (lane & 31);
       const v4i lo = *(const LDS_PTR(v4i))(a_st + r * BK + ((h ^ swz_a<BK>(r)) << 4));
-      const v4i hi = *(const LDS_PTR(v4i))(a_st + r * BK + (((2 + h) ^ swz_a<BK>(r)) << 4));
+      v4i hi = *(const LDS_PTR(v4i))(a_st + r * BK + (((2 + h) ^ swz_a<BK>(r)) << 4));
+      if (tail) hi = v4i{0, 0, 0, 0};
       af[i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       sa[i] = B8 ? 127 : (int)(sc_word(sca, BM, r) >> sel);
     }
@@ -1511,9 +1533,15 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       int pb = 0;
       dma_rows(cur, pb);
       set_sources(cur);
+      // running counts of slices issued and consumed (gfill, gstep) and of
+      // scale pairs issued and consumed (pfill, puse: a pair starts at each
+      // even tile-local slice)
+      int gfill = 0, gstep = 0, pfill = 0, puse = 0;
 #pragma unroll
-      for (int st = 0; st < STAGES - 1; ++st) issue_stage(st, st, st);
-      int gfill = STAGES - 1, gstep = 0;  // running counts of slices issued and consumed
+      for (int st = 0; st < STAGES - 1; ++st) {
+        if ((st & 1) == 0) ++pfill;
+        issue_stage(st, st, gfill++, pfill - 1);
+      }
       int stage = 0;
       bool prev_full = false;
       // After an ordered full-tile epilogue, its FM*FN*16 stores (issued
@@ -1549,9 +1577,12 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
             set_sources(nxt);
             if (t_nxt >= 0) dma_rows(nxt, pb ^ 1);
           }
-          issue_stage(stage == 0 ? STAGES - 1 : stage - 1, fill < ktiles ? fill : fill - ktiles, gfill);
+          const int fkt = fill < ktiles ? fill : fill - ktiles;
+          if ((fkt & 1) == 0) ++pfill;
+          issue_stage(stage == 0 ? STAGES - 1 : stage - 1, fkt, gfill, pfill - 1);
           ++gfill;
-          compute(stage, kt, gstep, acc);
+          if ((kt & 1) == 0) ++puse;
+          compute(stage, kt, gstep, puse - 1, acc);
           ++gstep;
           stage = stage + 1 == STAGES ? 0 : stage + 1;
         }
@@ -1578,7 +1609,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       set_sources(c);
 #pragma unroll
       for (int st = 0; st < STAGES - 1; ++st)
-        if (st < ktiles) issue_stage(st, st, st);
+        if (st < ktiles) issue_stage(st, st, st, st / 2);
       v16f acc[FM][FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -1594,14 +1625,29 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
           wait_vmcnt<0>();
         }
         lds_barrier();
-        if (kt + STAGES - 1 < ktiles) issue_stage((kt + STAGES - 1) % STAGES, kt + STAGES - 1, kt + STAGES - 1);
-        compute(kt % STAGES, kt, kt, acc);
+        if (kt + STAGES - 1 < ktiles)
+          issue_stage((kt + STAGES - 1) % STAGES, kt + STAGES - 1, kt + STAGES - 1, (kt + STAGES - 1) / 2);
+        compute(kt % STAGES, kt, kt, kt / 2, acc);
       }
       __builtin_amdgcn_s_setprio(0);
       epilogue(c, 0, acc);
     }
   }
   wait_vmcnt<0>();  // no copy in flight when the workgroup ends
+}
+
+// ---------------------------------------------------------------------------
+// MX block scales with k % 128 != 0: each row of `valid` scale bytes (k/32
+// blocks) is copied into a row of `dst_row` bytes (a whole number of dwords),
+// the bytes past the valid blocks set to 127 (a unit scale).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void mx_pad_scales_kernel(const uint8_t* src, uint8_t* dst, int64_t rows,
+                                                                 int64_t src_row, int64_t dst_row, int64_t valid) {
+  const int64_t total = rows * dst_row;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = i / dst_row, c = i % dst_row;
+    dst[i] = c < valid ? src[r * src_row + c] : (uint8_t)127;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1985,11 +2031,16 @@ const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Workspace workspace_layout(int64_t m, int64_t n, int64_t output_bs, bool ordered) {
+Workspace workspace_layout(int64_t m, int64_t n, int64_t output_bs, bool ordered, int64_t mx_pad_a,
+                           int64_t mx_pad_b) {
   Workspace w{};
   size_t off = 0;
   w.ctrl_off = off;
   off += kCtrlBytes;
+  w.mx_sa_off = off;
+  off += align256((size_t)mx_pad_a);
+  w.mx_sb_off = off;
+  off += align256((size_t)mx_pad_b);
   if (ordered) {
     w.y_off = off;
     off += align256((size_t)m * (size_t)n * sizeof(float));
@@ -2062,9 +2113,24 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
   kp.row_index_i32 = a.row_index_i32;
   kp.n_tiles_n = (int32_t)((a.n + ts.bn - 1) / ts.bn);
   kp.combine = plan.combine;
-  const Workspace w = workspace_layout(a.m, a.n, a.output_bs, plan.combine == kCombineOrdered);
+  const MxPad mp = mx_pad(a.mx, a.m, a.k, a.n, a.e);
+  const Workspace w = workspace_layout(a.m, a.n, a.output_bs, plan.combine == kCombineOrdered, mp.a_bytes, mp.b_bytes);
   char* ws = (char*)workspace;
   kp.tile_ctr = (int32_t*)(ws + w.ctrl_off);
+  if (mp.a_bytes > 0 && a.m > 0) {
+    // block scales padded to whole dwords per row and column (unit scales appended)
+    const int64_t src_row = 2 * ((a.k + 63) / 64), valid = a.k / 32;
+    uint8_t* sa = (uint8_t*)(ws + w.mx_sa_off);
+    uint8_t* sb = (uint8_t*)(ws + w.mx_sb_off);
+    const int ga = (int)std::min<int64_t>(4096, (mp.a_bytes + kThreads - 1) / kThreads);
+    const int gb = (int)std::min<int64_t>(4096, (mp.b_bytes + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(mx_pad_scales_kernel, dim3(ga), dim3(kThreads), 0, s, (const uint8_t*)a.pertoken, sa, a.m,
+                       src_row, mp.row_bytes, valid);
+    hipLaunchKernelGGL(mx_pad_scales_kernel, dim3(gb), dim3(kThreads), 0, s, (const uint8_t*)a.scale, sb,
+                       (int64_t)a.e * a.n, src_row, mp.row_bytes, valid);
+    kp.pertoken = (const float*)sa;
+    kp.scale = sb;
+  }
 
   const int64_t n4 = a.n / 4;
   // the tile-by-tile loop of the int8/int4 kernel takes its tiles from

@@ -326,8 +326,8 @@ def mx_problem(seed: int, m: int, k: int, n: int, e: int, *, group_list_type: in
                output_bs: Optional[int] = None, empty_frac: float = 0.25, uncovered: int = 0) -> Problem:
     """A random MxA8W4 problem (FP8 activations, FP4 weights given (e,n,k), E8M0
     block scales per 32 k) for parity and invariant tests."""
-    if k % 64:
-        raise ValueError("k must be a multiple of 64")
+    if k % 32:
+        raise ValueError("k must be a multiple of 32")
     rng = np.random.default_rng(seed)
     covered = m - uncovered
     w = rng.uniform(0.2, 1.0, size=e) * (rng.uniform(size=e) >= empty_frac)
@@ -340,8 +340,10 @@ def mx_problem(seed: int, m: int, k: int, n: int, e: int, *, group_list_type: in
     logit = rng.uniform(0.0, 1.0, size=m).astype(np.float32) if with_logit else None
     x1 = _fp8_codes(rng, (m, k))
     x2 = _fp4_pairs(rng, (e, n, k // 2))
-    pts = _e8m0(rng, (m, k // 64, 2))
-    scale = _e8m0(rng, (e, n, k // 64, 2))
+    # one E8M0 per 32 k, in pairs: (.., ceil(k/64), 2); with k % 64 == 32 the
+    # last pair's second byte is no block's scale (drawn like the others)
+    pts = _e8m0(rng, (m, (k + 63) // 64, 2))
+    scale = _e8m0(rng, (e, n, (k + 63) // 64, 2))
     shared = None
     if bsdp > 0:
         shared = f32_to_bf16_bits(rng.standard_normal((bsdp, n)).astype(np.float32) * 64.0)

@@ -324,8 +324,21 @@ MX_CASES = [
     ("mx_row_index_i32", _mx_args, dict(row_index=_fake(B.DT_INT32, 512)), B.ERR_DTYPE),
     ("mx_untransposed", _mx_args, dict(transpose_x2=0), B.ERR_ATTR),
     ("mx_acc_dump", _mx_args, dict(acc_out=_fake(B.DT_INT32, 512, 7168)), B.ERR_UNSUPPORTED),
-    ("mx_k_not_mult_128", _mx_args, dict(x1=_fake(B.DT_FLOAT8_E4M3FN, 512, 2112),
-                                         x2=_fake(B.DT_FLOAT4_E2M1X2, 8, 7168, 1056)), B.ERR_SHAPE),
+    # k a multiple of 32 (Atlas 350 MxA8W4 notes), scales (.., ceil(k/64), 2)
+    ("mx_k_mult_64_not_128", _mx_args, dict(x1=_fake(B.DT_FLOAT8_E4M3FN, 512, 2112),
+                                            x2=_fake(B.DT_FLOAT4_E2M1X2, 8, 7168, 1056),
+                                            scale=_fake(B.DT_FLOAT8_E8M0, 8, 7168, 33, 2),
+                                            pertoken_scale=_fake(B.DT_FLOAT8_E8M0, 512, 33, 2)), B.OK),
+    ("mx_k_mult_32", _mx_args, dict(x1=_fake(B.DT_FLOAT8_E4M3FN, 512, 96), x2=_fake(B.DT_FLOAT4_E2M1X2, 8, 7168, 48),
+                                    scale=_fake(B.DT_FLOAT8_E8M0, 8, 7168, 2, 2),
+                                    pertoken_scale=_fake(B.DT_FLOAT8_E8M0, 512, 2, 2)), B.OK),
+    ("mx_k_mult_32_floor_scales", _mx_args, dict(x1=_fake(B.DT_FLOAT8_E4M3FN, 512, 96),
+                                                 x2=_fake(B.DT_FLOAT4_E2M1X2, 8, 7168, 48),
+                                                 scale=_fake(B.DT_FLOAT8_E8M0, 8, 7168, 1, 2),
+                                                 pertoken_scale=_fake(B.DT_FLOAT8_E8M0, 512, 1, 2)), B.ERR_SHAPE),
+    ("mx_k_not_mult_32", _mx_args, dict(x1=_fake(B.DT_FLOAT8_E4M3FN, 512, 80), x2=_fake(B.DT_FLOAT4_E2M1X2, 8, 7168, 40),
+                                        scale=_fake(B.DT_FLOAT8_E8M0, 8, 7168, 2, 2),
+                                        pertoken_scale=_fake(B.DT_FLOAT8_E8M0, 512, 2, 2)), B.ERR_SHAPE),
     ("mx_scale_shape", _mx_args, dict(scale=_fake(B.DT_FLOAT8_E8M0, 8, 7168, 64)), B.ERR_SHAPE),
     ("fp8_ok", _fp8_args, {}, B.OK),
     ("fp8_per_tensor_pertoken", _fp8_args, dict(pertoken_scale=_fake(B.DT_FLOAT32, 1)), B.OK),

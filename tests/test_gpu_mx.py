@@ -28,6 +28,16 @@ CASES = {
     "k_512_many_empty": dict(seed=10, m=900, k=512, n=256, e=40, empty_frac=0.7, output_bs=300),
     # one group past 512 plus 128: the dword-per-pair path
     "k_640_dword_path": dict(seed=9, m=600, k=640, n=288, e=3, output_bs=300),
+    # k a multiple of 32 or 64 but not of 128 (Atlas 350 MxA8W4 notes: k % 32
+    # == 0): block scales padded to whole dwords in the workspace; k % 64 ==
+    # 32 leaves the last k-step half filled (an odd count of k-steps also
+    # shifts the scale ring's pairing between tiles)
+    "k_96_half_step": dict(seed=20, m=300, k=96, n=288, e=3, output_bs=120, bsdp=20, shared_offset=50),
+    "k_160_half_step": dict(seed=21, m=500, k=160, n=544, e=4, output_bs=200, group_list_type=1),
+    "k_224_half_step_continuous": dict(seed=22, m=700, k=224, n=512, e=3, output_bs=300, uncovered=7),
+    "k_192_odd_steps": dict(seed=23, m=600, k=192, n=256, e=4, output_bs=250, empty_frac=0.3),
+    "k_320_odd_steps_continuous": dict(seed=24, m=900, k=320, n=288, e=3, output_bs=400, bsdp=30, shared_offset=3),
+    "k_32_single_half_step": dict(seed=25, m=200, k=32, n=64, e=2, output_bs=80),
 }
 
 
@@ -155,7 +165,8 @@ def test_fp8_workload_sampled_rows():
 # ---------------------------------------------------------------- many tiles per workgroup
 
 GRID_CAPPED = ["ragged_shared", "counts_uncovered", "long_k", "k_512_one_scale_group", "k_1536_many_tiles",
-               "k_640_dword_path", "many_empty"]
+               "k_640_dword_path", "many_empty", "k_224_half_step_continuous", "k_320_odd_steps_continuous",
+               "k_160_half_step"]
 
 
 @pytest.mark.parametrize("name", GRID_CAPPED, ids=GRID_CAPPED)

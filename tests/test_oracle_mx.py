@@ -293,3 +293,56 @@ def test_fp8_untransposed_weights_equal_transposed():
     wrong.x2_transposed = True
     wrong.x2 = np.ascontiguousarray(q.x2.reshape(p.e, p.n, p.k))  # (e,k,n) bytes read as (e,n,k)
     assert not np.array_equal(MX.run(wrong)[0], op)
+
+
+# ---------------------------------------------------------------- k % 64 == 32 ("aclnnGroupedMatmulFinalize
+# RoutingWeightNzV2", Atlas 350 MxA8W4 notes: k % 32 == 0, scales of shape (.., ceil(k/64), 2))
+
+@pytest.mark.parametrize("k", [32, 96, 160])
+def test_half_pair_k_brute_force_matches_oracle(k):
+    """k a multiple of 32 but not of 64: the pure-Python brute force (which
+    indexes scale byte b of block b directly) agrees with the oracle."""
+    p = W.mx_problem(40 + k, 7, k, 32, 2, output_bs=5)
+    assert p.pertoken_scale.shape == (7, (k + 63) // 64, 2)
+    out, bound, acc = MX.run(p)
+    cov = np.zeros(p.m, dtype=bool)
+    s, e = MX.group_ranges(p)
+    for a, b in zip(s, e):
+        cov[a:b] = True
+    assert np.allclose(acc[cov], MX.brute(p)[cov], rtol=1e-12, atol=0.0)
+
+
+def test_half_pair_scale_byte_is_not_read():
+    """With k % 64 == 32 the second byte of each row's (and column's) last
+    scale pair stands for no block: changing it (to 0, or 255, the NaN code)
+    leaves every output as it was."""
+    p = W.mx_problem(50, 40, 96, 64, 3, output_bs=20, bsdp=5, shared_offset=3)
+    ref, _, _ = MX.run(p)
+    for v in (0, 255, 131):
+        q = copy.deepcopy(p)
+        q.pertoken_scale[:, -1, 1] = v
+        q.scale[:, :, -1, 1] = v
+        got, _, _ = MX.run(q)
+        assert np.array_equal(got, ref)
+
+
+def test_half_pair_equals_zero_padded_k():
+    """A k = 96 problem equals the k = 128 problem whose k 96..127 hold zero
+    activations and weights (any scales there): the closed form of the
+    shortened sum."""
+    p = W.mx_problem(51, 30, 96, 64, 2, output_bs=12)
+    q = copy.deepcopy(p)
+    q.k = 128
+    q.x1 = np.zeros((p.m, 128), dtype=np.uint8)
+    q.x1[:, :96] = p.x1
+    q.x2 = np.zeros((p.e, p.n, 64), dtype=np.uint8)
+    q.x2[:, :, :48] = p.x2
+    pts = np.full((p.m, 4), 140, dtype=np.uint8)          # blocks 0..3; block 3 covers k 96..127
+    pts[:, :3] = p.pertoken_scale.reshape(p.m, 4)[:, :3]
+    q.pertoken_scale = pts.reshape(p.m, 2, 2)
+    sc = np.full((p.e, p.n, 4), 121, dtype=np.uint8)
+    sc[:, :, :3] = p.scale.reshape(p.e, p.n, 4)[:, :, :3]
+    q.scale = sc.reshape(p.e, p.n, 2, 2)
+    a, _, _ = MX.run(p)
+    b, _, _ = MX.run(q)
+    assert np.array_equal(a, b)
