@@ -313,21 +313,40 @@ TileId choose_tile(const gmmfr_args* a, const Derived& d) {
   return kTile32x256;
 }
 
+// Rates measured on MI355X for the cost model below (per-workload table of
+// both combine modes from one box, in the design notes): fp32 atomics from the
+// epilogue retire at about 1.3 TB/s of payload; the grouped GEMM runs at about
+// 1.7 POP/s (int8, FP8 and MX) or 1.55 POP/s (int4 weights), or streams its
+// weights at about 5 TB/s when each expert has few rows; the ordered reduce
+// moves its bytes at about 5.4 TB/s.
+constexpr double kAtomicBytesPerSec = 1.3e12;
+constexpr double kGemmOpsPerSec = 1.7e15, kGemmOpsPerSecInt4 = 1.55e15;
+constexpr double kWeightBytesPerSec = 5.0e12;
+constexpr double kReduceBytesPerSec = 5.4e12;
+constexpr double kOrderedLaunchScan = 8e-6, kOrderedLaunchBuckets = 25e-6;  // extra launches and their gaps
+
+bool scan_lookup(const gmmfr_args* a, const Derived& d) {
+  const int64_t lookup = a->tuning_config_len > 3 ? a->tuning_config[3] : 0;
+  return lookup == 2 || (lookup == 0 && d.m * d.output_bs <= kScanReduceMax);
+}
+
 Combine choose_combine(const gmmfr_args* a, const Derived& d) {
   if (a->deterministic == 1 || a->combine == GMMFR_COMBINE_ORDERED) return kCombineOrdered;
   if (a->combine == GMMFR_COMBINE_ATOMIC) return kCombineAtomic;
-  // fp32 atomics retire at a fixed rate (about 1.3 TB/s of payload on this
-  // part) and slow the GEMM once they exceed about half of its own time; the
-  // ordered path costs a y round trip, the reduction and some 30 us of extra
-  // launches.  The GEMM's time is the larger of its MFMA time and its
-  // weight-streaming time, at measured rates, estimated from the shapes alone
-  // so the plan never depends on device data.
+  // From the shapes alone (the plan never reads device data).  Atomics
+  // overlap the GEMM but slow it once they take more than about half of its
+  // own time; the ordered path adds the reduce (contributions read once,
+  // the output written once, sharedInput read) and its launches.
   const double contributions = (double)d.m * (double)d.n;
-  const double t_atomic = contributions * 4.0 / 1.3e12;
-  const double t_mfma = 2.0 * (double)d.m * (double)d.k * (double)d.n / (d.int4 ? 0.93e15 : 1.6e15);
+  const double t_atomic = contributions * 4.0 / kAtomicBytesPerSec;
+  const double t_mfma = 2.0 * (double)d.m * (double)d.k * (double)d.n / (d.int4 ? kGemmOpsPerSecInt4 : kGemmOpsPerSec);
   const double experts = (double)std::min<int64_t>(d.e, std::max<int64_t>(d.m, 1));
-  const double t_weights = experts * (double)d.k * (double)d.n * (d.int4 ? 0.5 : 1.0) / 5.0e12;
-  return t_atomic < 0.5 * std::max(t_mfma, t_weights) + 30e-6 ? kCombineAtomic : kCombineOrdered;
+  const double t_weights = experts * (double)d.k * (double)d.n * (d.int4 ? 0.5 : 1.0) / kWeightBytesPerSec;
+  const double t_gemm = std::max(t_mfma, t_weights);
+  const double reduce_bytes = contributions * 4.0 + (double)d.output_bs * (double)d.n * 4.0 + (double)d.bsdp * (double)d.n * 2.0;
+  const double t_ordered_extra =
+      reduce_bytes / kReduceBytesPerSec + (scan_lookup(a, d) ? kOrderedLaunchScan : kOrderedLaunchBuckets);
+  return t_atomic <= 0.5 * t_gemm + t_ordered_extra ? kCombineAtomic : kCombineOrdered;
 }
 
 int make_plan(const gmmfr_args* a, const Derived& d, int cu_count, Plan* plan) {
@@ -344,9 +363,7 @@ int make_plan(const gmmfr_args* a, const Derived& d, int cu_count, Plan* plan) {
   // run many tiles in a row) is taken as given, rounded or not.
   if (a->tuning_config_len > 2 && a->tuning_config[2] > 0) grid = std::min(grid, a->tuning_config[2]);
   plan->grid = d.m > 0 ? (int32_t)grid : 0;
-  const int64_t lookup = a->tuning_config_len > 3 ? a->tuning_config[3] : 0;
-  plan->scan_reduce = plan->combine == kCombineOrdered &&
-                      (lookup == 2 || (lookup == 0 && d.m * d.output_bs <= kScanReduceMax));
+  plan->scan_reduce = plan->combine == kCombineOrdered && scan_lookup(a, d);
   const MxPad mp = mx_pad(d.mx, d.m, d.k, d.n, d.e);
   plan->workspace_bytes =
       workspace_layout(d.m, d.n, d.output_bs, plan->combine == kCombineOrdered, mp.a_bytes, mp.b_bytes).total;
