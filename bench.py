@@ -470,6 +470,28 @@ def main():
     print(f"[bench] step {ms_step:.4f} ms, gemm kernel {gemm_avg:.4f} ms "
           f"(min {min(gemm_ms):.4f}, max {max(gemm_ms):.4f})", file=sys.stderr, flush=True)
 
+    # the same calls with cold caches: before each, 1 GiB is written (the L2s
+    # and the 256 MB MALL evicted); events around the call alone
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    ev_c = [(hip.event(), hip.event(), hip.event(), hip.event()) for _ in range(args.steps)]
+    for s, (a, g0, g1, b) in enumerate(ev_c):
+        flush.fill_(float(s))
+        hip.record(a, stream)
+        st = B.lib().gmm_finalize_routing_profiled(ctypes.byref(cargs), ctypes.c_void_p(ws.data_ptr()),
+                                                    ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream), g0, g1)
+        if st != 0:
+            raise B.GmmfrError(st, "gmm_finalize_routing_profiled")
+        hip.record(b, stream)
+    torch.cuda.synchronize()
+    cold_step = sorted(hip.elapsed_ms(a, b) for a, _, _, b in ev_c)
+    cold_gemm = sorted(hip.elapsed_ms(g0, g1) for _, g0, g1, _ in ev_c)
+    del flush
+    cold = {"ms_per_step_median": round(cold_step[len(cold_step) // 2], 5),
+            "gemm_ms_median": round(cold_gemm[len(cold_gemm) // 2], 5), "calls": args.steps,
+            "flush": "1 GiB written before each call (L2s and MALL evicted); events around the call only"}
+    print(f"[bench] cold: step {cold['ms_per_step_median']:.4f} ms, gemm kernel {cold['gemm_ms_median']:.4f} ms "
+          f"(medians)", file=sys.stderr, flush=True)
+
     ops = 2.0 * p.covered_rows * p.k * p.n
     tops = ops / (ms_step * 1e-3) / 1e12
     gemm_tops = ops / (gemm_avg * 1e-3) / 1e12
@@ -513,6 +535,7 @@ def main():
                    "path_roofline_frac": round(t_roof_ms / ms_step, 4)},
         "roofline": roofline,
         "cpu_baseline": None,
+        "cold": cold,
     }
     if args.timing_detail:
         res["timing"] = timing_detail(p, dict(x1=x1, x2=x2, gl=gl, out=out, scale=scale, pts=pts, logit=logit, ri=ri,

@@ -206,6 +206,8 @@ def _torch_stream(stream):
         return torch.cuda.current_stream()
     if isinstance(stream, torch.cuda.Stream):
         return stream
+    if int(stream) == 0:  # the null stream
+        return torch.cuda.default_stream()
     return torch.cuda.ExternalStream(int(stream))
 
 
