@@ -197,6 +197,22 @@ def test_many_destinations_scan_in_chunks():
     _check_full(p, hints=(None, (0, 0, 0, 2)))
 
 
+@pytest.mark.parametrize("ri", ["int64", "int32", "identity", "long"])
+def test_scan_lookup_over_several_chunks(ri):
+    """The ordered combine's rowIndex scan (4096 rows per pass) over several
+    passes, with a covered count that is not a multiple of 16 (the scalar
+    tail) and every rowIndex form, and a destination receiving 3000 rows (the
+    long-segment fold); the bucket index on the same inputs."""
+    kw = dict(row_index_dtype=np.int32) if ri == "int32" else {}
+    if ri == "identity":
+        kw = dict(with_row_index=False)
+    p = W.random_problem(66, 9000, 64, 64, 3, output_bs=9000 if ri == "identity" else 700, uncovered=37,
+                         bsdp=50, shared_offset=10, **kw)
+    if ri == "long":
+        p.row_index[::3] = 5
+    _check_full(p, hints=((0, 0, 0, 2), (0, 0, 0, 1)))
+
+
 def test_extreme_accumulators_round_like_the_oracle():
     """x1 = x2 = -128, k = 2048: acc = 2^25 (above 2^24); plus mixed
     magnitudes whose int32 -> fp32 conversion must round to nearest even."""
