@@ -377,7 +377,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path runs on one GPU's share; see the design notes for sharding).", file=sys.stderr)
+              "(the path runs on one GPU's share: expert-parallel ranks would each run it on their local "
+              "experts' rows between two all-to-all exchanges).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -512,9 +513,9 @@ def main():
                     "unit": "TFLOP/s" if floating else "TOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                     "launch_ms": round(gemm_avg, 5), "traffic": traffic_from_profiles(kname, p.name)}
     res = {
-        "metric": "int8 TOPS (and % of MFMA/HBM roofline) for GMM+finalize-routing at 1 GPU",
+        "metric": ("FP8 TFLOPS" if floating else "int8 TOPS") + " (and % of MFMA/HBM roofline) for GMM+finalize-routing at 1 GPU",
         "value": round(tops, 2),
-        "unit": "TOPS",
+        "unit": "TFLOPS" if floating else "TOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

@@ -313,9 +313,9 @@ TileId choose_tile(const gmmfr_args* a, const Derived& d) {
   return kTile32x256;
 }
 
-// Rates measured on MI355X for the cost model below (per-workload table of
-// both combine modes from one box, in the design notes): fp32 atomics from the
-// epilogue retire at about 1.3 TB/s of payload; the grouped GEMM runs at about
+// Rates measured on MI355X for the cost model below (both combine modes timed
+// on every named workload on one box): fp32 atomics from the epilogue retire
+// at about 1.3 TB/s of payload; the grouped GEMM runs at about
 // 1.7 POP/s (int8, FP8 and MX) or 1.55 POP/s (int4 weights), or streams its
 // weights at about 5 TB/s when each expert has few rows; the ordered reduce
 // moves its bytes at about 5.4 TB/s.
