@@ -12,7 +12,7 @@ enum Combine : int32_t { kCombineAtomic = 1, kCombineOrdered = 2 };
 
 // GEMM tile variants compiled into the library.
 enum TileId : int32_t {
-  kTile256x256 = 0,   // BM=256 BN=256, 2x2 waves of 128x128, 3 stages, 1 workgroup per CU
+  kTile256x256 = 0,   // BM=256 BN=256, 4x2 waves of 64x128 (512 threads), 4 stages, 1 workgroup per CU
   kTile128x256 = 1,   // BM=128 BN=256, 2x2 waves of 64x128, 3 stages
   kTile64x256 = 2,    // BM=64  BN=256, 1x4 waves of 64x64, 3 stages
   kTile32x256 = 3,    // BM=32  BN=256, 1x4 waves of 32x64, 3 stages
@@ -85,8 +85,9 @@ constexpr int64_t kScanReduceMax = int64_t(1) << 23;
 // gemm_events: optional {start, stop} hipEvent_t recorded around the GEMM.
 int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* stream, void* const* gemm_events);
 
-// Workgroups per CU the GEMM variant is compiled for.
+// Workgroups per CU the GEMM variant is compiled for, and its LDS stages.
 int tile_occupancy(TileId id);
+int tile_stages(TileId id);
 // Whether the GEMM runs the continuous copy pipeline (int8 weights, tiles of
 // at least 64 rows and at least `stages` k-steps per tile) rather than the
 // tile-by-tile loop.

@@ -107,14 +107,15 @@ __device__ __forceinline__ int64_t dest_row(const KParams& p, int64_t i) {
 // non-decreasing (running max for type 0, running sum for type 1) and capped
 // at m, so a broken list never leads outside x1.
 // ---------------------------------------------------------------------------
-__device__ void block_scan_i64(int64_t (&v)[kMaxExperts / kThreads], bool use_max, int64_t* s_scan) {
-  constexpr int PER = kMaxExperts / kThreads;
+template <int NT>
+__device__ void block_scan_i64(int64_t (&v)[kMaxExperts / NT], bool use_max, int64_t* s_scan) {
+  constexpr int PER = kMaxExperts / NT;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int q = 1; q < PER; ++q) v[q] = use_max ? max(v[q - 1], v[q]) : v[q - 1] + v[q];
   s_scan[tid] = v[PER - 1];
   __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
+  for (int off = 1; off < NT; off <<= 1) {
     int64_t t = tid >= off ? s_scan[tid - off] : 0;
     __syncthreads();
     s_scan[tid] = use_max ? max(s_scan[tid], t) : s_scan[tid] + t;
@@ -128,8 +129,9 @@ __device__ void block_scan_i64(int64_t (&v)[kMaxExperts / kThreads], bool use_ma
 
 // s_ends[g] = end row of expert g; s_tile_pre[g] = first tile of expert g,
 // s_tile_pre[e] = total tiles.
+template <int NT = kThreads>
 __device__ void build_group_table(const KParams& p, int bm, int32_t* s_ends, int32_t* s_tile_pre, int64_t* s_scan) {
-  constexpr int PER = kMaxExperts / kThreads;
+  constexpr int PER = kMaxExperts / NT;
   const int tid = threadIdx.x;
   int64_t v[PER];
 #pragma unroll
@@ -138,7 +140,7 @@ __device__ void build_group_table(const KParams& p, int bm, int32_t* s_ends, int
     int64_t x = g < p.e ? p.group_list[g] : 0;
     v[q] = min(max(x, (int64_t)0), p.m);
   }
-  block_scan_i64(v, p.group_list_type == 0, s_scan);
+  block_scan_i64<NT>(v, p.group_list_type == 0, s_scan);
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
     const int g = tid * PER + q;
@@ -155,7 +157,7 @@ __device__ void build_group_table(const KParams& p, int bm, int32_t* s_ends, int
     }
     v[q] = t;
   }
-  block_scan_i64(v, false, s_scan);
+  block_scan_i64<NT>(v, false, s_scan);
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
     const int g = tid * PER + q;
@@ -317,8 +319,8 @@ __device__ __forceinline__ TileCoord tile_coord(const KParams& p, const int32_t*
 // checked by the host) over the tile-by-tile loop.  TRANSB: int8 weights
 // given transposed, (e,n,k) with k contiguous.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int OCC, bool INT4, int COMBINE, bool CONT,
-          bool TRANSB>
-__global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
+          bool TRANSB, int NT = kThreads>
+__global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int KK = BK / 32;
@@ -335,11 +337,11 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   constexpr int CPR_A = BK / 16, CPR_B = B_ROW / 16;
   constexpr int A_BYTES = BM * BK, B_BYTES = B_LROWS * B_ROW;
   constexpr int A_SLOTS = BM * CPR_A, B_SLOTS = B_LROWS * CPR_B;
-  constexpr int NWAVES = kThreads / 64;
-  constexpr int A_INSTR = (A_SLOTS + kThreads - 1) / kThreads;    // per thread (whole waves may idle)
-  constexpr int B_INSTR = (B_SLOTS + kThreads - 1) / kThreads;
+  constexpr int NWAVES = NT / 64;
+  constexpr int A_INSTR = (A_SLOTS + NT - 1) / NT;    // per thread (whole waves may idle)
+  constexpr int B_INSTR = (B_SLOTS + NT - 1) / NT;
   constexpr int B4_CHUNKS = BK * (BN / 32);                       // 16-byte packed chunks
-  constexpr int B4_PER = (B4_CHUNKS + kThreads - 1) / kThreads;
+  constexpr int B4_PER = (B4_CHUNKS + NT - 1) / NT;
   // vector-memory ops one thread issues per stage (DMA and int4 register
   // loads).  When A_SLOTS is not a multiple of the block, the last A copy is
   // issued by the first waves only; those waves wait with the larger count.
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   int32_t* s_ends = s_dyn;
   int32_t* s_tile_pre = s_dyn + p.e;
   int64_t* s_scan = (int64_t*)sA;  // scan scratch, used before the first copy into sA
-  static_assert(STAGES * A_BYTES >= kThreads * 8, "scan scratch fits in the A stages");
+  static_assert(STAGES * A_BYTES >= NT * 8, "scan scratch fits in the A stages");
   // Per-row epilogue inputs of a tile (pertokenScale, logit, rowIndex) and
   // per-column scales, as raw words of the caller's arrays, double-buffered
   // across consecutive tiles: rowIndex takes two words per row when int64,
@@ -379,11 +381,11 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   const bool pts_rows = p.pertoken && !p.pertoken_scalar;
   if (!pts_rows) {
     const float v = p.pertoken ? p.pertoken[0] : 1.0f;
-    for (int i = threadIdx.x; i < 2 * BM; i += kThreads) (&s_pts[0][0])[i] = v;
+    for (int i = threadIdx.x; i < 2 * BM; i += NT) (&s_pts[0][0])[i] = v;
   }
   if (!p.logit)
-    for (int i = threadIdx.x; i < 2 * BM; i += kThreads) (&s_logit[0][0])[i] = 1.0f;
-  build_group_table(p, BM, s_ends, s_tile_pre, s_scan);
+    for (int i = threadIdx.x; i < 2 * BM; i += NT) (&s_logit[0][0])[i] = 1.0f;
+  build_group_table<NT>(p, BM, s_ends, s_tile_pre, s_scan);
   const int total_tiles = s_tile_pre[p.e];
 
   const int tid = threadIdx.x;
@@ -481,7 +483,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     const int64_t k0 = (int64_t)kt * BK;
 #pragma unroll
     for (int q = 0; q < B4_PER; ++q) {
-      const int s = q * kThreads + tid;
+      const int s = q * NT + tid;
       if (s < B4_CHUNKS) {
         const int r = s / (BN / 32), cc = s % (BN / 32);
         const int64_t col = min(b4_col0 + cc * 32, n - 32);
@@ -492,7 +494,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
   auto store_b4 = [&](int sc) {
 #pragma unroll
     for (int q = 0; q < B4_PER; ++q) {
-      const int s = q * kThreads + tid;
+      const int s = q * NT + tid;
       if (s < B4_CHUNKS) {
         const int r = s / (BN / 32), cc = s % (BN / 32);
         uint4 c0, c1;
@@ -551,7 +553,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
     }
     const uint32_t* ri = (const uint32_t*)p.row_index;
     if (tid < ridx_words) fr_ridx0 = ri[row_word_src(c, tid, ridx_words / BM)];
-    if (tid + kThreads < ridx_words) fr_ridx1 = ri[row_word_src(c, tid + kThreads, ridx_words / BM)];
+    if (tid + NT < ridx_words) fr_ridx1 = ri[row_word_src(c, tid + NT, ridx_words / BM)];
     if (tid < scale_words) fr_scale = ((const uint32_t*)p.scale)[scale_word_src(c, tid)];
   };
   auto store_rows = [&](int pb) {
@@ -560,7 +562,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       s_logit[pb][tid] = __uint_as_float(fr_logit);
     }
     if (tid < ridx_words) s_ridx[pb][tid] = fr_ridx0;
-    if (tid + kThreads < ridx_words) s_ridx[pb][tid + kThreads] = fr_ridx1;
+    if (tid + NT < ridx_words) s_ridx[pb][tid + NT] = fr_ridx1;
     if (tid < scale_words) s_scale[pb][tid] = fr_scale;
   };
   // Copy path (the continuous pipeline): straight to LDS, one word per lane,
@@ -572,11 +574,11 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
       const int q = wave * 64 + lane;
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
-        const int qq = q + pass * kThreads;
-        if (pass * kThreads + wave * 64 < nwords) {  // wave-uniform
+        const int qq = q + pass * NT;
+        if (pass * NT + wave * 64 < nwords) {  // wave-uniform
           if (qq < nwords)
             lds_dma4_sv(base, (uint32_t)word_off(qq) * 4u,
-                        __builtin_amdgcn_readfirstlane(lds_addr(dst + pass * kThreads + wave * 64)));
+                        __builtin_amdgcn_readfirstlane(lds_addr(dst + pass * NT + wave * 64)));
         }
       }
     };
@@ -598,7 +600,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gmm_kernel(KParams p) {
               [&](int q) { return (int)(min(c.col0 + q, n - 1) - c.col0); });
     }
   };
-  static_assert(BM <= kThreads && BN <= kThreads && 2 * BM <= 2 * kThreads, "one pass per tile row and column");
+  static_assert(BM <= NT && BN <= NT && 2 * BM <= 2 * NT, "one pass per tile row and column");
 
   // Fragment reads.  Read item r of a k-substep: A fragments first, then B.
   auto read_a = [&](int sc, int kk, int i, v4i& dst) {
@@ -1998,6 +2000,8 @@ TileShape tile_shape(TileId id) {
 
 int tile_occupancy(TileId id) { return id == kTile256x256 ? 1 : 2; }
 
+int tile_stages(TileId id) { return id == kTile256x256 ? 4 : 3; }
+
 // The 32-row tile serves groups of a few dozen rows, where the dynamic
 // per-XCD queues of the tile-by-tile loop balance the uneven groups better.
 bool uses_continuous_pipeline(bool int4, int64_t k, int bm, int bk, int stages) {
@@ -2010,9 +2014,9 @@ const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool
   if (fp8) return trans_b ? "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8>" : "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8,kn>";
   // per tile: i8, i4, i8 cont, i4 cont, i8 transposed weights, i8 cont transposed weights
   static const char* names[kNumTiles][6] = {
-      {"gmm_kernel<256,256,64,2x2,s3,i8>", "gmm_kernel<256,256,64,2x2,s3,i4>", "gmm_kernel<256,256,64,2x2,s3,i8,cont>",
-       "gmm_kernel<256,256,64,2x2,s3,i4,cont>", "gmm_kernel<256,256,64,2x2,s3,i8,tb>",
-       "gmm_kernel<256,256,64,2x2,s3,i8,cont,tb>"},
+      {"gmm_kernel<256,256,64,4x2,s4,i8>", "gmm_kernel<256,256,64,4x2,s4,i4>", "gmm_kernel<256,256,64,4x2,s4,i8,cont>",
+       "gmm_kernel<256,256,64,4x2,s4,i4,cont>", "gmm_kernel<256,256,64,4x2,s4,i8,tb>",
+       "gmm_kernel<256,256,64,4x2,s4,i8,cont,tb>"},
       {"gmm_kernel<128,256,64,2x2,s3,i8>", "gmm_kernel<128,256,64,2x2,s3,i4>", "gmm_kernel<128,256,64,2x2,s3,i8,cont>",
        "gmm_kernel<128,256,64,2x2,s3,i4,cont>", "gmm_kernel<128,256,64,2x2,s3,i8,tb>",
        "gmm_kernel<128,256,64,2x2,s3,i8,cont,tb>"},
@@ -2024,7 +2028,7 @@ const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool
        "gmm_kernel<32,256,64,1x4,s3,i8,cont,tb>"},
   };
   const TileShape ts = tile_shape(id);
-  const bool cont = uses_continuous_pipeline(int4, k, ts.bm, ts.bk, 3);
+  const bool cont = uses_continuous_pipeline(int4, k, ts.bm, ts.bk, tile_stages(id));
   if (trans_b && !int4) return names[(int)id][cont ? 5 : 4];
   return names[(int)id][(int4 ? 1 : 0) + (cont ? 2 : 0)];
 }
@@ -2058,31 +2062,31 @@ Workspace workspace_layout(int64_t m, int64_t n, int64_t output_bs, bool ordered
 }
 
 // The continuous pipeline exists for tiles of at least 64 rows.
-template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC, int COMB>
+template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC, int COMB, int NT>
 static void launch_gemm_mode(const KParams& kp, bool int4, bool trans_b, bool cont, dim3 gd, dim3 bd, size_t dyn,
                              hipStream_t s) {
   constexpr bool C = BM >= 64;
   if (int4) {
-    if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, COMB, C, false>), gd, bd, dyn, s, kp);
-    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, COMB, false, false>), gd, bd, dyn, s, kp);
+    if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, COMB, C, false, NT>), gd, bd, dyn, s, kp);
+    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, COMB, false, false, NT>), gd, bd, dyn, s, kp);
   } else if (trans_b) {
-    if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, C, true>), gd, bd, dyn, s, kp);
-    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, false, true>), gd, bd, dyn, s, kp);
+    if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, C, true, NT>), gd, bd, dyn, s, kp);
+    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, false, true, NT>), gd, bd, dyn, s, kp);
   } else {
-    if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, C, false>), gd, bd, dyn, s, kp);
-    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, false, false>), gd, bd, dyn, s, kp);
+    if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, C, false, NT>), gd, bd, dyn, s, kp);
+    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, false, false, NT>), gd, bd, dyn, s, kp);
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC>
+template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC, int NT = kThreads>
 static void launch_gemm(const KParams& kp, bool int4, bool trans_b, int grid, hipStream_t s) {
-  const dim3 gd(grid), bd(kThreads);
+  const dim3 gd(grid), bd(NT);
   const size_t dyn = ((size_t)(2 * kp.e + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
   const bool cont = uses_continuous_pipeline(int4, kp.k, BM, BK, ST);
   if (kp.combine == kCombineOrdered)
-    launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineOrdered>(kp, int4, trans_b, cont, gd, bd, dyn, s);
+    launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineOrdered, NT>(kp, int4, trans_b, cont, gd, bd, dyn, s);
   else
-    launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineAtomic>(kp, int4, trans_b, cont, gd, bd, dyn, s);
+    launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineAtomic, NT>(kp, int4, trans_b, cont, gd, bd, dyn, s);
 }
 
 int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* stream, void* const* gemm_events) {
@@ -2136,7 +2140,7 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
   // the tile-by-tile loop of the int8/int4 kernel takes its tiles from
   // queues whose counters start at zero; the other loops use a static order
   const bool dynamic_queues =
-      !a.mx && !a.fp8 && !(ts.bm >= 64 && uses_continuous_pipeline(a.int4, a.k, ts.bm, ts.bk, 3));
+      !a.mx && !a.fp8 && !(ts.bm >= 64 && uses_continuous_pipeline(a.int4, a.k, ts.bm, ts.bk, tile_stages(plan.tile)));
   if (plan.combine == kCombineOrdered && plan.scan_reduce) {
     kp.y = (float*)(ws + w.y_off);
     if (dynamic_queues)
@@ -2185,7 +2189,7 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
           hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, true, true>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
       }
     } else switch (plan.tile) {
-      case kTile256x256: launch_gemm<256, 256, 64, 2, 2, 3, 1>(kp, a.int4, a.trans_b, plan.grid, s); break;
+      case kTile256x256: launch_gemm<256, 256, 64, 4, 2, 4, 1, 512>(kp, a.int4, a.trans_b, plan.grid, s); break;
       case kTile128x256: launch_gemm<128, 256, 64, 2, 2, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;
       case kTile64x256: launch_gemm<64, 256, 64, 1, 4, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;
       default: launch_gemm<32, 256, 64, 1, 4, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;

@@ -93,7 +93,20 @@ def test_auto_picks_ordered_for_large_problems():
     info = B.PlanInfo()
     assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
     assert info.combine == B.COMBINE["ordered"]
-    assert info.tile_m == 128
+    assert info.tile_m == 256
+
+
+@pytest.mark.parametrize("m,e,int4,want", [
+    (131072, 32, False, 256),   # prefill-sized experts, int8 weights: the eight-wave 256-row tile
+    (131072, 32, True, 128),    # int4 weights keep the 128-row tile
+    (4096, 8, False, 128),      # 512-row experts: too few 256-row tiles for the CUs
+    (2048, 256, False, 32),     # a few rows per expert
+])
+def test_auto_tile_follows_the_shape(m, e, int4, want):
+    a = _args(m=m, e=e, obs=max(m // 8, 1), int4=int4)
+    info = B.PlanInfo()
+    assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
+    assert info.tile_m == want
 
 
 @pytest.mark.parametrize("m,e,int4,want", [
