@@ -12,11 +12,13 @@ enum Combine : int32_t { kCombineAtomic = 1, kCombineOrdered = 2 };
 
 // GEMM tile variants compiled into the library.
 enum TileId : int32_t {
-  kTile256x256 = 0,   // BM=256 BN=256, 4x2 waves of 64x128 (512 threads), 4 stages, 1 workgroup per CU
-  kTile128x256 = 1,   // BM=128 BN=256, 2x2 waves of 64x128, 3 stages
-  kTile64x256 = 2,    // BM=64  BN=256, 1x4 waves of 64x64, 3 stages
-  kTile32x256 = 3,    // BM=32  BN=256, 1x4 waves of 32x64, 3 stages
-  kNumTiles = 4
+  kTile256x256 = 0,     // BM=256 BN=256 BK=128, 4x2 waves of 64x128 (512 threads), 2 stages, 1 workgroup
+                        // per CU; int8 weights and k % 128 == 0 only
+  kTile128x256 = 1,     // BM=128 BN=256, 2x2 waves of 64x128, 3 stages
+  kTile64x256 = 2,      // BM=64  BN=256, 1x4 waves of 64x64, 3 stages
+  kTile32x256 = 3,      // BM=32  BN=256, 1x4 waves of 32x64, 3 stages
+  kTile256x256k64 = 4,  // BM=256 BN=256 BK=64, 4x2 waves of 64x128 (512 threads), 4 stages, 1 workgroup per CU
+  kNumTiles = 5
 };
 
 struct TileShape {

@@ -924,10 +924,11 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
   // (blocks of kTileBlock consecutive tiles dealt to the 8 queues in turn,
   // workgroups being dealt to the 8 XCDs in the same way) in turn with the
   // other workgroups of that queue.  Every k-step has the same shape: the
-  // MFMAs of substep 0 with the reads of substep 1; the wait for the next
-  // k-step's copies and a barrier; the MFMAs of substep 1 with the refill of
-  // the buffer just released and the next k-step's substep-0 reads.
-  static_assert(!CONT || KK == 2, "continuous pipeline: two substeps per stage");
+  // MFMAs of each substep but the last with the reads of the one after it;
+  // the wait for the next k-step's copies and a barrier; the MFMAs of the
+  // last substep with the refill of the buffer just released and the next
+  // k-step's substep-0 reads.
+  static_assert(KK % 2 == 0, "substeps alternate between two fragment sets");
   if constexpr (CONT) {
     {
       const int G = gridDim.x;
@@ -969,9 +970,13 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
       v16i acc[FM][FN];
       auto kstep = [&](int kt, int fill_ks) {
         const int stage_next = stage + 1 == STAGES ? 0 : stage + 1;
-        auto rd1 = [&](auto r_) { read_item(r_, stage, 1, af[1], bf[1]); };
-        mfma_step(af[0], bf[0], acc, std::integral_constant<int, 0>{}, std::integral_constant<int, NREAD>{},
-                  no_copy, rd1);
+        // substeps 0 .. KK-2, each with the fragment reads of the next one
+        static_for<0, KK - 1>([&](auto kk_) {
+          constexpr int kk = decltype(kk_)::value;
+          auto rd = [&](auto r_) { read_item(r_, stage, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]); };
+          mfma_step(af[kk & 1], bf[kk & 1], acc, std::integral_constant<int, 0>{}, std::integral_constant<int, NREAD>{},
+                    no_copy, rd);
+        });
         // the next k-step's copies have landed and every wave holds this
         // stage's fragments; after the first k-step of a tile the previous
         // tile's epilogue stores may still be in flight
@@ -985,8 +990,8 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
         lds_barrier();
         auto cp = [&](auto d_) { copy_item(d_, stage, fill_ks); };
         auto rd0 = [&](auto r_) { read_item(r_, stage_next, 0, af[0], bf[0]); };
-        mfma_step(af[1], bf[1], acc, std::integral_constant<int, N_COPY>{}, std::integral_constant<int, NREAD>{},
-                  cp, rd0);
+        mfma_step(af[(KK - 1) & 1], bf[(KK - 1) & 1], acc, std::integral_constant<int, N_COPY>{},
+                  std::integral_constant<int, NREAD>{}, cp, rd0);
         stage = stage_next;
       };
       while (true) {
@@ -1991,16 +1996,17 @@ __global__ __launch_bounds__(kThreads) void reduce_scan_kernel(KParams p) {
 // ---------------------------------------------------------------------------
 TileShape tile_shape(TileId id) {
   switch (id) {
-    case kTile256x256: return {256, 256, 64};
+    case kTile256x256: return {256, 256, 128};
+    case kTile256x256k64: return {256, 256, 64};
     case kTile128x256: return {128, 256, 64};
     case kTile64x256: return {64, 256, 64};
     default: return {32, 256, 64};
   }
 }
 
-int tile_occupancy(TileId id) { return id == kTile256x256 ? 1 : 2; }
+int tile_occupancy(TileId id) { return id == kTile256x256 || id == kTile256x256k64 ? 1 : 2; }
 
-int tile_stages(TileId id) { return id == kTile256x256 ? 4 : 3; }
+int tile_stages(TileId id) { return id == kTile256x256 ? 2 : id == kTile256x256k64 ? 4 : 3; }
 
 // The 32-row tile serves groups of a few dozen rows, where the dynamic
 // per-XCD queues of the tile-by-tile loop balance the uneven groups better.
@@ -2014,9 +2020,8 @@ const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool
   if (fp8) return trans_b ? "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8>" : "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8,kn>";
   // per tile: i8, i4, i8 cont, i4 cont, i8 transposed weights, i8 cont transposed weights
   static const char* names[kNumTiles][6] = {
-      {"gmm_kernel<256,256,64,4x2,s4,i8>", "gmm_kernel<256,256,64,4x2,s4,i4>", "gmm_kernel<256,256,64,4x2,s4,i8,cont>",
-       "gmm_kernel<256,256,64,4x2,s4,i4,cont>", "gmm_kernel<256,256,64,4x2,s4,i8,tb>",
-       "gmm_kernel<256,256,64,4x2,s4,i8,cont,tb>"},
+      {"gmm_kernel<256,256,128,4x2,s2,i8>", "-", "gmm_kernel<256,256,128,4x2,s2,i8,cont>", "-",
+       "gmm_kernel<256,256,128,4x2,s2,i8,tb>", "gmm_kernel<256,256,128,4x2,s2,i8,cont,tb>"},
       {"gmm_kernel<128,256,64,2x2,s3,i8>", "gmm_kernel<128,256,64,2x2,s3,i4>", "gmm_kernel<128,256,64,2x2,s3,i8,cont>",
        "gmm_kernel<128,256,64,2x2,s3,i4,cont>", "gmm_kernel<128,256,64,2x2,s3,i8,tb>",
        "gmm_kernel<128,256,64,2x2,s3,i8,cont,tb>"},
@@ -2026,6 +2031,9 @@ const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool
       {"gmm_kernel<32,256,64,1x4,s3,i8>", "gmm_kernel<32,256,64,1x4,s3,i4>", "gmm_kernel<32,256,64,1x4,s3,i8,cont>",
        "gmm_kernel<32,256,64,1x4,s3,i4,cont>", "gmm_kernel<32,256,64,1x4,s3,i8,tb>",
        "gmm_kernel<32,256,64,1x4,s3,i8,cont,tb>"},
+      {"gmm_kernel<256,256,64,4x2,s4,i8>", "gmm_kernel<256,256,64,4x2,s4,i4>", "gmm_kernel<256,256,64,4x2,s4,i8,cont>",
+       "gmm_kernel<256,256,64,4x2,s4,i4,cont>", "gmm_kernel<256,256,64,4x2,s4,i8,tb>",
+       "gmm_kernel<256,256,64,4x2,s4,i8,cont,tb>"},
   };
   const TileShape ts = tile_shape(id);
   const bool cont = uses_continuous_pipeline(int4, k, ts.bm, ts.bk, tile_stages(id));
@@ -2061,14 +2069,17 @@ Workspace workspace_layout(int64_t m, int64_t n, int64_t output_bs, bool ordered
   return w;
 }
 
-// The continuous pipeline exists for tiles of at least 64 rows.
-template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC, int COMB, int NT>
+// The continuous pipeline exists for tiles of at least 64 rows.  Variants
+// built without int4 weights (I4 = false) are never planned for them.
+template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC, int COMB, int NT, bool I4>
 static void launch_gemm_mode(const KParams& kp, bool int4, bool trans_b, bool cont, dim3 gd, dim3 bd, size_t dyn,
                              hipStream_t s) {
   constexpr bool C = BM >= 64;
   if (int4) {
-    if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, COMB, C, false, NT>), gd, bd, dyn, s, kp);
-    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, COMB, false, false, NT>), gd, bd, dyn, s, kp);
+    if constexpr (I4) {
+      if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, COMB, C, false, NT>), gd, bd, dyn, s, kp);
+      else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, COMB, false, false, NT>), gd, bd, dyn, s, kp);
+    }
   } else if (trans_b) {
     if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, C, true, NT>), gd, bd, dyn, s, kp);
     else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, false, true, NT>), gd, bd, dyn, s, kp);
@@ -2078,15 +2089,15 @@ static void launch_gemm_mode(const KParams& kp, bool int4, bool trans_b, bool co
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC, int NT = kThreads>
+template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC, int NT = kThreads, bool I4 = true>
 static void launch_gemm(const KParams& kp, bool int4, bool trans_b, int grid, hipStream_t s) {
   const dim3 gd(grid), bd(NT);
   const size_t dyn = ((size_t)(2 * kp.e + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
   const bool cont = uses_continuous_pipeline(int4, kp.k, BM, BK, ST);
   if (kp.combine == kCombineOrdered)
-    launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineOrdered, NT>(kp, int4, trans_b, cont, gd, bd, dyn, s);
+    launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineOrdered, NT, I4>(kp, int4, trans_b, cont, gd, bd, dyn, s);
   else
-    launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineAtomic, NT>(kp, int4, trans_b, cont, gd, bd, dyn, s);
+    launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineAtomic, NT, I4>(kp, int4, trans_b, cont, gd, bd, dyn, s);
 }
 
 int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* stream, void* const* gemm_events) {
@@ -2189,7 +2200,8 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
           hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, true, true>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
       }
     } else switch (plan.tile) {
-      case kTile256x256: launch_gemm<256, 256, 64, 4, 2, 4, 1, 512>(kp, a.int4, a.trans_b, plan.grid, s); break;
+      case kTile256x256: launch_gemm<256, 256, 128, 4, 2, 2, 1, 512, false>(kp, a.int4, a.trans_b, plan.grid, s); break;
+      case kTile256x256k64: launch_gemm<256, 256, 64, 4, 2, 4, 1, 512>(kp, a.int4, a.trans_b, plan.grid, s); break;
       case kTile128x256: launch_gemm<128, 256, 64, 2, 2, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;
       case kTile64x256: launch_gemm<64, 256, 64, 1, 4, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;
       default: launch_gemm<32, 256, 64, 1, 4, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;
