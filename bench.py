@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--timing-detail", action="store_true",
                     help="after the timed steps, add a 'timing' object: per-call median/min/p90 with warm caches "
                          "and with 1 GiB written before each call (L2 and MALL evicted), and both combine modes")
+    ap.add_argument("--zero-operands", action="store_true",
+                    help="power study: x1 and x2 all zero (int8 workloads; the matrix cores then draw little "
+                         "power); the line is marked, carries no CPU baseline, and is never the headline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (torch copy_) 5 times: the reference kernel whose "
                          "FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic figures")
@@ -435,6 +438,13 @@ def main():
         x1, x2 = T(p.x1), T(p.x2)
         scale = None if p.scale is None else (bf16(p.scale) if p.scale_bf16 else T(p.scale))
         pts = T(p.pertoken_scale)
+    if args.zero_operands:
+        if p.mx or p.fp8:
+            print("--zero-operands applies to the int8 workloads", file=sys.stderr)
+            sys.exit(2)
+        x1.zero_()
+        x2.zero_()
+        args.no_cpu_baseline = True
     logit, gl, ri = T(p.logit), T(p.group_list), T(p.row_index)
     shared = bf16(p.shared_input)
     out = torch.empty((p.output_bs, p.n), dtype=torch.float32, device=dev)
@@ -524,7 +534,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8xfp4" if p.mx else ("fp8" if p.fp8 else "int8"),
-        "data": "synthetic (seeded generator; random int8 weights/activations, routing and scales of the stated shapes)",
+        "data": ("synthetic, x1 and x2 all zero (power study, not the workload's data); routing and scales seeded"
+                 if args.zero_operands else
+                 "synthetic (seeded generator; random int8 weights/activations, routing and scales of the stated shapes)"),
         "config": {"workload": p.name, "tokens": p.output_bs, "top_k": p.m // max(p.output_bs, 1), "m": p.m,
                    "e": p.e, "k": p.k, "n": p.n,
                    "weights": "fp4 e2m1, e8m0 per 32 k" if p.mx else
