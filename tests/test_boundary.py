@@ -96,6 +96,25 @@ def test_auto_picks_ordered_for_large_problems():
     assert info.tile_m == 256
 
 
+@pytest.mark.parametrize("k,int4,want_k,want_name", [
+    (2048, False, 128, "gmm_kernel<256,256,128,4x2,s2,i8,cont>"),  # 128 k per stage, two stages
+    (512, False, 128, "gmm_kernel<256,256,128,4x2,s2,i8,cont>"),
+    (128, False, 128, "gmm_kernel<256,256,128,4x2,s2,i8>"),        # one k-step: tile by tile
+    (192, False, 64, "gmm_kernel<256,256,64,4x2,s4,i8>"),          # k % 128 != 0: 64 k, four stages
+    (448, False, 64, "gmm_kernel<256,256,64,4x2,s4,i8,cont>"),
+    (2048, True, 64, "gmm_kernel<256,256,64,4x2,s4,i4,cont>"),     # int4 weights: 64 k
+])
+def test_256_row_tile_stage_depth(k, int4, want_k, want_name):
+    a = _args(m=8192, k=k, e=4, obs=1024, int4=int4)
+    tc = (ctypes.c_int64 * 2)(0, 256)
+    a.tuning_config = ctypes.cast(tc, ctypes.POINTER(ctypes.c_int64))
+    a.tuning_config_len = 2
+    info = B.PlanInfo()
+    assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
+    assert (info.tile_m, info.tile_n, info.tile_k) == (256, 256, want_k)
+    assert info.gemm_kernel.decode() == want_name
+
+
 @pytest.mark.parametrize("m,e,int4,want", [
     (131072, 32, False, 256),   # prefill-sized experts, int8 weights: the eight-wave 256-row tile
     (131072, 32, True, 128),    # int4 weights keep the 128-row tile
