@@ -293,7 +293,18 @@ int validate(const gmmfr_args* a, Derived* d) {
 // Tile choice from the expected rows per expert: tuningConfig[0] when given
 // (the operator's tiling hint), else m / e.  Results do not depend on it.
 TileId choose_tile(const gmmfr_args* a, const Derived& d, int cu_count) {
-  if (d.mx || d.fp8) return kTile128x256;   // the FP8 GEMMs have one tile shape
+  int64_t expect = (d.m + d.e - 1) / d.e;
+  if (a->tuning_config_len > 0 && a->tuning_config[0] > 0) expect = a->tuning_config[0];
+  const int64_t ntn = (d.n + 255) / 256;
+  // enough 256-row tiles for every CU to run several
+  const bool big_ok = expect >= 1024 && (d.m / 256) * ntn >= 8 * (int64_t)std::max(cu_count, 1);
+  if (d.mx || d.fp8) {  // the FP8 GEMMs: 256 x 256 (eight waves) or 128 x 256
+    // Measured on the prefill shape: FP8 -3% (weights (e,k,n)) and -8%
+    // ((e,n,k)) with the 256-row tile; MxA8W4 +0.5%, so it keeps 128 rows.
+    const int64_t hint = a->tuning_config_len > 1 ? a->tuning_config[1] : 0;
+    if (hint == 256 || (hint == 0 && big_ok && d.fp8)) return kTileMx256;
+    return kTile128x256;
+  }
   // The 256-row tile copies 128 k per stage (two stages) where it can: int8
   // weights and k % 128 == 0 (-2.6% GEMM time against 64 k per stage, four
   // stages, on the prefill shape); 64 k otherwise.
@@ -307,16 +318,13 @@ TileId choose_tile(const gmmfr_args* a, const Derived& d, int cu_count) {
       default: break;
     }
   }
-  int64_t expect = (d.m + d.e - 1) / d.e;
-  if (a->tuning_config_len > 0 && a->tuning_config[0] > 0) expect = a->tuning_config[0];
   // The 256-row tile (eight waves, one workgroup per CU) copies a third less
   // data per MAC than two 128-row tiles.  Measured GEMM times on MI355X, 32
   // experts of about 4096 rows, k = 2048, n = 7168: -6% with int8 weights
   // given (e,k,n), -15% given (e,n,k), but +4% with int4 weights; and +54%
   // with 512-row experts (8 experts, 4096 rows), where too few tiles reach
   // the 256 CUs.
-  const int64_t ntn = (d.n + 255) / 256;
-  if (expect >= 1024 && !d.int4 && (d.m / 256) * ntn >= 8 * (int64_t)std::max(cu_count, 1)) return big;
+  if (big_ok && !d.int4) return big;
   if (expect >= 256) return kTile128x256;
   if (expect >= 64) return kTile64x256;
   return kTile32x256;

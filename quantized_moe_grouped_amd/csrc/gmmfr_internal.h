@@ -18,7 +18,9 @@ enum TileId : int32_t {
   kTile64x256 = 2,      // BM=64  BN=256, 1x4 waves of 64x64, 3 stages
   kTile32x256 = 3,      // BM=32  BN=256, 1x4 waves of 32x64, 3 stages
   kTile256x256k64 = 4,  // BM=256 BN=256 BK=64, 4x2 waves of 64x128 (512 threads), 4 stages, 1 workgroup per CU
-  kNumTiles = 5
+  kTileMx256 = 5,       // FP8 / MxA8W4: BM=256 BN=256 BK=64, 4x2 waves of 64x128 (512 threads), 1 workgroup
+                        // per CU (the FP8 kernels' other tile is kTile128x256)
+  kNumTiles = 6
 };
 
 struct TileShape {

@@ -1175,25 +1175,36 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // acc is the fp32 sum and y = ((acc * scale) * pertokenScale) * logit.
 // Measured on the device: with both operands FP8, B lane l holds column l%32
 // with the byte layout of A.
-template <int COMBINE, bool B8, bool BKN>
-__global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
+// BM_ = 128 (NT = 256, two workgroups per CU) or 256 (NT = 512, eight waves
+// of 64 x 128, one workgroup per CU).
+template <int COMBINE, bool B8, bool BKN, int BM_ = 128, int NT = kThreads>
+__global__ __launch_bounds__(NT, NT == kThreads ? 2 : 1) void mx_gemm_kernel(KParams p) {
   // BKN (FP8 only): weights given (e,k,n); a B stage then holds BK weight rows
   // of BN bytes, laid out and read with the int8 kernel's transpose reads
   static_assert(!BKN || B8, "the (e,k,n) weight layout is an FP8 mode");
-  constexpr int BM = 128, BN = 256, BK = 64, STAGES = B8 ? 3 : 4;
+  constexpr int BM = BM_, BN = 256, BK = 64, STAGES = B8 ? 3 : 4;
+  constexpr int NWAVES = NT / 64;
   constexpr int WAVES_N = 2, WTM = 64, WTN = 128, FM = 2, FN = 4;
+  static_assert(BM == WTM * (NWAVES / WAVES_N) && BN == WTN * WAVES_N, "waves cover the tile");
   constexpr int A_BYTES = BM * BK;         // fp8: one byte per k
   constexpr int B_COLB = B8 ? BK : BK / 2;  // fp8: 64 bytes per column and k-step; fp4: 32
   constexpr int B_BYTES = BN * B_COLB;
-  constexpr int A_INSTR = A_BYTES / 16 / kThreads, B_INSTR = B_BYTES / 16 / kThreads;
-  static_assert(A_INSTR == 2 && B_INSTR == (B8 ? 4 : 2) && BN == kThreads && BM == kThreads / 2, "copy split");
+  constexpr int A_INSTR = A_BYTES / 16 / NT, B_INSTR = B_BYTES / 16 / NT;
+  static_assert(A_INSTR >= 1 && B_INSTR >= 1 && A_INSTR * 16 * NT == A_BYTES && B_INSTR * 16 * NT == B_BYTES,
+                "whole copies per thread");
+  // Block-scale copies (MX): one dword per column (threads 0..BN-1) and per
+  // row.  With 256 threads the rows' copies come from waves 0-1 on top of
+  // their column copies; with 512 threads waves 4-7 copy the rows, so every
+  // wave issues one scale copy per pair of slices.
+  constexpr bool SC_SPLIT = NT == BM + BN;
+  static_assert(SC_SPLIT || (NT == BN && BM <= NT), "scale copies cover the rows and columns");
   // Copies per thread and k-slice: A and B.  MX: a scale dword holds the
   // block scales of two k-slices, so even slices add one B-scale dword copy
   // per thread (waves 0-1 also an A-scale dword) into a ring of SC_SLOTS slots
   // of its own, indexed by the running count of slices.  A wait for a slice
   // allows the fewest copies its STAGES-2 younger slices can have issued.
   constexpr int LOADS_AB = A_INSTR + B_INSTR;
-  constexpr int SC_LO = B8 ? 0 : 2, SC_HI = B8 ? 0 : 1;
+  constexpr int SC_LO = B8 ? 0 : (SC_SPLIT ? 1 : 2), SC_HI = B8 ? 0 : 1;
   constexpr int LOADS_LO = (STAGES - 2) * LOADS_AB + (STAGES - 2) / 2 * SC_LO;
   constexpr int LOADS_HI = (STAGES - 2) * LOADS_AB + (STAGES - 2) / 2 * SC_HI;
   constexpr int SC_SLOTS = B8 ? 1 : 4;
@@ -1222,7 +1233,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   int32_t* s_ends = s_dyn;
   int32_t* s_tile_pre = s_dyn + p.e;
   int64_t* s_scan = (int64_t*)sA;
-  static_assert(STAGES * A_BYTES >= kThreads * 8, "scan scratch fits in the A stages");
+  static_assert(STAGES * A_BYTES >= NT * 8, "scan scratch fits in the A stages");
 
   // an absent logit or pertokenScale reads as 1.0, a per-tensor
   // pertokenScale as its one value (filled once; the table build's barriers
@@ -1231,12 +1242,12 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   const bool pt_rows = B8 && p.pertoken != nullptr && !p.pertoken_scalar;
   {
     const float pt_fill = (B8 && p.pertoken && p.pertoken_scalar) ? p.pertoken[0] : 1.0f;
-    for (int q = threadIdx.x; q < 2 * BM; q += kThreads) {
+    for (int q = threadIdx.x; q < 2 * BM; q += NT) {
       if (!lg_rows) (&s_lg[0][0])[q] = 1.0f;
       if (!pt_rows) (&s_pt[0][0])[q] = pt_fill;
     }
   }
-  build_group_table(p, BM, s_ends, s_tile_pre, s_scan);
+  build_group_table<NT>(p, BM, s_ends, s_tile_pre, s_scan);
   const int total_tiles = s_tile_pre[p.e];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1252,7 +1263,11 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
   // MX: scale dwords per row or column; when k % 128 != 0 the block scales
   // come from copies padded to a whole dword (unit scales appended)
   const int64_t kdw = (k + 127) / 128;
-  const bool lo_wave = wave < 2;       // waves that copy the A-scale dwords (rows 0..127)
+  // waves that copy column (B) and row (A) scale dwords; lo_wave: both
+  const bool b_sc_wave = wave * 64 < BN;
+  const int a_sc_blk = SC_SPLIT ? wave - BN / 64 : wave;  // rows a_sc_blk*64 .. +63
+  const bool a_sc_wave = a_sc_blk >= 0 && a_sc_blk * 64 < BM;
+  const bool lo_wave = a_sc_wave && b_sc_wave;
   const uint32_t* sa_words = (const uint32_t*)p.pertoken;
   const uint32_t* sb_words = (const uint32_t*)p.scale;
 
@@ -1276,7 +1291,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
     a_tail_mask = 0;
 #pragma unroll
     for (int q = 0; q < A_INSTR; ++q) {
-      const int slot = (q * 4 + wave) * 64 + lane;
+      const int slot = (q * NWAVES + wave) * 64 + lane;
       const int r = slot / 4, cpos = slot % 4;
       const int64_t row = min(c.row0 + r, p.m - 1);  // rows past the group: loaded, never stored
       a_off[q] = (uint32_t)((row - c.row0) * k + ((cpos ^ swz_a<BK>(r)) * 16));
@@ -1288,7 +1303,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       b_base = (const int8_t*)uniform64((int64_t)((const int8_t*)p.x2 + (int64_t)c.g * k * n + c.col0));
 #pragma unroll
       for (int q = 0; q < B_INSTR; ++q) {
-        const int slot = (q * 4 + wave) * 64 + lane;
+        const int slot = (q * NWAVES + wave) * 64 + lane;
         const int r = slot / (BN / 16), cpos = slot % (BN / 16);
         const int64_t colb = min(c.col0 + ((cpos ^ swz_b(r)) * 16), n - 16);
         b_off[q] = (uint32_t)((int64_t)r * n + (colb - c.col0));
@@ -1299,7 +1314,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       b_tail_mask = 0;
 #pragma unroll
       for (int q = 0; q < B_INSTR; ++q) {
-        const int slot = (q * 4 + wave) * 64 + lane;
+        const int slot = (q * NWAVES + wave) * 64 + lane;
         const int64_t cpr = B_COLB / 16;  // 16-byte chunks of a column per k-step
         const int r = slot / cpr, cpos = slot % cpr;
         const int64_t col = min(c.col0 + r, n - 1);    // columns past n: loaded, never stored
@@ -1309,7 +1324,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
       }
     }
     sa_base = (const uint32_t*)uniform64((int64_t)(sa_words + c.row0 * kdw));
-    sa_off = (uint32_t)((min(c.row0 + tid, p.m - 1) - c.row0) * kdw * 4);
+    sa_off = (uint32_t)((min(c.row0 + (SC_SPLIT ? tid - BN : tid), p.m - 1) - c.row0) * kdw * 4);
     sb_base = (const uint32_t*)uniform64((int64_t)(sb_words + ((int64_t)c.g * n + c.col0) * kdw));
     sb_off = (uint32_t)((min(c.col0 + tid, n - 1) - c.col0) * kdw * 4);
   };
@@ -1325,27 +1340,30 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(KParams p) {
 #pragma unroll
     for (int q = 0; q < A_INSTR; ++q)
       lds_dma16_sv(a_base + (int64_t)kt * BK, a_off[q] - ((tail && ((a_tail_mask >> q) & 1u)) ? 32u : 0u),
-                   __builtin_amdgcn_readfirstlane(lds_addr(sA + st * A_BYTES + (q * 4 + wave) * 64 * 16)));
+                   __builtin_amdgcn_readfirstlane(lds_addr(sA + st * A_BYTES + (q * NWAVES + wave) * 64 * 16)));
 #pragma unroll
     for (int q = 0; q < B_INSTR; ++q)
       lds_dma16_sv(b_base + (int64_t)kt * (BKN ? (int64_t)BK * n : (int64_t)B_COLB),
                    b_off[q] - ((tail && ((b_tail_mask >> q) & 1u)) ? 16u : 0u),
-                   __builtin_amdgcn_readfirstlane(lds_addr(sB + st * B_BYTES + (q * 4 + wave) * 64 * 16)));
+                   __builtin_amdgcn_readfirstlane(lds_addr(sB + st * B_BYTES + (q * NWAVES + wave) * 64 * 16)));
     if constexpr (!B8) {
       if (grp8) {
         if ((kt & 7) == 0) {  // the four dwords of slices kt .. kt + 7, [row][4 dwords]
           const int slot = (gs >> 3) % G8_SLOTS;
-          lds_dma16_sv(sb_base + kt / 2, sb_off,
-                       __builtin_amdgcn_readfirstlane(lds_addr(&sSB[0][0] + (slot * BN + wave * 64) * 4)));
-          if (lo_wave)
+          if (b_sc_wave)
+            lds_dma16_sv(sb_base + kt / 2, sb_off,
+                         __builtin_amdgcn_readfirstlane(lds_addr(&sSB[0][0] + (slot * BN + wave * 64) * 4)));
+          if (a_sc_wave)
             lds_dma16_sv(sa_base + kt / 2, sa_off,
-                         __builtin_amdgcn_readfirstlane(lds_addr(&sSA[0][0] + (slot * BM + wave * 64) * 4)));
+                         __builtin_amdgcn_readfirstlane(lds_addr(&sSA[0][0] + (slot * BM + a_sc_blk * 64) * 4)));
         }
       } else if ((kt & 1) == 0) {  // the dword holding the block scales of slices kt and kt + 1
         const int slot = pr % SC_SLOTS;
-        lds_dma4_sv(sb_base + kt / 2, sb_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSB[slot][wave * 64])));
-        if (lo_wave)
-          lds_dma4_sv(sa_base + kt / 2, sa_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSA[slot][wave * 64])));
+        if (b_sc_wave)
+          lds_dma4_sv(sb_base + kt / 2, sb_off, __builtin_amdgcn_readfirstlane(lds_addr(&sSB[slot][wave * 64])));
+        if (a_sc_wave)
+          lds_dma4_sv(sa_base + kt / 2, sa_off,
+                      __builtin_amdgcn_readfirstlane(lds_addr(&sSA[slot][a_sc_blk * 64])));
       }
     }
   };
@@ -2001,14 +2019,15 @@ __global__ __launch_bounds__(kThreads) void reduce_scan_kernel(KParams p) {
 TileShape tile_shape(TileId id) {
   switch (id) {
     case kTile256x256: return {256, 256, 128};
-    case kTile256x256k64: return {256, 256, 64};
+    case kTile256x256k64:
+    case kTileMx256: return {256, 256, 64};
     case kTile128x256: return {128, 256, 64};
     case kTile64x256: return {64, 256, 64};
     default: return {32, 256, 64};
   }
 }
 
-int tile_occupancy(TileId id) { return id == kTile256x256 || id == kTile256x256k64 ? 1 : 2; }
+int tile_occupancy(TileId id) { return id == kTile256x256 || id == kTile256x256k64 || id == kTileMx256 ? 1 : 2; }
 
 int tile_stages(TileId id) { return id == kTile256x256 ? 2 : id == kTile256x256k64 ? 4 : 3; }
 
@@ -2020,8 +2039,12 @@ bool uses_continuous_pipeline(bool int4, int64_t k, int bm, int bk, int stages) 
 }
 
 const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool mx, bool fp8) {
-  if (mx) return "mx_gemm_kernel<128,256,64,2x2,s4,fp8xfp4>";
-  if (fp8) return trans_b ? "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8>" : "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8,kn>";
+  const bool big = id == kTileMx256;
+  if (mx) return big ? "mx_gemm_kernel<256,256,64,4x2,s4,fp8xfp4>" : "mx_gemm_kernel<128,256,64,2x2,s4,fp8xfp4>";
+  if (fp8) {
+    if (big) return trans_b ? "mx_gemm_kernel<256,256,64,4x2,s3,fp8xfp8>" : "mx_gemm_kernel<256,256,64,4x2,s3,fp8xfp8,kn>";
+    return trans_b ? "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8>" : "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8,kn>";
+  }
   // per tile: i8, i4, i8 cont, i4 cont, i8 transposed weights, i8 cont transposed weights
   static const char* names[kNumTiles][6] = {
       {"gmm_kernel<256,256,128,4x2,s2,i8>", "-", "gmm_kernel<256,256,128,4x2,s2,i8,cont>", "-",
@@ -2038,6 +2061,7 @@ const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool
       {"gmm_kernel<256,256,64,4x2,s4,i8>", "gmm_kernel<256,256,64,4x2,s4,i4>", "gmm_kernel<256,256,64,4x2,s4,i8,cont>",
        "gmm_kernel<256,256,64,4x2,s4,i4,cont>", "gmm_kernel<256,256,64,4x2,s4,i8,tb>",
        "gmm_kernel<256,256,64,4x2,s4,i8,cont,tb>"},
+      {"-", "-", "-", "-", "-", "-"},  // FP8 / MxA8W4 only
   };
   const TileShape ts = tile_shape(id);
   const bool cont = uses_continuous_pipeline(int4, k, ts.bm, ts.bk, tile_stages(id));
@@ -2186,22 +2210,33 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
       if (er != hipSuccess) return (int)er;
     }
     const size_t dyn = ((size_t)(2 * kp.e + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
-    if (a.mx) {
-      if (kp.combine == kCombineOrdered)
-        hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, false, false>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
-      else
-        hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, false, false>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
-    } else if (a.fp8) {
-      if (a.trans_b) {
-        if (kp.combine == kCombineOrdered)
-          hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, true, false>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
-        else
-          hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, true, false>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
+    if (a.mx || a.fp8) {
+      const int B = a.mx ? 0 : (a.trans_b ? 1 : 2);  // MxA8W4, FP8 (e,n,k), FP8 (e,k,n)
+      const bool ord = kp.combine == kCombineOrdered;
+      if (plan.tile == kTileMx256) {
+        const dim3 gd(plan.grid), bd(512);
+        if (B == 0) {
+          if (ord) hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, false, false, 256, 512>), gd, bd, dyn, s, kp);
+          else hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, false, false, 256, 512>), gd, bd, dyn, s, kp);
+        } else if (B == 1) {
+          if (ord) hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, true, false, 256, 512>), gd, bd, dyn, s, kp);
+          else hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, true, false, 256, 512>), gd, bd, dyn, s, kp);
+        } else {
+          if (ord) hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, true, true, 256, 512>), gd, bd, dyn, s, kp);
+          else hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, true, true, 256, 512>), gd, bd, dyn, s, kp);
+        }
       } else {
-        if (kp.combine == kCombineOrdered)
-          hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, true, true>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
-        else
-          hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, true, true>), dim3(plan.grid), dim3(kThreads), dyn, s, kp);
+        const dim3 gd(plan.grid), bd(kThreads);
+        if (B == 0) {
+          if (ord) hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, false, false>), gd, bd, dyn, s, kp);
+          else hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, false, false>), gd, bd, dyn, s, kp);
+        } else if (B == 1) {
+          if (ord) hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, true, false>), gd, bd, dyn, s, kp);
+          else hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, true, false>), gd, bd, dyn, s, kp);
+        } else {
+          if (ord) hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, true, true>), gd, bd, dyn, s, kp);
+          else hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, true, true>), gd, bd, dyn, s, kp);
+        }
       }
     } else switch (plan.tile) {
       case kTile256x256: launch_gemm<256, 256, 128, 4, 2, 2, 1, 512, false>(kp, a.int4, a.trans_b, plan.grid, s); break;

@@ -173,20 +173,24 @@ GRID_CAPPED = ["ragged_shared", "counts_uncovered", "long_k", "k_512_one_scale_g
 def test_mx_grid_capped(name):
     """The persistent GEMM with its grid capped (tuningConfig[2]), so that
     each workgroup runs many tiles through the continuous pipeline's
-    handoff: within the bound, and the ordered combine bit-identical to the
-    uncapped launch (each element's k-loop is the same whatever tile runs
-    where)."""
-    p = W.mx_problem(**CASES[name])
+    handoff, with either tile (128 x 256, or 256 x 256 with eight waves):
+    within the bound, and the ordered combine bit-identical to the uncapped
+    launch (each element's k-loop is the same whatever tile runs where)."""
+    _check_capped(W.mx_problem(**CASES[name]))
+
+
+def _check_capped(p):
     ref, bound, _ = MX.run(p)
     d = G.to_device(p)
     base, _ = G.run_gpu(p, d, deterministic=True)
     base = base.cpu().numpy()
-    for cap in (3, 8, 16):
-        out, _ = G.run_gpu(p, d, deterministic=True, tuning_config=[0, 0, cap])
-        G.assert_bitexact(out.cpu().numpy(), base)
-        _check(p, out.cpu().numpy(), ref, bound)
-        out, _ = G.run_gpu(p, d, deterministic=False, combine="atomic", tuning_config=[0, 0, cap])
-        _check(p, out.cpu().numpy(), ref, bound)
+    for tile in (0, 256):
+        for cap in ((0, 3, 8, 16) if tile else (3, 8, 16)):
+            out, _ = G.run_gpu(p, d, deterministic=True, tuning_config=[0, tile, cap])
+            G.assert_bitexact(out.cpu().numpy(), base)
+            _check(p, out.cpu().numpy(), ref, bound)
+            out, _ = G.run_gpu(p, d, deterministic=False, combine="atomic", tuning_config=[0, tile, cap])
+            _check(p, out.cpu().numpy(), ref, bound)
 
 
 @pytest.mark.parametrize("name", list(FP8_CASES), ids=list(FP8_CASES))
@@ -195,16 +199,7 @@ def test_fp8_grid_capped(name, layout):
     p = W.fp8_problem(**FP8_CASES[name])
     if layout == "kn":
         p = W.with_untransposed_fp8_weights(p)
-    ref, bound, _ = MX.run(p)
-    d = G.to_device(p)
-    base, _ = G.run_gpu(p, d, deterministic=True)
-    base = base.cpu().numpy()
-    for cap in (3, 8, 16):
-        out, _ = G.run_gpu(p, d, deterministic=True, tuning_config=[0, 0, cap])
-        G.assert_bitexact(out.cpu().numpy(), base)
-        _check(p, out.cpu().numpy(), ref, bound)
-        out, _ = G.run_gpu(p, d, deterministic=False, combine="atomic", tuning_config=[0, 0, cap])
-        _check(p, out.cpu().numpy(), ref, bound)
+    _check_capped(p)
 
 
 # ---------------------------------------------------------------- the matrix core's block arithmetic
