@@ -512,3 +512,21 @@ def test_row_lookup_hint_is_checked():
         a.tuning_config = ctypes.cast(hint, ctypes.POINTER(ctypes.c_int64))
         a.tuning_config_len = 4
         assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == want
+
+
+@pytest.mark.parametrize("maker,m,e,hint,want_m,want_name", [
+    (_fp8_args, 131072, 32, 0, 256, "mx_gemm_kernel<256,256,64,4x2,s3,fp8xfp8>"),   # large experts: eight waves
+    (_fp8_args, 4096, 8, 0, 128, "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8>"),
+    (_mx_args, 131072, 32, 0, 128, "mx_gemm_kernel<128,256,64,2x2,s4,fp8xfp4>"),    # MxA8W4 keeps 128 rows
+    (_mx_args, 4096, 8, 256, 256, "mx_gemm_kernel<256,256,64,4x2,s4,fp8xfp4>"),     # unless asked
+])
+def test_fp8_tile_choice(maker, m, e, hint, want_m, want_name):
+    a = maker(m=m, e=e, obs=m // 8)
+    if hint:
+        tc = (ctypes.c_int64 * 2)(0, hint)
+        a.tuning_config = ctypes.cast(tc, ctypes.POINTER(ctypes.c_int64))
+        a.tuning_config_len = 2
+    info = B.PlanInfo()
+    assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
+    assert (info.tile_m, info.tile_n, info.tile_k) == (want_m, 256, 64)
+    assert info.gemm_kernel.decode() == want_name
