@@ -203,6 +203,8 @@ __device__ __forceinline__ int swz_a(int r) {
   else return (r ^ (r >> 3)) & 7;
 }
 __device__ __forceinline__ int swz_b(int r) { return (r & 7) << 1; }
+// FP4 (MxA8W4) B stage: column r's two 16-byte chunks, swapped when bit 3 of r is set
+__device__ __forceinline__ int swz_b4(int r) { return (r >> 3) & 1; }
 
 // HBM -> LDS copy of 16 bytes per lane: lane i of the wave writes LDS bytes
 // [lds_base + 16 i, lds_base + 16 i + 16).  lds_base must be wave-uniform.
@@ -1318,9 +1320,13 @@ __global__ __launch_bounds__(NT, NT == kThreads ? 2 : 1) void mx_gemm_kernel(KPa
         const int64_t cpr = B_COLB / 16;  // 16-byte chunks of a column per k-step
         const int r = slot / cpr, cpos = slot % cpr;
         const int64_t col = min(c.col0 + r, n - 1);    // columns past n: loaded, never stored
-        // fp8 columns are stored and read like A rows (same swizzle)
-        b_off[q] = (uint32_t)((col - c.col0) * colb + (B8 ? (cpos ^ swz_a<BK>(r)) : cpos) * 16);
-        if (!B8 && cpos == 1) b_tail_mask |= 1u << q;  // fp4: nibbles of k 32..63 of the step
+        // fp8 columns are stored and read like A rows (same swizzle); fp4
+        // columns (two chunks) swap their chunks in every other group of 8
+        // columns, so that 16 lanes reading 16 consecutive columns cover
+        // all 64 banks (unswizzled, columns c and c + 8 share banks)
+        const int gch = B8 ? (cpos ^ swz_a<BK>(r)) : (cpos ^ swz_b4(r));
+        b_off[q] = (uint32_t)((col - c.col0) * colb + gch * 16);
+        if (!B8 && gch == 1) b_tail_mask |= 1u << q;  // fp4: nibbles of k 32..63 of the step
       }
     }
     sa_base = (const uint32_t*)uniform64((int64_t)(sa_words + c.row0 * kdw));
@@ -1458,7 +1464,7 @@ __global__ __launch_bounds__(NT, NT == kThreads ? 2 : 1) void mx_gemm_kernel(KPa
         bf[jj] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         sb[jj] = 127;
       } else {
-        const v4i w = *(const LDS_PTR(v4i))(b_st + cl * B_COLB + h * 16);
+        const v4i w = *(const LDS_PTR(v4i))(b_st + cl * B_COLB + ((h ^ swz_b4(cl)) << 4));
         bf[jj] = v8i{w.x, w.y, w.z, w.w, 0, 0, 0, 0};
         sb[jj] = (int)(sc_word(scb, BN, cl) >> sel);
       }
