@@ -10,13 +10,17 @@
 //
 // Kernels
 //   seed_kernel        out := 0, rows [off, off+bsdp) := widened sharedInput
-//   gmm_kernel<...>    persistent grouped int8 / int4 GEMM; epilogue adds into
-//                      out with fp32 atomics, or stores y for the ordered combine
+//   gmm_kernel<...>    persistent grouped int8 / int4 GEMM (256x256 tiles with
+//                      eight waves, or 128/64/32 x 256 with four); epilogue adds
+//                      into out with fp32 atomics, or stores y for the ordered
+//                      combine
 //   mx_gemm_kernel<..> the same for FP8 x FP4 (MxA8W4, E8M0 block scales) and
 //                      FP8 x FP8 weights, on the block-scaled MFMA
 //   hist/scan/scatter  rows bucketed by destination (ordered combine)
 //   reduce_kernel      per destination: sort its rows ascending, fold
 //                      seed + y[rows] in that order, write out once
+//   reduce_scan_kernel the same without the buckets: each destination scans
+//                      rowIndex for its rows (small m * outputBS)
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
   constexpr int B_ISSUED = REGB4 ? B4_PER : B_INSTR;
   constexpr int LOADS_FULL = A_INSTR + B_ISSUED;
   constexpr int LOADS_SHORT = A_INSTR - 1 + B_ISSUED;
-  static_assert(WAVES_M * WAVES_N == NWAVES, "4 waves");
+  static_assert(WAVES_M * WAVES_N == NWAVES, "waves cover the workgroup");
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(BN >= 256, "B swizzle needs 16 chunks per row (8 when packed)");
   static_assert(A_SLOTS % 64 == 0 && B_SLOTS % 64 == 0, "whole waves per copy");
