@@ -119,6 +119,16 @@ def test_fp8_untransposed_weights(name):
         _check(p, out.cpu().numpy(), ref, bound)
 
 
+@pytest.mark.parametrize("layout", ["nk", "kn"])
+def test_fp8_maximum_expert_count(layout):
+    """e = 1024 with FP8 weights: the group table's scans full, most experts
+    empty or a few rows, both tiles, a capped grid."""
+    p = W.fp8_problem(24, 3000, 256, 256, 1024, empty_frac=0.6, output_bs=700)
+    if layout == "kn":
+        p = W.with_untransposed_fp8_weights(p)
+    _check_capped(p)
+
+
 def test_fp8_untransposed_ordered_is_run_to_run_identical():
     """The ordered combine is run-to-run identical with (e,k,n) weights."""
     p = W.with_untransposed_fp8_weights(W.fp8_problem(**FP8_CASES["long_k"]))

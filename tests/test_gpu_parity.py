@@ -176,6 +176,19 @@ def test_grid_capped_single_workgroup():
     _check_grid_capped(q, caps=(1,), tiles=(0, 64, 128))
 
 
+@pytest.mark.parametrize("glt", [0, 1])
+def test_maximum_expert_count(glt):
+    """e = 1024, the largest groupList the library takes ("aclnnGroupedMatmul
+    FinalizeRoutingWeightNzV2", parameter notes: e <= 1024 on the A2/A3
+    parts): the group table's scans fill every entry (four per thread with
+    256 threads, two with 512), most experts empty or a few rows, under every
+    tile height and a capped grid, with k long enough for the continuous
+    pipeline and for the 256-row tile's 128-k stages."""
+    p = W.random_problem(20 + glt, 4000, 256, 272, 1024, group_list_type=glt, empty_frac=0.6, output_bs=900,
+                         bsdp=64, shared_offset=30)
+    _check_full(p, hints=(None, (0, 256), (0, 128), (0, 64), (0, 32), (0, 256, 16), (0, 64, 8)))
+
+
 def test_zero_rows_gives_seed():
     p = W.random_problem(9, 0, 64, 64, 2, output_bs=20, bsdp=6, shared_offset=3)
     ref, _ = oracle.run(p)
