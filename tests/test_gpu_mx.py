@@ -129,6 +129,12 @@ def test_fp8_maximum_expert_count(layout):
     _check_capped(p)
 
 
+def test_mx_fp8_maximum_k():
+    """k = 65536 (1024 k-steps per tile) for MxA8W4 and FP8, both tiles."""
+    _check_capped(W.mx_problem(28, 96, 65536, 256, 2, empty_frac=0.0, output_bs=60))
+    _check_capped(W.fp8_problem(27, 96, 65536, 256, 2, empty_frac=0.0, output_bs=60))
+
+
 def test_fp8_untransposed_ordered_is_run_to_run_identical():
     """The ordered combine is run-to-run identical with (e,k,n) weights."""
     p = W.with_untransposed_fp8_weights(W.fp8_problem(**FP8_CASES["long_k"]))

@@ -189,6 +189,21 @@ def test_maximum_expert_count(glt):
     _check_full(p, hints=(None, (0, 256), (0, 128), (0, 64), (0, 32), (0, 256, 16), (0, 64, 8)))
 
 
+@pytest.mark.parametrize("int4", [False, True], ids=["int8", "int4"])
+def test_maximum_k(int4):
+    """k = 65536, the largest the library takes: 512 k-steps of the
+    256-row tile (1024 of the others) per tile, and some rows all -128 against
+    weights all -128, whose accumulators reach 2^30 (int8)."""
+    p = W.random_problem(25 + int4, 96, 65536, 288 if int4 else 272, 2, int4=int4, empty_frac=0.0, output_bs=60)
+    if not int4:
+        x1 = np.array(p.x1)
+        x1[:8] = -128
+        x2 = np.array(p.x2)
+        x2[:, :, :40] = -128
+        p.x1, p.x2 = x1, x2
+    _check_full(p, hints=(None, (0, 256), (0, 32), (0, 256, 3)))
+
+
 def test_zero_rows_gives_seed():
     p = W.random_problem(9, 0, 64, 64, 2, output_bs=20, bsdp=6, shared_offset=3)
     ref, _ = oracle.run(p)
