@@ -56,6 +56,7 @@ struct KParams {
   int32_t n_tiles_n;
   int32_t combine;
   int32_t* tile_ctr;    // per-XCD tile queues (kTileQueues counters, 64 bytes apart), zeroed before the GEMM
+  int32_t reduce_split; // ordered combine: workgroups (column ranges) per destination row, >= 1
 };
 
 constexpr int kTileQueues = 8;       // one per XCD
@@ -1843,19 +1844,21 @@ constexpr int kSegMax = 1024;  // longer segments take the scanning path
 // LDS in ascending order.  Rows in batches of kBatch: the batch's loads are
 // issued together (independent, streamed once), then folded in ascending
 // order; four float4 columns a kThreads apart per pass (32 loads in flight).
-__device__ void fold_sorted_rows(const KParams& p, int64_t d, const int32_t* s_sorted, int len) {
+__device__ void fold_sorted_rows(const KParams& p, int64_t d, const int32_t* s_sorted, int len, int64_t j_lo,
+                                 int64_t j_hi, bool from_out) {
   const int tid = threadIdx.x;
-  const int64_t n = p.n, n4 = n / 4;
+  const int64_t n = p.n;
   constexpr int kBatch = 8;
   typedef float v4f __attribute__((ext_vector_type(4)));
   constexpr int kCols = 4;
-  for (int64_t j0 = tid; j0 < n4; j0 += kCols * kThreads) {
+  for (int64_t j0 = j_lo + tid; j0 < j_hi; j0 += kCols * kThreads) {
     v4f v[kCols];
     bool ok[kCols];
 #pragma unroll
     for (int c = 0; c < kCols; ++c) {
-      ok[c] = j0 + c * kThreads < n4;
-      const float4 sd = ok[c] ? seed4(p, d, j0 + c * kThreads) : make_float4(0.f, 0.f, 0.f, 0.f);
+      ok[c] = j0 + c * kThreads < j_hi;
+      float4 sd = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ok[c]) sd = from_out ? *((const float4*)(p.out + d * n) + j0 + c * kThreads) : seed4(p, d, j0 + c * kThreads);
       v[c] = v4f{sd.x, sd.y, sd.z, sd.w};
     }
     for (int s0 = 0; s0 < len; s0 += kBatch) {
@@ -1882,46 +1885,82 @@ __device__ void fold_sorted_rows(const KParams& p, int64_t d, const int32_t* s_s
   }
 }
 
-// The same fold for a destination with more than kSegMax rows: walk all
-// covered rows in ascending order, kThreads at a time, per column block.
-__device__ void fold_long_segment(const KParams& p, int64_t d, int64_t covered, int32_t* s_dst) {
-  const int tid = threadIdx.x;
-  const int64_t n = p.n, n4 = n / 4;
-  for (int64_t j4b = 0; j4b < n4; j4b += kThreads) {
-    const int64_t j4 = j4b + tid;
-    float4 v = j4 < n4 ? seed4(p, d, j4) : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int64_t i0 = 0; i0 < covered; i0 += kThreads) {
-      const int64_t i = i0 + tid;
-      s_dst[tid] = i < covered ? (int32_t)dest_row(p, i) : -1;
-      __syncthreads();
-      const int cnt = (int)min((int64_t)kThreads, covered - i0);
-      if (j4 < n4) {
-        for (int c = 0; c < cnt; ++c) {
-          if (s_dst[c] != d) continue;
-          const float4 y = *(const float4*)(p.y + (i0 + c) * n + j4 * 4);
-          v.x = v.x + y.x;
-          v.y = v.y + y.y;
-          v.z = v.z + y.z;
-          v.w = v.w + y.w;
-        }
-      }
-      __syncthreads();
+// The same fold for a destination with more than kSegMax rows: the covered
+// rows are walked in ascending order, kSegMax at a time; each chunk's rows
+// sent to d (found with a count per thread and a block-wide scan, so they
+// come out ascending) are folded onto the running sum, which waits in out
+// between chunks (the first chunk starts from the seed) -- the additions are
+// the same, in the same order, as one fold over all the rows.  Each thread
+// reads back only the out elements it wrote itself.
+__device__ void fold_long_chunked(const KParams& p, int64_t d, int64_t covered, int32_t* s_rows, int32_t* s_wave,
+                                  int64_t j_lo, int64_t j_hi) {
+  constexpr int PER = kSegMax / kThreads;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  bool started = false;
+  for (int64_t c0 = 0; c0 < covered; c0 += kSegMax) {
+    const int64_t i0 = c0 + (int64_t)tid * PER;
+    uint32_t hits = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (i0 + u < covered && dest_row(p, i0 + u) == d) hits |= 1u << u;
+    const int mine = __popc(hits);
+    int incl = mine;  // inclusive scan over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
     }
-    if (j4 < n4) *(float4*)(p.out + d * n + j4 * 4) = v;
+    if (lane == 63) s_wave[wv] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+      const int t = s_wave[w];
+      before += w < wv ? t : 0;
+      total += t;
+    }
+    int pos = before + incl - mine;
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if ((hits >> u) & 1u) s_rows[pos++] = (int32_t)(i0 + u);
+    __syncthreads();
+    if (total > 0 || (!started && c0 + kSegMax >= covered)) {
+      fold_sorted_rows(p, d, s_rows, total, j_lo, j_hi, started);
+      started = true;
+    }
+    __syncthreads();  // s_rows and s_wave are rewritten by the next chunk
   }
 }
 
-// One workgroup per destination row (grid-stride).  The destination's rows
-// (unordered after the scatter) are ranked in LDS -- ranks are unique because
-// row ids are -- then every column folds seed + y[rows] in ascending order.
+// Work item w of an ordered reduce: destination w / reduce_split and its
+// float4 columns [lo, hi), part w % reduce_split of the row.
+struct FoldItem {
+  int64_t d, lo, hi;
+};
+__device__ __forceinline__ FoldItem fold_item(const KParams& p, int64_t w) {
+  const int64_t n4 = p.n / 4, parts = p.reduce_split;
+  const int64_t chunk = (n4 + parts - 1) / parts;
+  FoldItem f;
+  f.d = w / parts;
+  f.lo = min(n4, (w % parts) * chunk);
+  f.hi = min(n4, f.lo + chunk);
+  return f;
+}
+
+// One work item (destination row, or a column range of it) per workgroup,
+// grid-stride.  The destination's rows (unordered after the scatter) are
+// ranked in LDS -- ranks are unique because row ids are -- then every column
+// folds seed + y[rows] in ascending order.
 __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p, const int32_t* offsets, const int32_t* list) {
   __shared__ int32_t s_src[kSegMax];
   __shared__ int32_t s_sorted[kSegMax];
-  __shared__ int32_t s_dst[kThreads];
+  __shared__ int32_t s_wave[kThreads / 64];
   __shared__ int64_t s_red[kThreads];
   const int tid = threadIdx.x;
   int64_t covered = -1;
-  for (int64_t d = blockIdx.x; d < p.output_bs; d += gridDim.x) {
+  for (int64_t w = blockIdx.x; w < p.output_bs * p.reduce_split; w += gridDim.x) {
+    const FoldItem f = fold_item(p, w);
+    const int64_t d = f.d;
     const int32_t beg = offsets[d];
     const int32_t len = offsets[d + 1] - beg;
     if (len <= kSegMax) {
@@ -1934,11 +1973,11 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p, const int32
         s_sorted[rank] = x;
       }
       __syncthreads();
-      fold_sorted_rows(p, d, s_sorted, len);
+      fold_sorted_rows(p, d, s_sorted, len, f.lo, f.hi, false);
       __syncthreads();
     } else {
       if (covered < 0) covered = block_covered_rows(p, s_red);
-      fold_long_segment(p, d, covered, s_dst);
+      fold_long_chunked(p, d, covered, s_sorted, s_wave, f.lo, f.hi);
     }
   }
 }
@@ -1952,12 +1991,13 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p, const int32
 constexpr int kScanPerThread = 16, kScanRows = kThreads * kScanPerThread;
 __global__ __launch_bounds__(kThreads) void reduce_scan_kernel(KParams p) {
   __shared__ int32_t s_rows[kSegMax];
-  __shared__ int32_t s_dst[kThreads];
   __shared__ int32_t s_wave[kThreads / 64];
   __shared__ int64_t s_red[kThreads];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t covered = block_covered_rows(p, s_red);
-  for (int64_t d = blockIdx.x; d < p.output_bs; d += gridDim.x) {
+  for (int64_t w = blockIdx.x; w < p.output_bs * p.reduce_split; w += gridDim.x) {
+    const FoldItem f = fold_item(p, w);
+    const int64_t d = f.d;
     int len = 0;  // rows found so far (the same in every thread)
     for (int64_t c0 = 0; c0 < covered; c0 += kScanRows) {
       const int64_t i0 = c0 + (int64_t)tid * kScanPerThread;
@@ -2017,8 +2057,12 @@ __global__ __launch_bounds__(kThreads) void reduce_scan_kernel(KParams p) {
       len += total;
       __syncthreads();  // s_wave is rewritten by the next chunk
     }
-    if (len <= kSegMax) fold_sorted_rows(p, d, s_rows, len);
-    else fold_long_segment(p, d, covered, s_dst);
+    if (len <= kSegMax) {
+      fold_sorted_rows(p, d, s_rows, len, f.lo, f.hi, false);
+    } else {
+      __syncthreads();  // every thread is done with this destination's first kSegMax rows
+      fold_long_chunked(p, d, covered, s_rows, s_wave, f.lo, f.hi);
+    }
     __syncthreads();  // s_rows is rewritten for the next destination
   }
 }
@@ -2138,6 +2182,15 @@ static void launch_gemm(const KParams& kp, bool int4, bool trans_b, int grid, hi
     launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineAtomic, NT, I4>(kp, int4, trans_b, cont, gd, bd, dyn, s);
 }
 
+// Work items per destination row of the ordered reduce.  Destinations of
+// more than kSegMax rows on average are folded in chunks, one serial chain
+// of additions per column; their columns are then split over up to 16
+// workgroups (kThreads float4 columns each), so that more chains run at once.
+static int32_t ordered_reduce_split(int64_t m, int64_t output_bs, int64_t n) {
+  if (output_bs <= 0 || m <= (int64_t)kSegMax * output_bs) return 1;
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(16, (n / 4) / kThreads));
+}
+
 int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* stream, void* const* gemm_events) {
   hipStream_t s = (hipStream_t)stream;
   const TileShape ts = tile_shape(plan.tile);
@@ -2166,6 +2219,7 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
   kp.row_index_i32 = a.row_index_i32;
   kp.n_tiles_n = (int32_t)((a.n + ts.bn - 1) / ts.bn);
   kp.combine = plan.combine;
+  kp.reduce_split = ordered_reduce_split(a.m, a.output_bs, a.n);
   const MxPad mp = mx_pad(a.mx, a.m, a.k, a.n, a.e);
   const Workspace w = workspace_layout(a.m, a.n, a.output_bs, plan.combine == kCombineOrdered, mp.a_bytes, mp.b_bytes);
   char* ws = (char*)workspace;
@@ -2261,7 +2315,7 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
     }
   }
   if (plan.combine == kCombineOrdered) {
-    const int gr = (int)std::min<int64_t>(65535, a.output_bs);
+    const int gr = (int)std::min<int64_t>(65535, a.output_bs * kp.reduce_split);
     if (plan.scan_reduce)
       hipLaunchKernelGGL(reduce_scan_kernel, dim3(gr > 0 ? gr : 1), dim3(kThreads), 0, s, kp);
     else

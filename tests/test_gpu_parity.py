@@ -221,6 +221,17 @@ def test_long_segment_path():
     _check_full(p, hints=(None, (0, 0, 0, 1), (0, 0, 0, 2)))
 
 
+def test_long_segments_split_columns():
+    """Destinations averaging more than 1024 rows: each destination's fold
+    runs over chunks of the covered rows with the running sum kept in out, and
+    its columns are split over several workgroups; one destination receives
+    no row (seed only), rows past the groups stay out."""
+    p = W.random_problem(67, 5000, 64, 2048, 3, output_bs=3, bsdp=2, shared_offset=1, uncovered=300)
+    rng = np.random.default_rng(68)
+    p.row_index[:] = rng.integers(0, 2, size=p.m)
+    _check_full(p, hints=(None, (0, 0, 0, 1), (0, 0, 0, 2), (0, 256, 4, 2)))
+
+
 def test_many_destinations_scan_in_chunks():
     """output_bs above the index scan's LDS chunk (32768 destinations): the
     offsets are built over several chunks with a carry."""
