@@ -166,3 +166,40 @@ def test_mx_producer_feeds_the_mx_matmul():
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     assert (np.abs(got - ref) <= bound).all()
+
+
+# ---------------------------------------------------------------- seeded sweep
+
+N_SWEEP = 60
+
+
+def _sweep_case(i):
+    rng = np.random.default_rng(29000 + i)
+    mode = ("int8", "int8", "fp8", "mx")[int(rng.integers(0, 4))]
+    T = int(rng.choice([0, 1, 33, 500, 2000]))
+    K = int(rng.integers(1, 9))
+    e = int(rng.choice([1, 4, 32, 300, 1024]))
+    off = int(rng.choice([0, 0, 8]))
+    n_gate = e + off + int(rng.choice([0, 0, 5]))
+    K = min(K, n_gate)
+    k = (64 * int(rng.integers(1, 65))) if mode == "mx" else (16 * int(rng.integers(1, 260)))
+    rp = W.route_problem(29000 + i, T, k, K, e, n_gate=n_gate, expert_offset=off,
+                         ids_dtype=np.int32 if rng.random() < 0.4 else np.int64,
+                         with_weights=bool(rng.random() < 0.8), group_list_type=int(rng.integers(0, 2)),
+                         zero_tokens=int(rng.integers(0, 3)) if T else 0, repeat_slots=bool(rng.random() < 0.2))
+    rp.mode = mode
+    return rp, (torch.int32 if rng.random() < 0.3 else torch.int64)
+
+
+@pytest.mark.parametrize("i", range(N_SWEEP))
+def test_quant_permute_sweep(i):
+    """Seeded draws of tokens, hidden size, top-K, expert count and offset
+    (ids of other ranks), id and rowIndex types, weights or none, groupList
+    type, zero tokens, repeated experts and the output encoding (int8, FP8,
+    MX): every output bit-exact."""
+    rp, ri_dtype = _sweep_case(i)
+    got = _run_gpu(rp, ri_dtype)
+    ref = Q.run(rp)
+    if rp.topk_weights is None:
+        assert got["logit"] is None
+    _compare(rp, got, ref)
