@@ -302,7 +302,8 @@ TileId choose_tile(const gmmfr_args* a, const Derived& d, int cu_count) {
     // Measured on the prefill shape: FP8 -3% (weights (e,k,n)) and -8%
     // ((e,n,k)) with the 256-row tile; MxA8W4 +0.5%, so it keeps 128 rows.
     const int64_t hint = a->tuning_config_len > 1 ? a->tuning_config[1] : 0;
-    if (hint == 256 || (hint == 0 && big_ok && d.fp8)) return kTileMx256;
+    if (hint == 256 || (hint == 0 && big_ok && d.fp8))
+      return (d.fp8 && d.k % 128 == 0) ? kTileFp8x256k128 : kTileMx256;
     return kTile128x256;
   }
   // The 256-row tile copies 128 k per stage (two stages) where it can: int8

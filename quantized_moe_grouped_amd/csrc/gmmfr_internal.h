@@ -20,7 +20,8 @@ enum TileId : int32_t {
   kTile256x256k64 = 4,  // BM=256 BN=256 BK=64, 4x2 waves of 64x128 (512 threads), 4 stages, 1 workgroup per CU
   kTileMx256 = 5,       // FP8 / MxA8W4: BM=256 BN=256 BK=64, 4x2 waves of 64x128 (512 threads), 1 workgroup
                         // per CU (the FP8 kernels' other tile is kTile128x256)
-  kNumTiles = 6
+  kTileFp8x256k128 = 6, // FP8 with k % 128 == 0: as kTileMx256 with BK=128, 2 stages
+  kNumTiles = 7
 };
 
 struct TileShape {

@@ -1183,16 +1183,21 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // Measured on the device: with both operands FP8, B lane l holds column l%32
 // with the byte layout of A.
 // BM_ = 128 (NT = 256, two workgroups per CU) or 256 (NT = 512, eight waves
-// of 64 x 128, one workgroup per CU).
-template <int COMBINE, bool B8, bool BKN, int BM_ = 128, int NT = kThreads>
+// of 64 x 128, one workgroup per CU); WN_ waves across the tile's columns;
+// BK_ = 64, or 128 (FP8 only: two 64-k MFMA slices per stage, two stages).
+template <int COMBINE, bool B8, bool BKN, int BM_ = 128, int NT = kThreads, int WN_ = 2, int BK_ = 64>
 __global__ __launch_bounds__(NT, NT == kThreads ? 2 : 1) void mx_gemm_kernel(KParams p) {
   // BKN (FP8 only): weights given (e,k,n); a B stage then holds BK weight rows
   // of BN bytes, laid out and read with the int8 kernel's transpose reads
   static_assert(!BKN || B8, "the (e,k,n) weight layout is an FP8 mode");
-  constexpr int BM = BM_, BN = 256, BK = 64, STAGES = B8 ? 3 : 4;
+  constexpr int BM = BM_, BN = 256, BK = BK_, STAGES = B8 ? (BK_ == 128 ? 2 : 3) : 4;
+  static_assert(BK == 64 || (B8 && BK == 128), "128 k per stage: FP8 only");
+  constexpr int KSUB = BK / 64;  // 64-k MFMA slices per stage
   constexpr int NWAVES = NT / 64;
-  constexpr int WAVES_N = 2, WTM = 64, WTN = 128, FM = 2, FN = 4;
-  static_assert(BM == WTM * (NWAVES / WAVES_N) && BN == WTN * WAVES_N, "waves cover the tile");
+  constexpr int WAVES_N = WN_, WAVES_M = NWAVES / WAVES_N;
+  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 32, FN = WTN / 32;
+  static_assert(WAVES_M * WAVES_N == NWAVES && FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0,
+                "waves cover the tile");
   constexpr int A_BYTES = BM * BK;         // fp8: one byte per k
   constexpr int B_COLB = B8 ? BK : BK / 2;  // fp8: 64 bytes per column and k-step; fp4: 32
   constexpr int B_BYTES = BN * B_COLB;
@@ -1204,7 +1209,7 @@ __global__ __launch_bounds__(NT, NT == kThreads ? 2 : 1) void mx_gemm_kernel(KPa
   // their column copies; with 512 threads waves 4-7 copy the rows, so every
   // wave issues one scale copy per pair of slices.
   constexpr bool SC_SPLIT = NT == BM + BN;
-  static_assert(SC_SPLIT || (NT == BN && BM <= NT), "scale copies cover the rows and columns");
+  static_assert(B8 || SC_SPLIT || (NT == BN && BM <= NT), "scale copies cover the rows and columns");
   // Copies per thread and k-slice: A and B.  MX: a scale dword holds the
   // block scales of two k-slices, so even slices add one B-scale dword copy
   // per thread (waves 0-1 also an A-scale dword) into a ring of SC_SLOTS slots
@@ -1299,7 +1304,7 @@ __global__ __launch_bounds__(NT, NT == kThreads ? 2 : 1) void mx_gemm_kernel(KPa
 #pragma unroll
     for (int q = 0; q < A_INSTR; ++q) {
       const int slot = (q * NWAVES + wave) * 64 + lane;
-      const int r = slot / 4, cpos = slot % 4;
+      const int r = slot / (BK / 16), cpos = slot % (BK / 16);
       const int64_t row = min(c.row0 + r, p.m - 1);  // rows past the group: loaded, never stored
       a_off[q] = (uint32_t)((row - c.row0) * k + ((cpos ^ swz_a<BK>(r)) * 16));
       if ((cpos ^ swz_a<BK>(r)) >= 2) a_tail_mask |= 1u << q;
@@ -1420,7 +1425,7 @@ __global__ __launch_bounds__(NT, NT == kThreads ? 2 : 1) void mx_gemm_kernel(KPa
   };
 
   // one k-step on stage st (tile-local k-step kt): fragment reads, 8 MFMAs
-  auto compute = [&](int st, int kt, int gs, int pr, v16f (&acc)[FM][FN]) {
+  auto compute = [&](int st, int sub, int kt, int gs, int pr, v16f (&acc)[FM][FN]) {
     // scale dword of row or column q: ring slot of this slice's pair, or (8-slice
     // groups) word (kt/2)%4 of the group's slot
     const uint32_t* sca = &sSA[0][0];
@@ -1438,8 +1443,9 @@ __global__ __launch_bounds__(NT, NT == kThreads ? 2 : 1) void mx_gemm_kernel(KPa
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = wm * WTM + i * 32 + (lane & 31);
-      const v4i lo = *(const LDS_PTR(v4i))(a_st + r * BK + ((h ^ swz_a<BK>(r)) << 4));
-      v4i hi = *(const LDS_PTR(v4i))(a_st + r * BK + (((2 + h) ^ swz_a<BK>(r)) << 4));
+      // slice sub of the stage: 16-byte chunks 4 sub + h and 4 sub + 2 + h of row r
+      const v4i lo = *(const LDS_PTR(v4i))(a_st + r * BK + ((((sub << 2) | h) ^ swz_a<BK>(r)) << 4));
+      v4i hi = *(const LDS_PTR(v4i))(a_st + r * BK + ((((sub << 2) | (2 + h)) ^ swz_a<BK>(r)) << 4));
       if (tail) hi = v4i{0, 0, 0, 0};
       af[i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       sa[i] = B8 ? 127 : (int)(sc_word(sca, BM, r) >> sel);
@@ -1454,7 +1460,7 @@ __global__ __launch_bounds__(NT, NT == kThreads ? 2 : 1) void mx_gemm_kernel(KPa
         v4i half[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const int r = kk * 32 + h * 16 + ((lane & 15) >> 1);
+          const int r = sub * 64 + kk * 32 + h * 16 + ((lane & 15) >> 1);
           const int col = wn * WTN + jj * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
           const int8_t* a0 = b_st + r * BN + (((col >> 4) ^ swz_b(r)) << 4) + (col & 15);
           const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_PTR(v2i))(a0));
@@ -1464,8 +1470,8 @@ __global__ __launch_bounds__(NT, NT == kThreads ? 2 : 1) void mx_gemm_kernel(KPa
         bf[jj] = v8i{half[0].x, half[0].y, half[0].z, half[0].w, half[1].x, half[1].y, half[1].z, half[1].w};
         sb[jj] = 127;
       } else if constexpr (B8) {
-        const v4i lo = *(const LDS_PTR(v4i))(b_st + cl * BK + ((h ^ swz_a<BK>(cl)) << 4));
-        const v4i hi = *(const LDS_PTR(v4i))(b_st + cl * BK + (((2 + h) ^ swz_a<BK>(cl)) << 4));
+        const v4i lo = *(const LDS_PTR(v4i))(b_st + cl * BK + ((((sub << 2) | h) ^ swz_a<BK>(cl)) << 4));
+        const v4i hi = *(const LDS_PTR(v4i))(b_st + cl * BK + ((((sub << 2) | (2 + h)) ^ swz_a<BK>(cl)) << 4));
         bf[jj] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         sb[jj] = 127;
       } else {
@@ -1622,7 +1628,8 @@ __global__ __launch_bounds__(NT, NT == kThreads ? 2 : 1) void mx_gemm_kernel(KPa
           issue_stage(stage == 0 ? STAGES - 1 : stage - 1, fkt, gfill, pfill - 1);
           ++gfill;
           if ((kt & 1) == 0) ++puse;
-          compute(stage, kt, gstep, puse - 1, acc);
+#pragma unroll
+          for (int sub = 0; sub < KSUB; ++sub) compute(stage, sub, kt, gstep, puse - 1, acc);
           ++gstep;
           stage = stage + 1 == STAGES ? 0 : stage + 1;
         }
@@ -1667,7 +1674,8 @@ __global__ __launch_bounds__(NT, NT == kThreads ? 2 : 1) void mx_gemm_kernel(KPa
         lds_barrier();
         if (kt + STAGES - 1 < ktiles)
           issue_stage((kt + STAGES - 1) % STAGES, kt + STAGES - 1, kt + STAGES - 1, (kt + STAGES - 1) / 2);
-        compute(kt % STAGES, kt, kt, kt / 2, acc);
+#pragma unroll
+        for (int sub = 0; sub < KSUB; ++sub) compute(kt % STAGES, sub, kt, kt, kt / 2, acc);
       }
       __builtin_amdgcn_s_setprio(0);
       epilogue(c, 0, acc);
@@ -2075,13 +2083,16 @@ TileShape tile_shape(TileId id) {
     case kTile256x256: return {256, 256, 128};
     case kTile256x256k64:
     case kTileMx256: return {256, 256, 64};
+    case kTileFp8x256k128: return {256, 256, 128};
     case kTile128x256: return {128, 256, 64};
     case kTile64x256: return {64, 256, 64};
     default: return {32, 256, 64};
   }
 }
 
-int tile_occupancy(TileId id) { return id == kTile256x256 || id == kTile256x256k64 || id == kTileMx256 ? 1 : 2; }
+int tile_occupancy(TileId id) {
+  return id == kTile256x256 || id == kTile256x256k64 || id == kTileMx256 || id == kTileFp8x256k128 ? 1 : 2;
+}
 
 int tile_stages(TileId id) { return id == kTile256x256 ? 2 : id == kTile256x256k64 ? 4 : 3; }
 
@@ -2096,6 +2107,8 @@ const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool
   const bool big = id == kTileMx256;
   if (mx) return big ? "mx_gemm_kernel<256,256,64,4x2,s4,fp8xfp4>" : "mx_gemm_kernel<128,256,64,2x2,s4,fp8xfp4>";
   if (fp8) {
+    if (id == kTileFp8x256k128)
+      return trans_b ? "mx_gemm_kernel<256,256,128,4x2,s2,fp8xfp8>" : "mx_gemm_kernel<256,256,128,4x2,s2,fp8xfp8,kn>";
     if (big) return trans_b ? "mx_gemm_kernel<256,256,64,4x2,s3,fp8xfp8>" : "mx_gemm_kernel<256,256,64,4x2,s3,fp8xfp8,kn>";
     return trans_b ? "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8>" : "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8,kn>";
   }
@@ -2116,6 +2129,7 @@ const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool
        "gmm_kernel<256,256,64,4x2,s4,i4,cont>", "gmm_kernel<256,256,64,4x2,s4,i8,tb>",
        "gmm_kernel<256,256,64,4x2,s4,i8,cont,tb>"},
       {"-", "-", "-", "-", "-", "-"},  // FP8 / MxA8W4 only
+      {"-", "-", "-", "-", "-", "-"},  // FP8 only
   };
   const TileShape ts = tile_shape(id);
   const bool cont = uses_continuous_pipeline(int4, k, ts.bm, ts.bk, tile_stages(id));
@@ -2277,7 +2291,16 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
     if (a.mx || a.fp8) {
       const int B = a.mx ? 0 : (a.trans_b ? 1 : 2);  // MxA8W4, FP8 (e,n,k), FP8 (e,k,n)
       const bool ord = kp.combine == kCombineOrdered;
-      if (plan.tile == kTileMx256) {
+      if (plan.tile == kTileFp8x256k128) {
+        const dim3 gd(plan.grid), bd(512);
+        if (B == 1) {
+          if (ord) hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, true, false, 256, 512, 2, 128>), gd, bd, dyn, s, kp);
+          else hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, true, false, 256, 512, 2, 128>), gd, bd, dyn, s, kp);
+        } else if (B == 2) {
+          if (ord) hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, true, true, 256, 512, 2, 128>), gd, bd, dyn, s, kp);
+          else hipLaunchKernelGGL((mx_gemm_kernel<kCombineAtomic, true, true, 256, 512, 2, 128>), gd, bd, dyn, s, kp);
+        }
+      } else if (plan.tile == kTileMx256) {
         const dim3 gd(plan.grid), bd(512);
         if (B == 0) {
           if (ord) hipLaunchKernelGGL((mx_gemm_kernel<kCombineOrdered, false, false, 256, 512>), gd, bd, dyn, s, kp);

@@ -515,7 +515,7 @@ def test_row_lookup_hint_is_checked():
 
 
 @pytest.mark.parametrize("maker,m,e,hint,want_m,want_name", [
-    (_fp8_args, 131072, 32, 0, 256, "mx_gemm_kernel<256,256,64,4x2,s3,fp8xfp8>"),   # large experts: eight waves
+    (_fp8_args, 131072, 32, 0, 256, "mx_gemm_kernel<256,256,128,4x2,s2,fp8xfp8>"),  # large experts: eight waves
     (_fp8_args, 4096, 8, 0, 128, "mx_gemm_kernel<128,256,64,2x2,s3,fp8xfp8>"),
     (_mx_args, 131072, 32, 0, 128, "mx_gemm_kernel<128,256,64,2x2,s4,fp8xfp4>"),    # MxA8W4 keeps 128 rows
     (_mx_args, 4096, 8, 256, 256, "mx_gemm_kernel<256,256,64,4x2,s4,fp8xfp4>"),     # unless asked
@@ -528,5 +528,15 @@ def test_fp8_tile_choice(maker, m, e, hint, want_m, want_name):
         a.tuning_config_len = 2
     info = B.PlanInfo()
     assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
-    assert (info.tile_m, info.tile_n, info.tile_k) == (want_m, 256, 64)
+    assert (info.tile_m, info.tile_n) == (want_m, 256)
+    assert info.tile_k == (128 if ",s2," in want_name else 64)
     assert info.gemm_kernel.decode() == want_name
+
+
+def test_fp8_big_tile_takes_128_k_per_stage_when_k_allows():
+    for k, want in ((2048, "mx_gemm_kernel<256,256,128,4x2,s2,fp8xfp8>"), (2112, "mx_gemm_kernel<256,256,64,4x2,s3,fp8xfp8>")):
+        a = _fp8_args(m=131072, k=k, e=32, obs=16384, x1=_fake(B.DT_FLOAT8_E4M3FN, 131072, k),
+                      x2=_fake(B.DT_FLOAT8_E4M3FN, 32, 7168, k))
+        info = B.PlanInfo()
+        assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
+        assert info.gemm_kernel.decode() == want
