@@ -21,7 +21,8 @@ enum TileId : int32_t {
   kTileMx256 = 5,       // FP8 / MxA8W4: BM=256 BN=256 BK=64, 4x2 waves of 64x128 (512 threads), 1 workgroup
                         // per CU (the FP8 kernels' other tile is kTile128x256)
   kTileFp8x256k128 = 6, // FP8 with k % 128 == 0: as kTileMx256 with BK=128, 2 stages
-  kNumTiles = 7
+  kTile128x256i4 = 7,   // int4 weights with k % 128 == 0: as kTile128x256 with BK=128, 2 stages
+  kNumTiles = 8
 };
 
 struct TileShape {

@@ -2084,6 +2084,7 @@ TileShape tile_shape(TileId id) {
     case kTile256x256k64:
     case kTileMx256: return {256, 256, 64};
     case kTileFp8x256k128: return {256, 256, 128};
+    case kTile128x256i4: return {128, 256, 128};
     case kTile128x256: return {128, 256, 64};
     case kTile64x256: return {64, 256, 64};
     default: return {32, 256, 64};
@@ -2094,7 +2095,9 @@ int tile_occupancy(TileId id) {
   return id == kTile256x256 || id == kTile256x256k64 || id == kTileMx256 || id == kTileFp8x256k128 ? 1 : 2;
 }
 
-int tile_stages(TileId id) { return id == kTile256x256 ? 2 : id == kTile256x256k64 ? 4 : 3; }
+int tile_stages(TileId id) {
+  return id == kTile256x256 || id == kTile128x256i4 ? 2 : id == kTile256x256k64 ? 4 : 3;
+}
 
 // The 32-row tile serves groups of a few dozen rows, where the dynamic
 // per-XCD queues of the tile-by-tile loop balance the uneven groups better.
@@ -2130,6 +2133,7 @@ const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool
        "gmm_kernel<256,256,64,4x2,s4,i8,cont,tb>"},
       {"-", "-", "-", "-", "-", "-"},  // FP8 / MxA8W4 only
       {"-", "-", "-", "-", "-", "-"},  // FP8 only
+      {"-", "gmm_kernel<128,256,128,2x2,s2,i4>", "-", "gmm_kernel<128,256,128,2x2,s2,i4,cont>", "-", "-"},
   };
   const TileShape ts = tile_shape(id);
   const bool cont = uses_continuous_pipeline(int4, k, ts.bm, ts.bk, tile_stages(id));
@@ -2166,8 +2170,9 @@ Workspace workspace_layout(int64_t m, int64_t n, int64_t output_bs, bool ordered
 }
 
 // The continuous pipeline exists for tiles of at least 64 rows.  Variants
-// built without int4 weights (I4 = false) are never planned for them.
-template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC, int COMB, int NT, bool I4>
+// built without int4 weights (I4 = false), or with int4 weights only
+// (I8 = false), are never planned for the others.
+template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC, int COMB, int NT, bool I4, bool I8>
 static void launch_gemm_mode(const KParams& kp, bool int4, bool trans_b, bool cont, dim3 gd, dim3 bd, size_t dyn,
                              hipStream_t s) {
   constexpr bool C = BM >= 64;
@@ -2176,24 +2181,26 @@ static void launch_gemm_mode(const KParams& kp, bool int4, bool trans_b, bool co
       if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, COMB, C, false, NT>), gd, bd, dyn, s, kp);
       else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, COMB, false, false, NT>), gd, bd, dyn, s, kp);
     }
-  } else if (trans_b) {
-    if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, C, true, NT>), gd, bd, dyn, s, kp);
-    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, false, true, NT>), gd, bd, dyn, s, kp);
-  } else {
-    if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, C, false, NT>), gd, bd, dyn, s, kp);
-    else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, false, false, NT>), gd, bd, dyn, s, kp);
+  } else if constexpr (I8) {
+    if (trans_b) {
+      if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, C, true, NT>), gd, bd, dyn, s, kp);
+      else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, false, true, NT>), gd, bd, dyn, s, kp);
+    } else {
+      if (C && cont) hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, C, false, NT>), gd, bd, dyn, s, kp);
+      else hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, COMB, false, false, NT>), gd, bd, dyn, s, kp);
+    }
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC, int NT = kThreads, bool I4 = true>
+template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC, int NT = kThreads, bool I4 = true, bool I8 = true>
 static void launch_gemm(const KParams& kp, bool int4, bool trans_b, int grid, hipStream_t s) {
   const dim3 gd(grid), bd(NT);
   const size_t dyn = ((size_t)(2 * kp.e + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
   const bool cont = uses_continuous_pipeline(int4, kp.k, BM, BK, ST);
   if (kp.combine == kCombineOrdered)
-    launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineOrdered, NT, I4>(kp, int4, trans_b, cont, gd, bd, dyn, s);
+    launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineOrdered, NT, I4, I8>(kp, int4, trans_b, cont, gd, bd, dyn, s);
   else
-    launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineAtomic, NT, I4>(kp, int4, trans_b, cont, gd, bd, dyn, s);
+    launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineAtomic, NT, I4, I8>(kp, int4, trans_b, cont, gd, bd, dyn, s);
 }
 
 // Work items per destination row of the ordered reduce.  Destinations of
@@ -2329,6 +2336,9 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
       case kTile256x256: launch_gemm<256, 256, 128, 4, 2, 2, 1, 512, false>(kp, a.int4, a.trans_b, plan.grid, s); break;
       case kTile256x256k64: launch_gemm<256, 256, 64, 4, 2, 4, 1, 512>(kp, a.int4, a.trans_b, plan.grid, s); break;
       case kTile128x256: launch_gemm<128, 256, 64, 2, 2, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;
+      case kTile128x256i4:
+        launch_gemm<128, 256, 128, 2, 2, 2, 2, kThreads, true, false>(kp, a.int4, a.trans_b, plan.grid, s);
+        break;
       case kTile64x256: launch_gemm<64, 256, 64, 1, 4, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;
       default: launch_gemm<32, 256, 64, 1, 4, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;
     }

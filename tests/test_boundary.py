@@ -540,3 +540,16 @@ def test_fp8_big_tile_takes_128_k_per_stage_when_k_allows():
         info = B.PlanInfo()
         assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
         assert info.gemm_kernel.decode() == want
+
+
+@pytest.mark.parametrize("k,want", [
+    (2048, "gmm_kernel<128,256,128,2x2,s2,i4,cont>"),   # 128 k per stage, two stages
+    (128, "gmm_kernel<128,256,128,2x2,s2,i4>"),         # one k-step: tile by tile
+    (2112, "gmm_kernel<128,256,64,2x2,s3,i4,cont>"),    # k % 128 != 0: 64 k, three stages
+])
+def test_int4_128_row_tile_stage_depth(k, want):
+    a = _args(m=32768, k=k, e=64, obs=4096, int4=True)
+    info = B.PlanInfo()
+    assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
+    assert info.gemm_kernel.decode() == want
+    assert info.tile_k == (128 if ",s2," in want else 64)

@@ -85,6 +85,9 @@ CASES = {
     "long_k_i32_index_bf16_shared": dict(seed=16, m=900, k=256, n=528, e=4, row_index_dtype=np.int32,
                                          scale_bf16=True, output_bs=450, bsdp=100, shared_offset=350),
     "long_k_many_empty": dict(seed=17, m=1500, k=192, n=256, e=40, empty_frac=0.7, output_bs=400, uncovered=20),
+    # int4 weights with k % 128 == 0: the 128-row tile's 128-k stages
+    "int4_k512": dict(seed=21, m=1300, k=512, n=544, e=4, int4=True, empty_frac=0.0, output_bs=450, bsdp=30,
+                      shared_offset=100),
     # k % 128 == 0 with more k-steps than stages: the 256-row tile's 128-k stages past its prologue
     "k512_256_row_tiles": dict(seed=19, m=1400, k=512, n=528, e=4, empty_frac=0.0, output_bs=500, bsdp=80,
                                shared_offset=60),
