@@ -99,7 +99,11 @@ typedef struct {
 typedef enum {
   GMMFR_COMBINE_AUTO = 0,     /* library picks the fastest strategy            */
   GMMFR_COMBINE_ATOMIC = 1,   /* fp32 atomic adds from the GEMM epilogue       */
-  GMMFR_COMBINE_ORDERED = 2   /* rows sorted by destination, ordered reduction */
+  GMMFR_COMBINE_ORDERED = 2,  /* rows sorted by destination, ordered reduction */
+  GMMFR_COMBINE_HYBRID = 3    /* reported by the plan only (not a request):
+                                 some 256-column tiles by atomics, the others
+                                 by the ordered reduction, which then overlaps
+                                 the atomics with the GEMM; order unspecified */
 } gmmfr_combine;
 
 /* Arguments.  Names follow the operator's parameter list. */
@@ -169,10 +173,16 @@ typedef struct {
    * rejected (ATTR).  Element 3 (ours, for tests) picks how the ordered
    * combine finds each destination's rows: 0 by problem size, 1 a bucket
    * index, 2 a scan of rowIndex per destination; other values are rejected
-   * (ATTR).  Results never depend on elements 0-3: the int32
-   * accumulators and the ordered combine are bit-identical for any value,
-   * the unordered combine differs only in the order of its additions.  May
-   * be NULL.                                                                  */
+   * (ATTR).  Element 4 (ours, for tuning and tests), if present and
+   * non-zero, asks for the hybrid combine with that many atomic column tiles
+   * in every 8 consecutive 256-column tiles (1 .. 7; other values ATTR); it is
+   * honoured only with combine AUTO, deterministic = 0, int8 or int4 weights
+   * and a GEMM tile and k that run the continuous copy pipeline with it
+   * (256 x 256 with k % 128 == 0, or 128 x 256), and ignored elsewhere.  AUTO
+   * alone never takes the hybrid combine.  Results never depend on elements 0-4:
+   * the int32 accumulators and the ordered combine are bit-identical for any
+   * value, the unordered combines differ only in the order of their
+   * additions.  May be NULL.                                                  */
   const int64_t* tuning_config;
   int64_t tuning_config_len;
 } gmmfr_args;
@@ -233,13 +243,15 @@ int gmm_finalize_routing_noalloc(const gmmfr_args* args, void* stream);
 
 /* Description of the plan stage 2 would use for `args` (host only). */
 typedef struct {
-  int32_t combine;          /* gmmfr_combine actually used (ATOMIC or ORDERED) */
+  int32_t combine;          /* gmmfr_combine actually used (ATOMIC, ORDERED or
+                               HYBRID)                                         */
   int32_t tile_m, tile_n;   /* GEMM block tile                                 */
   int32_t tile_k;           /* k step per pipeline stage                       */
   int32_t grid;             /* workgroups of the grouped GEMM launch           */
   int32_t int4_weights;     /* 1 if x2 is int4                                 */
   int64_t workspace_bytes;
   char gemm_kernel[96];     /* symbol-like name of the GEMM kernel variant     */
+  int32_t hybrid_atomic;    /* HYBRID: atomic column tiles in every 8, else 0  */
 } gmmfr_plan_info;
 
 int gmm_finalize_routing_plan(const gmmfr_args* args, gmmfr_plan_info* info);

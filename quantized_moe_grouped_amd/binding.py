@@ -21,6 +21,7 @@ STATUS_NAMES = {0: "OK", 1: "NULLPTR", 2: "DTYPE", 3: "SHAPE", 4: "ATTR", 5: "UN
 DT_NONE, DT_INT8, DT_INT4, DT_INT32, DT_INT64, DT_FLOAT32, DT_BFLOAT16 = range(7)
 DT_FLOAT8_E4M3FN, DT_FLOAT4_E2M1X2, DT_FLOAT8_E8M0 = 7, 8, 9
 COMBINE = {"auto": 0, "atomic": 1, "ordered": 2}
+COMBINE_HYBRID = 3  # reported by the plan only
 
 EXPORTED = ("gmm_finalize_routing_workspace", "gmm_finalize_routing", "gmm_finalize_routing_profiled",
             "gmm_finalize_routing_plan", "gmmfr_status_string", "gmm_quant_permute_workspace",
@@ -64,7 +65,8 @@ class QpArgs(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("combine", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("tile_k", ctypes.c_int32), ("grid", ctypes.c_int32), ("int4_weights", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_int64), ("gemm_kernel", ctypes.c_char * 96)]
+                ("workspace_bytes", ctypes.c_int64), ("gemm_kernel", ctypes.c_char * 96),
+                ("hybrid_atomic", ctypes.c_int32)]
 
 
 _lib = None
@@ -193,9 +195,10 @@ def plan(args: Args) -> dict:
     st = lib().gmm_finalize_routing_plan(ctypes.byref(args), ctypes.byref(info))
     if st != OK:
         raise GmmfrError(st, "gmm_finalize_routing_plan")
-    return {"combine": {1: "atomic", 2: "ordered"}[info.combine], "tile_m": info.tile_m, "tile_n": info.tile_n,
-            "tile_k": info.tile_k, "grid": info.grid, "int4_weights": bool(info.int4_weights),
-            "workspace_bytes": int(info.workspace_bytes), "gemm_kernel": info.gemm_kernel.decode()}
+    return {"combine": {1: "atomic", 2: "ordered", 3: "hybrid"}[info.combine], "tile_m": info.tile_m,
+            "tile_n": info.tile_n, "tile_k": info.tile_k, "grid": info.grid, "int4_weights": bool(info.int4_weights),
+            "workspace_bytes": int(info.workspace_bytes), "gemm_kernel": info.gemm_kernel.decode(),
+            "hybrid_atomic": int(info.hybrid_atomic)}
 
 
 def _torch_stream(stream):

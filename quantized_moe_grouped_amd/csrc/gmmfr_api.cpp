@@ -65,6 +65,9 @@ int check_attributes(const gmmfr_args* a) {
     return GMMFR_ERR_ATTR;
   // element 3: the ordered combine's row lookup (0 = by size, 1 = bucket index, 2 = scan)
   if (a->tuning_config_len > 3 && (a->tuning_config[3] < 0 || a->tuning_config[3] > 2)) return GMMFR_ERR_ATTR;
+  // element 4: hybrid combine with that many atomic column tiles in each kHybridPeriod (0 = AUTO's choice)
+  if (a->tuning_config_len > 4 && (a->tuning_config[4] < 0 || a->tuning_config[4] >= kHybridPeriod))
+    return GMMFR_ERR_ATTR;
   return GMMFR_OK;
 }
 
@@ -352,9 +355,23 @@ bool scan_lookup(const gmmfr_args* a, const Derived& d) {
   return lookup == 2 || (lookup == 0 && d.m * d.output_bs <= kScanReduceMax);
 }
 
-Combine choose_combine(const gmmfr_args* a, const Derived& d) {
+// Whether the hybrid combine is available: AUTO, int8 or int4 weights, and a
+// tile whose continuous copy pipeline is compiled with it runs at this k.
+bool hybrid_eligible(const gmmfr_args* a, const Derived& d, TileId tile) {
+  if (a->deterministic == 1 || a->combine != GMMFR_COMBINE_AUTO || d.mx || d.fp8) return false;
+  const TileShape ts = tile_shape(tile);
+  return hybrid_compiled(tile) && uses_continuous_pipeline(d.int4, d.k, ts.bm, ts.bk, tile_stages(tile));
+}
+
+Combine choose_combine(const gmmfr_args* a, const Derived& d, TileId tile, int32_t* hybrid_atomic) {
+  *hybrid_atomic = 0;
   if (a->deterministic == 1 || a->combine == GMMFR_COMBINE_ORDERED) return kCombineOrdered;
   if (a->combine == GMMFR_COMBINE_ATOMIC) return kCombineAtomic;
+  const bool hyb_ok = hybrid_eligible(a, d, tile);
+  if (hyb_ok && a->tuning_config_len > 4 && a->tuning_config[4] > 0) {
+    *hybrid_atomic = (int32_t)a->tuning_config[4];
+    return kCombineHybrid;
+  }
   // From the shapes alone (the plan never reads device data).  Atomics
   // overlap the GEMM but slow it once they take more than about half of its
   // own time; the ordered path adds the reduce (contributions read once,
@@ -372,9 +389,9 @@ Combine choose_combine(const gmmfr_args* a, const Derived& d) {
 }
 
 int make_plan(const gmmfr_args* a, const Derived& d, int cu_count, Plan* plan) {
-  plan->combine = choose_combine(a, d);
   plan->tile = choose_tile(a, d, cu_count);
   const TileShape ts = tile_shape(plan->tile);
+  plan->combine = choose_combine(a, d, plan->tile, &plan->hybrid_atomic);
   const int64_t ntn = (d.n + ts.bn - 1) / ts.bn;
   const int64_t max_tiles = ((d.m + ts.bm - 1) / ts.bm + d.e) * ntn;
   if (max_tiles >= (int64_t(1) << 31)) return GMMFR_ERR_SHAPE;
@@ -385,10 +402,10 @@ int make_plan(const gmmfr_args* a, const Derived& d, int cu_count, Plan* plan) {
   // run many tiles in a row) is taken as given, rounded or not.
   if (a->tuning_config_len > 2 && a->tuning_config[2] > 0) grid = std::min(grid, a->tuning_config[2]);
   plan->grid = d.m > 0 ? (int32_t)grid : 0;
-  plan->scan_reduce = plan->combine == kCombineOrdered && scan_lookup(a, d);
+  const bool ordered = plan->combine != kCombineAtomic;  // y and the ordered reduce (also hybrid)
+  plan->scan_reduce = ordered && scan_lookup(a, d);
   const MxPad mp = mx_pad(d.mx, d.m, d.k, d.n, d.e);
-  plan->workspace_bytes =
-      workspace_layout(d.m, d.n, d.output_bs, plan->combine == kCombineOrdered, mp.a_bytes, mp.b_bytes).total;
+  plan->workspace_bytes = workspace_layout(d.m, d.n, d.output_bs, ordered, mp.a_bytes, mp.b_bytes).total;
   return GMMFR_OK;
 }
 
@@ -494,8 +511,10 @@ static int run_stage2(const gmmfr_args* args, void* workspace, size_t workspace_
   st = make_plan(args, d, cus, &plan);
   if (st != GMMFR_OK) return st;
   if (log_enabled())
-    std::fprintf(stderr, "[gmmfr] m=%lld k=%lld n=%lld e=%lld combine=%s %s grid=%d ws=%zu\n", (long long)d.m,
-                 (long long)d.k, (long long)d.n, (long long)d.e, plan.combine == kCombineOrdered ? "ordered" : "atomic",
+    std::fprintf(stderr, "[gmmfr] m=%lld k=%lld n=%lld e=%lld combine=%s(%d) %s grid=%d ws=%zu\n", (long long)d.m,
+                 (long long)d.k, (long long)d.n, (long long)d.e,
+                 plan.combine == kCombineOrdered ? "ordered" : plan.combine == kCombineHybrid ? "hybrid" : "atomic",
+                 plan.hybrid_atomic,
                  tile_kernel_name(plan.tile, d.int4, d.k, d.trans_b, d.mx, d.fp8), plan.grid, plan.workspace_bytes);
   const int err = launch_all(to_launch(args, d), plan, workspace, stream, gemm_events);
   return err == 0 ? GMMFR_OK : GMMFR_ERR_HIP;
@@ -537,7 +556,10 @@ int gmm_finalize_routing_plan(const gmmfr_args* args, gmmfr_plan_info* info) {
   if (st != GMMFR_OK) return st;
   const TileShape ts = tile_shape(plan.tile);
   std::memset(info, 0, sizeof(*info));
-  info->combine = plan.combine == kCombineOrdered ? GMMFR_COMBINE_ORDERED : GMMFR_COMBINE_ATOMIC;
+  info->combine = plan.combine == kCombineOrdered  ? GMMFR_COMBINE_ORDERED
+                  : plan.combine == kCombineHybrid ? GMMFR_COMBINE_HYBRID
+                                                   : GMMFR_COMBINE_ATOMIC;
+  info->hybrid_atomic = plan.combine == kCombineHybrid ? plan.hybrid_atomic : 0;
   info->tile_m = ts.bm;
   info->tile_n = ts.bn;
   info->tile_k = ts.bk;

@@ -8,7 +8,12 @@ namespace gmmfr {
 
 constexpr int kMaxExperts = 1024;
 
-enum Combine : int32_t { kCombineAtomic = 1, kCombineOrdered = 2 };
+// kCombineHybrid: of every kHybridPeriod consecutive 256-column tiles, the
+// first Plan::hybrid_atomic are combined by atomics from the GEMM epilogue
+// and the others through y and the ordered reduce (an unspecified order of
+// additions, like the atomic mode).
+enum Combine : int32_t { kCombineAtomic = 1, kCombineOrdered = 2, kCombineHybrid = 3 };
+constexpr int kHybridPeriod = 8;
 
 // GEMM tile variants compiled into the library.
 enum TileId : int32_t {
@@ -80,6 +85,7 @@ struct Plan {
   TileId tile;
   int32_t grid;             // GEMM workgroups (persistent)
   bool scan_reduce;         // ordered combine without the bucket index (small m * outputBS)
+  int32_t hybrid_atomic;    // kCombineHybrid: atomic column tiles in each kHybridPeriod (1 .. period-1)
   size_t workspace_bytes;
 };
 
@@ -98,6 +104,10 @@ int tile_stages(TileId id);
 // at least 64 rows and at least `stages` k-steps per tile) rather than the
 // tile-by-tile loop.
 bool uses_continuous_pipeline(bool int4, int64_t k, int bm, int bk, int stages);
+// Tiles whose continuous pipeline is compiled with the hybrid combine.
+bool hybrid_compiled(TileId id);
+// Float4 columns in the atomic (or the ordered) column tiles of a hybrid plan.
+int64_t hybrid_cols4(int64_t n, int atomic_tiles, bool atomic_class);
 const char* tile_kernel_name(TileId id, bool int4, int64_t k, bool trans_b, bool mx, bool fp8);
 
 }  // namespace gmmfr

@@ -57,7 +57,21 @@ struct KParams {
   int32_t combine;
   int32_t* tile_ctr;    // per-XCD tile queues (kTileQueues counters, 64 bytes apart), zeroed before the GEMM
   int32_t reduce_split; // ordered combine: workgroups (column ranges) per destination row, >= 1
+  int32_t hyb_atomic;   // hybrid combine: atomic column tiles in each kHybridPeriod (0: not hybrid)
+  int64_t n4_ord;       // float4 columns the ordered reduce folds (n / 4 unless hybrid)
+  int64_t n4_seed;      // float4 columns the seed kernel writes (n / 4 unless hybrid)
 };
+
+// Hybrid combine: float4 column of the jj-th float4 column of one class
+// (the atomic column tiles, or the ordered ones) in ascending order.  A
+// 256-column tile holds 64 float4 columns; tile nt is atomic when
+// nt % kHybridPeriod < hyb_atomic.  The identity when not hybrid.
+__device__ __forceinline__ int64_t hyb_col4(const KParams& p, int64_t jj, bool atomic_class) {
+  if (p.hyb_atomic == 0) return jj;
+  const int64_t per = atomic_class ? p.hyb_atomic : kHybridPeriod - p.hyb_atomic;
+  const int64_t b = jj >> 6;
+  return ((b / per) * kHybridPeriod + (atomic_class ? 0 : p.hyb_atomic) + b % per) * 64 + (jj & 63);
+}
 
 constexpr int kTileQueues = 8;       // one per XCD
 constexpr int kTileQueueStride = 16; // int32 elements between counters (one 64-byte line each)
@@ -543,7 +557,8 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
   // Per-row and per-column epilogue inputs of a tile into buffer `pb`, as raw
   // words.  Rows past the group or past m and columns past n read a clamped,
   // valid address; the epilogue never uses them.
-  const int ridx_words = p.row_index ? (p.row_index_i32 ? BM : 2 * BM) : 0;
+  // rowIndex words per tile: only the atomic combine reads them here
+  const int ridx_words = (COMBINE != kCombineOrdered && p.row_index) ? (p.row_index_i32 ? BM : 2 * BM) : 0;
   const int scale_words = p.scale ? (p.scale_bf16 ? BN / 2 : BN) : 0;
   auto row_word_src = [&](const TileCoord& c, int q, int words_per_row) -> int64_t {
     const int64_t row = min(c.row0 + q / words_per_row, p.m - 1);
@@ -593,7 +608,12 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
         }
       }
     };
-    auto row_off = [&](int q, int wpr) { return (int)(min(c.row0 + q / wpr, p.m - 1) - c.row0) * wpr + q % wpr; };
+    // Clamps in 32 bits against a wave-uniform limit (rows of the tile that
+    // exist in x1, columns that exist in the weight): a 64-bit per-lane row
+    // index here was spilled and reloaded behind a full memory wait per tile.
+    const int row_lim = (int)min(p.m - 1 - c.row0, (int64_t)BM);
+    const int col_lim = (int)min(n - 1 - c.col0, (int64_t)BN);
+    auto row_off = [&](int q, int wpr) { return min(q / wpr, row_lim) * wpr + q % wpr; };
     if (pts_rows)
       words((const uint32_t*)p.pertoken + c.row0, (uint32_t*)s_pts[pb], BM, [&](int q) { return row_off(q, 1); });
     if (p.logit)
@@ -605,10 +625,10 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
     if (scale_words) {
       if (p.scale_bf16)
         words((const uint32_t*)((const uint16_t*)p.scale + (int64_t)c.g * n + c.col0), s_scale[pb], scale_words,
-              [&](int q) { return (int)(min(c.col0 + 2 * q, n - 2) - c.col0) / 2; });
+              [&](int q) { return min(2 * q, col_lim - 1) / 2; });
       else
         words((const uint32_t*)p.scale + (int64_t)c.g * n + c.col0, s_scale[pb], scale_words,
-              [&](int q) { return (int)(min(c.col0 + q, n - 1) - c.col0); });
+              [&](int q) { return min(q, col_lim); });
     }
   };
   static_assert(BM <= NT && BN <= NT && 2 * BM <= 2 * NT, "one pass per tile row and column");
@@ -728,7 +748,7 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
   // full-tile epilogue (FM*FN*16 separate stores, counted at half in case the
   // compiler pairs some) the wait allows that many more; after any other
   // epilogue only the later stages (younger than stage 0 either way).
-  constexpr int FAST_STORES = COMBINE == kCombineOrdered ? FM * FN * (PACKED ? 4 : 8) : 0;
+  constexpr int FAST_STORES = COMBINE != kCombineAtomic ? FM * FN * (PACKED ? 4 : 8) : 0;
   constexpr int W0_FULL = (STAGES - 2) * LOADS_FULL + FAST_STORES < 63 ? (STAGES - 2) * LOADS_FULL + FAST_STORES : 63;
   constexpr int W0_SHORT = (STAGES - 2) * LOADS_SHORT + FAST_STORES < 63 ? (STAGES - 2) * LOADS_SHORT + FAST_STORES : 63;
   bool stores_counted = false;  // the previous epilogue took the ordered full-tile path
@@ -768,6 +788,11 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
     int wm = wave_m, wn = wave_n;
     asm volatile("" : "+v"(lane), "+s"(wm), "+s"(wn));
     const bool dump = p.acc_out != nullptr;
+    // Whether this tile's rows go to y (the ordered reduce folds them) or
+    // are added into out by atomics; per tile in the hybrid combine.
+    const bool ord_tile =
+        COMBINE == kCombineOrdered ||
+        (COMBINE == kCombineHybrid && (int)((e_col0 / BN) % kHybridPeriod) >= p.hyb_atomic);
     // Tile-local column of this lane in MFMA block j (packed int4: block 2g
     // holds the even columns of pair g, block 2g+1 the odd ones).
     auto col_of = [&](int j) {
@@ -795,7 +820,7 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
       L4 = *(const float4*)(&s_logit[pb][lr0]);
     };
     auto dests = [&](int lr0, int (&Dv)[4]) {
-      if constexpr (COMBINE == kCombineAtomic) {
+      if (!ord_tile) {
         // destination of each row from the raw rowIndex words; -1 when
         // outside [0, outputBS)
 #pragma unroll
@@ -845,7 +870,7 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
           const float Pv[4] = {P4.x, P4.y, P4.z, P4.w}, Lv[4] = {L4.x, L4.y, L4.z, L4.w};
           int Dv[4];
           dests(lr0, Dv);
-          if constexpr (COMBINE == kCombineOrdered) {
+          if (ord_tile) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               float* rowp = wave_y + (int64_t)(i * 32 + q * 8 + u) * n;
@@ -900,7 +925,7 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
             const int lr = lr0 + u;
             if (lr >= e_valid) continue;
             float* base;
-            if constexpr (COMBINE == kCombineOrdered) {
+            if (ord_tile) {
               base = p.y + (e_row0 + lr) * n;
             } else {
               if (Dv[u] < 0) continue;
@@ -915,7 +940,7 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
                 p.acc_out[(e_row0 + lr) * n + colj[j]] = a;
               }
               const float v = value(i, j, q * 4 + u, Pv[u], Lv[u]);
-              if constexpr (COMBINE == kCombineOrdered)
+              if (ord_tile)
                 __builtin_nontemporal_store(v, base + colj[j]);
               else
                 __hip_atomic_fetch_add(base + colj[j], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -924,6 +949,7 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
         }
       }
     }
+    if constexpr (COMBINE == kCombineHybrid) return fast_epi && ord_tile;
     return fast_epi;
   };
 
@@ -1717,9 +1743,10 @@ __device__ __forceinline__ float4 seed4(const KParams& p, int64_t d, int64_t j4)
 
 __global__ __launch_bounds__(kThreads) void seed_kernel(KParams p) {
   if (blockIdx.x == 0 && threadIdx.x < (int)(kCtrlBytes / 4)) p.tile_ctr[threadIdx.x] = 0;
-  const int64_t n4 = p.n / 4, total = p.output_bs * n4;
+  // every column (atomic combine) or the atomic column tiles (hybrid)
+  const int64_t ns = p.n4_seed, total = p.output_bs * ns;
   for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * kThreads) {
-    const int64_t d = idx / n4, j4 = idx % n4;
+    const int64_t d = idx / ns, j4 = hyb_col4(p, idx % ns, true);
     *(float4*)(p.out + d * p.n + j4 * 4) = seed4(p, d, j4);
   }
 }
@@ -1859,14 +1886,16 @@ __device__ void fold_sorted_rows(const KParams& p, int64_t d, const int32_t* s_s
   constexpr int kBatch = 8;
   typedef float v4f __attribute__((ext_vector_type(4)));
   constexpr int kCols = 4;
-  for (int64_t j0 = j_lo + tid; j0 < j_hi; j0 += kCols * kThreads) {
+  for (int64_t jj0 = j_lo + tid; jj0 < j_hi; jj0 += kCols * kThreads) {
     v4f v[kCols];
     bool ok[kCols];
+    int64_t jc[kCols];  // float4 column (the ordered columns' jj0 + c * kThreads-th)
 #pragma unroll
     for (int c = 0; c < kCols; ++c) {
-      ok[c] = j0 + c * kThreads < j_hi;
+      ok[c] = jj0 + c * kThreads < j_hi;
+      jc[c] = ok[c] ? hyb_col4(p, jj0 + c * kThreads, false) : 0;
       float4 sd = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (ok[c]) sd = from_out ? *((const float4*)(p.out + d * n) + j0 + c * kThreads) : seed4(p, d, j0 + c * kThreads);
+      if (ok[c]) sd = from_out ? *((const float4*)(p.out + d * n) + jc[c]) : seed4(p, d, jc[c]);
       v[c] = v4f{sd.x, sd.y, sd.z, sd.w};
     }
     for (int s0 = 0; s0 < len; s0 += kBatch) {
@@ -1877,7 +1906,7 @@ __device__ void fold_sorted_rows(const KParams& p, int64_t d, const int32_t* s_s
           const v4f* r = (const v4f*)(p.y + (int64_t)s_sorted[s0 + u] * n);
 #pragma unroll
           for (int c = 0; c < kCols; ++c)
-            if (ok[c]) yb[u][c] = __builtin_nontemporal_load(r + j0 + c * kThreads);
+            if (ok[c]) yb[u][c] = __builtin_nontemporal_load(r + jc[c]);
         }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
@@ -1889,7 +1918,7 @@ __device__ void fold_sorted_rows(const KParams& p, int64_t d, const int32_t* s_s
     }
 #pragma unroll
     for (int c = 0; c < kCols; ++c)
-      if (ok[c]) __builtin_nontemporal_store(v[c], (v4f*)(p.out + d * n) + j0 + c * kThreads);
+      if (ok[c]) __builtin_nontemporal_store(v[c], (v4f*)(p.out + d * n) + jc[c]);
   }
 }
 
@@ -1941,12 +1970,13 @@ __device__ void fold_long_chunked(const KParams& p, int64_t d, int64_t covered, 
 }
 
 // Work item w of an ordered reduce: destination w / reduce_split and its
-// float4 columns [lo, hi), part w % reduce_split of the row.
+// ordered float4 columns [lo, hi) (indices into the ordered columns, which
+// are all columns unless hybrid), part w % reduce_split of the row.
 struct FoldItem {
   int64_t d, lo, hi;
 };
 __device__ __forceinline__ FoldItem fold_item(const KParams& p, int64_t w) {
-  const int64_t n4 = p.n / 4, parts = p.reduce_split;
+  const int64_t n4 = p.n4_ord, parts = p.reduce_split;
   const int64_t chunk = (n4 + parts - 1) / parts;
   FoldItem f;
   f.d = w / parts;
@@ -2192,15 +2222,45 @@ static void launch_gemm_mode(const KParams& kp, bool int4, bool trans_b, bool co
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC, int NT = kThreads, bool I4 = true, bool I8 = true>
+// The hybrid combine is compiled for the continuous pipeline of the tiles
+// that plan it (HYB); the planner never picks it elsewhere.
+template <int BM, int BN, int BK, int WM, int WN, int ST, int OCC, int NT = kThreads, bool I4 = true, bool I8 = true,
+          bool HYB = false>
 static void launch_gemm(const KParams& kp, bool int4, bool trans_b, int grid, hipStream_t s) {
   const dim3 gd(grid), bd(NT);
   const size_t dyn = ((size_t)(2 * kp.e + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
   const bool cont = uses_continuous_pipeline(int4, kp.k, BM, BK, ST);
-  if (kp.combine == kCombineOrdered)
+  if (kp.combine == kCombineOrdered) {
     launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineOrdered, NT, I4, I8>(kp, int4, trans_b, cont, gd, bd, dyn, s);
-  else
+  } else if (kp.combine == kCombineHybrid) {
+    if constexpr (HYB && BM >= 64) {
+      if (!cont) return;
+      if (int4) {
+        if constexpr (I4)
+          hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, true, kCombineHybrid, true, false, NT>), gd, bd, dyn,
+                             s, kp);
+      } else if constexpr (I8) {
+        if (trans_b)
+          hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineHybrid, true, true, NT>), gd, bd, dyn,
+                             s, kp);
+        else
+          hipLaunchKernelGGL((gmm_kernel<BM, BN, BK, WM, WN, ST, OCC, false, kCombineHybrid, true, false, NT>), gd, bd,
+                             dyn, s, kp);
+      }
+    }
+  } else {
     launch_gemm_mode<BM, BN, BK, WM, WN, ST, OCC, kCombineAtomic, NT, I4, I8>(kp, int4, trans_b, cont, gd, bd, dyn, s);
+  }
+}
+
+bool hybrid_compiled(TileId id) { return id == kTile256x256 || id == kTile128x256 || id == kTile128x256i4; }
+
+int64_t hybrid_cols4(int64_t n, int atomic_tiles, bool atomic_class) {
+  const int64_t n4 = n / 4;
+  int64_t cnt = 0;
+  for (int64_t nt = 0; nt * 64 < n4; ++nt)
+    if (((nt % kHybridPeriod) < atomic_tiles) == atomic_class) cnt += std::min<int64_t>(64, n4 - nt * 64);
+  return cnt;
 }
 
 // Work items per destination row of the ordered reduce.  Destinations of
@@ -2240,9 +2300,14 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
   kp.row_index_i32 = a.row_index_i32;
   kp.n_tiles_n = (int32_t)((a.n + ts.bn - 1) / ts.bn);
   kp.combine = plan.combine;
-  kp.reduce_split = ordered_reduce_split(a.m, a.output_bs, a.n);
+  const bool hybrid = plan.combine == kCombineHybrid;
+  const bool ordered = plan.combine == kCombineOrdered || hybrid;  // y and the ordered reduce
+  kp.hyb_atomic = hybrid ? plan.hybrid_atomic : 0;
+  kp.n4_ord = hybrid ? hybrid_cols4(a.n, plan.hybrid_atomic, false) : a.n / 4;
+  kp.n4_seed = hybrid ? hybrid_cols4(a.n, plan.hybrid_atomic, true) : a.n / 4;
+  kp.reduce_split = ordered_reduce_split(a.m, a.output_bs, kp.n4_ord * 4);
   const MxPad mp = mx_pad(a.mx, a.m, a.k, a.n, a.e);
-  const Workspace w = workspace_layout(a.m, a.n, a.output_bs, plan.combine == kCombineOrdered, mp.a_bytes, mp.b_bytes);
+  const Workspace w = workspace_layout(a.m, a.n, a.output_bs, ordered, mp.a_bytes, mp.b_bytes);
   char* ws = (char*)workspace;
   kp.tile_ctr = (int32_t*)(ws + w.ctrl_off);
   if (mp.a_bytes > 0 && a.m > 0) {
@@ -2260,16 +2325,15 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
     kp.scale = sb;
   }
 
-  const int64_t n4 = a.n / 4;
   // the tile-by-tile loop of the int8/int4 kernel takes its tiles from
   // queues whose counters start at zero; the other loops use a static order
   const bool dynamic_queues =
       !a.mx && !a.fp8 && !(ts.bm >= 64 && uses_continuous_pipeline(a.int4, a.k, ts.bm, ts.bk, tile_stages(plan.tile)));
-  if (plan.combine == kCombineOrdered && plan.scan_reduce) {
+  if (ordered && plan.scan_reduce) {
     kp.y = (float*)(ws + w.y_off);
     if (dynamic_queues)
       hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(kThreads), 0, s, (int32_t*)nullptr, (int64_t)0, kp.tile_ctr);
-  } else if (plan.combine == kCombineOrdered) {
+  } else if (ordered) {
     kp.y = (float*)(ws + w.y_off);
     int32_t* counts = (int32_t*)(ws + w.counts_off);
     int32_t* cursor = (int32_t*)(ws + w.cursor_off);
@@ -2285,8 +2349,9 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
     } else {
       hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, cursor, a.output_bs);
     }
-  } else {
-    const int gs = (int)std::min<int64_t>(4096, (a.output_bs * n4 + kThreads - 1) / kThreads);
+  }
+  if (!ordered || hybrid) {  // out seeded where the GEMM adds by atomics
+    const int gs = (int)std::min<int64_t>(4096, (a.output_bs * kp.n4_seed + kThreads - 1) / kThreads);
     hipLaunchKernelGGL(seed_kernel, dim3(gs > 0 ? gs : 1), dim3(kThreads), 0, s, kp);
   }
   if (a.m > 0 && plan.grid > 0) {
@@ -2333,11 +2398,15 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
         }
       }
     } else switch (plan.tile) {
-      case kTile256x256: launch_gemm<256, 256, 128, 4, 2, 2, 1, 512, false>(kp, a.int4, a.trans_b, plan.grid, s); break;
+      case kTile256x256:
+        launch_gemm<256, 256, 128, 4, 2, 2, 1, 512, false, true, true>(kp, a.int4, a.trans_b, plan.grid, s);
+        break;
       case kTile256x256k64: launch_gemm<256, 256, 64, 4, 2, 4, 1, 512>(kp, a.int4, a.trans_b, plan.grid, s); break;
-      case kTile128x256: launch_gemm<128, 256, 64, 2, 2, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;
+      case kTile128x256:
+        launch_gemm<128, 256, 64, 2, 2, 3, 2, kThreads, true, true, true>(kp, a.int4, a.trans_b, plan.grid, s);
+        break;
       case kTile128x256i4:
-        launch_gemm<128, 256, 128, 2, 2, 2, 2, kThreads, true, false>(kp, a.int4, a.trans_b, plan.grid, s);
+        launch_gemm<128, 256, 128, 2, 2, 2, 2, kThreads, true, false, true>(kp, a.int4, a.trans_b, plan.grid, s);
         break;
       case kTile64x256: launch_gemm<64, 256, 64, 1, 4, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;
       default: launch_gemm<32, 256, 64, 1, 4, 3, 2>(kp, a.int4, a.trans_b, plan.grid, s); break;
@@ -2347,7 +2416,7 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
       if (er != hipSuccess) return (int)er;
     }
   }
-  if (plan.combine == kCombineOrdered) {
+  if (ordered) {
     const int gr = (int)std::min<int64_t>(65535, a.output_bs * kp.reduce_split);
     if (plan.scan_reduce)
       hipLaunchKernelGGL(reduce_scan_kernel, dim3(gr > 0 ? gr : 1), dim3(kThreads), 0, s, kp);

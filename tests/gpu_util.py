@@ -58,6 +58,36 @@ def call(p, d, out, *, deterministic=False, combine="auto", acc=None, tuning_con
         tuning_config=tuning_config, workspace=workspace, transpose_x2=getattr(p, "x2_transposed", False))
 
 
+def plan_of(p, d, *, deterministic=False, combine="auto", tuning_config=None):
+    """The plan the library takes for these arguments (host only)."""
+    import torch
+    out = torch.empty((p.output_bs, p.n), dtype=torch.float32, device="cuda")
+    args, keep = B.make_args(
+        d["x1"], d["x2"], d["group_list"], out,
+        scale=d["scale"], pertoken_scale=d["pertoken_scale"], logit=d["logit"], row_index=d["row_index"],
+        shared_input=d["shared_input"], shared_input_offset=p.shared_input_offset if p.shared_input is not None else 0,
+        group_list_type=p.group_list_type, deterministic=deterministic, combine=combine,
+        tuning_config=tuning_config, transpose_x2=getattr(p, "x2_transposed", False))
+    plan = B.plan(args)
+    del keep
+    return plan
+
+
+def hybrid_ordered_columns(n, atomic_tiles):
+    """Columns the hybrid combine folds through the ordered reduce: those of
+    the 256-column tiles nt with nt % 8 >= atomic_tiles."""
+    return (np.arange(n) // 256) % 8 >= atomic_tiles
+
+
+def assert_hybrid(got, ref, atomic_tiles):
+    """Hybrid combine: every element within the unordered tolerance, and the
+    columns of the ordered tiles bit-exact."""
+    got = np.asarray(got, dtype=np.float32)
+    assert_close_atomic(got, ref)
+    cols = hybrid_ordered_columns(got.shape[1], atomic_tiles)
+    assert_bitexact(got[:, cols], np.asarray(ref, dtype=np.float32)[:, cols])
+
+
 def run_gpu(p, d=None, *, deterministic=False, combine="auto", want_acc=False, tuning_config=None,
             acc_sentinel=-0x55555556):
     import torch

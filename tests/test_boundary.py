@@ -553,3 +553,60 @@ def test_int4_128_row_tile_stage_depth(k, want):
     assert B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info)) == B.OK
     assert info.gemm_kernel.decode() == want
     assert info.tile_k == (128 if ",s2," in want else 64)
+
+
+def _plan_with(a, tc):
+    hint = (ctypes.c_int64 * len(tc))(*tc)
+    a.tuning_config = ctypes.cast(hint, ctypes.POINTER(ctypes.c_int64))
+    a.tuning_config_len = len(tc)
+    info = B.PlanInfo()
+    st = B.lib().gmm_finalize_routing_plan(ctypes.byref(a), ctypes.byref(info))
+    return st, info
+
+
+def test_hybrid_request_is_checked():
+    """tuningConfig[4]: 0 .. 7 atomic column tiles in every 8; other values ATTR."""
+    a = _args(m=4096, n=7168, obs=512, e=8)
+    for v, want in ((0, B.OK), (1, B.OK), (7, B.OK), (8, B.ERR_ATTR), (-1, B.ERR_ATTR)):
+        assert _plan_with(a, [0, 0, 0, 0, v])[0] == want
+
+
+@pytest.mark.parametrize("m,k,e,int4,tile", [
+    (4096, 2048, 8, False, 0),      # 128-row tile, 64 k in three stages
+    (131072, 2048, 32, False, 0),   # 256-row tile, 128 k in two stages
+    (32768, 2048, 64, True, 0),     # int4 weights, 128-row tile with 128 k per stage
+    (4096, 192, 8, False, 128),     # three k-steps: the continuous pipeline's minimum
+])
+def test_hybrid_plan_where_available(m, k, e, int4, tile):
+    a = _args(m=m, k=k, e=e, obs=m // 8, int4=int4)
+    st, ordered = _plan_with(a, [0, tile])
+    assert st == B.OK
+    st, info = _plan_with(a, [0, tile, 0, 0, 3])
+    assert st == B.OK
+    assert info.combine == B.COMBINE_HYBRID and info.hybrid_atomic == 3
+    assert info.gemm_kernel.decode() == ordered.gemm_kernel.decode()
+    a.deterministic = 1  # the ordered combine's workspace
+    a.tuning_config_len = 0
+    assert _ws(a)[1] == info.workspace_bytes
+
+
+@pytest.mark.parametrize("case", ["deterministic", "atomic", "ordered", "short_k", "k64_stages", "fp8", "mx", "tile32"])
+def test_hybrid_request_ignored_elsewhere(case):
+    kw = dict(m=4096, k=2048, e=8, obs=512)
+    if case == "short_k":
+        kw["k"] = 128          # one k-step: tile by tile
+    if case == "k64_stages":
+        kw.update(m=131072, e=32, obs=16384, k=2112)  # the 256-row tile with 64 k in four stages
+    if case == "fp8":
+        a = _fp8_args(m=4096, e=8, obs=512)
+    elif case == "mx":
+        a = _mx_args(m=4096, e=8, obs=512)
+    else:
+        a = _args(**kw)
+    if case == "deterministic":
+        a.deterministic = 1
+    if case in ("atomic", "ordered"):
+        a.combine = B.COMBINE[case]
+    st, info = _plan_with(a, [0, 32 if case == "tile32" else 0, 0, 0, 3])
+    assert st == B.OK
+    assert info.combine != B.COMBINE_HYBRID and info.hybrid_atomic == 0

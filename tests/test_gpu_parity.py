@@ -170,6 +170,63 @@ def test_grid_capped_transposed_weights(name):
     _check_grid_capped(W.with_transposed_weights(W.random_problem(**CASES[name])))
 
 
+# ---------------------------------------------------------------- hybrid combine
+
+HYB_CASES = ["counts_i32_bf16_uncovered", "int4_counts_many_tiles", "full_int8_range", "long_k_no_factors",
+             "long_k_i32_index_bf16_shared", "long_k_many_empty", "int4_k512", "k512_256_row_tiles"]
+
+
+def _check_hybrid(p, splits=(1, 3, 7), tiles=None, caps=(0, 8)):
+    """The hybrid combine (tuningConfig[4] atomic column tiles in every 8):
+    the plan takes it, every output element is written, the atomic tiles'
+    columns are within the unordered tolerance and the ordered tiles'
+    columns bit-exact (the ordered combine's fold), with the grid capped or
+    not and under both row lookups."""
+    if tiles is None:  # the 256-row tile takes the hybrid combine with int8 weights and k % 128 == 0
+        tiles = (128, 256) if not p.x2_int4 and p.k % 128 == 0 else (128,)
+    ref, _ = oracle.run(p)
+    d = G.to_device(p)
+    for a in splits:
+        for tile in tiles:
+            for cap in caps:
+                tc = [0, tile, cap, 1 + (a + tiles.index(tile)) % 2, a]
+                plan = G.plan_of(p, d, tuning_config=tc)
+                assert plan["combine"] == "hybrid" and plan["hybrid_atomic"] == a, plan
+                out, _ = G.run_gpu(p, d, tuning_config=tc)
+                G.assert_hybrid(out.cpu().numpy(), ref, a)
+
+
+@pytest.mark.parametrize("name", HYB_CASES, ids=HYB_CASES)
+def test_hybrid_combine(name):
+    p = W.random_problem(**CASES[name])
+    _check_hybrid(p)
+
+
+def test_hybrid_combine_many_column_tiles():
+    """More than 8 column tiles and a ragged n tail: the second period of
+    atomic tiles and a partial last tile in either class; also with
+    transposed weights."""
+    p = W.random_problem(31, 700, 256, 2320, 3, output_bs=300, bsdp=60, shared_offset=200, uncovered=9)
+    _check_hybrid(p, splits=(1, 2, 5, 7))
+    _check_hybrid(W.with_transposed_weights(p), splits=(3,), caps=(0,))
+
+
+def test_hybrid_request_ignored_where_unavailable():
+    """tuningConfig[4] is honoured only where AUTO may take the hybrid
+    combine: deterministic calls, a forced combine and short k keep their
+    own plans and results."""
+    p = W.random_problem(**CASES["long_k_no_factors"])
+    ref, _ = oracle.run(p)
+    d = G.to_device(p)
+    assert G.plan_of(p, d, deterministic=True, tuning_config=[0, 0, 0, 0, 3])["combine"] == "ordered"
+    assert G.plan_of(p, d, combine="atomic", tuning_config=[0, 0, 0, 0, 3])["combine"] == "atomic"
+    out, _ = G.run_gpu(p, d, deterministic=True, tuning_config=[0, 0, 0, 0, 3])
+    G.assert_bitexact(out.cpu().numpy(), ref)
+    q = W.random_problem(**CASES["ragged_n_shared"])  # k = 128: the tile-by-tile loop
+    dq = G.to_device(q)
+    assert G.plan_of(q, dq, tuning_config=[0, 128, 0, 0, 3])["combine"] != "hybrid"
+
+
 def test_grid_capped_single_workgroup():
     """One workgroup runs every tile of a case with a ragged n tail, an empty
     expert and two group tails, in both loop structures."""
