@@ -716,12 +716,16 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
   // Scheduling barriers pin this order, so that neither copies (which stall
   // issue while the address unit is busy) nor LDS reads bunch up in front of
   // the matrix core.
-  auto mfma_step = [&](v4i (&af)[FM], v4i (&bf)[FN], v16i (&acc)[FM][FN], auto ND_, auto NR_, auto&& copy, auto&& read) {
-    constexpr int NM = FM * FN, ND = decltype(ND_)::value, NR = decltype(NR_)::value;
+  // NB_: row blocks of the wave that hold rows of the tile (the MFMAs of
+  // the others, all padding rows, are skipped; copies and reads stay).
+  auto mfma_step = [&](v4i (&af)[FM], v4i (&bf)[FN], v16i (&acc)[FM][FN], auto ND_, auto NR_, auto&& copy, auto&& read,
+                       auto NB_) {
+    constexpr int NM = FM * FN, ND = decltype(ND_)::value, NR = decltype(NR_)::value, NB = decltype(NB_)::value;
     constexpr int RSPAN = NM > 2 ? NM - 2 : NM;
     static_for<0, NM>([&](auto m_) {
       constexpr int m = decltype(m_)::value;
-      acc[m / FN][m % FN] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[m / FN], bf[m % FN], acc[m / FN][m % FN], 0, 0, 0);
+      if constexpr (m / FN < NB)
+        acc[m / FN][m % FN] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[m / FN], bf[m % FN], acc[m / FN][m % FN], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, ND>([&](auto d_) {
         if constexpr (decltype(d_)::value * NM / ND == m) {
@@ -1005,14 +1009,14 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
       int stage = 0;
       bool prev_fast = false;
       v16i acc[FM][FN];
-      auto kstep = [&](int kt, int fill_ks) {
+      auto kstep = [&](int kt, int fill_ks, auto NB_) {
         const int stage_next = stage + 1 == STAGES ? 0 : stage + 1;
         // substeps 0 .. KK-2, each with the fragment reads of the next one
         static_for<0, KK - 1>([&](auto kk_) {
           constexpr int kk = decltype(kk_)::value;
           auto rd = [&](auto r_) { read_item(r_, stage, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]); };
           mfma_step(af[kk & 1], bf[kk & 1], acc, std::integral_constant<int, 0>{}, std::integral_constant<int, NREAD>{},
-                    no_copy, rd);
+                    no_copy, rd, NB_);
         });
         // the next k-step's copies have landed and every wave holds this
         // stage's fragments; after the first k-step of a tile the previous
@@ -1028,19 +1032,34 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
         auto cp = [&](auto d_) { copy_item(d_, stage, fill_ks); };
         auto rd0 = [&](auto r_) { read_item(r_, stage_next, 0, af[0], bf[0]); };
         mfma_step(af[(KK - 1) & 1], bf[(KK - 1) & 1], acc, std::integral_constant<int, N_COPY>{},
-                  std::integral_constant<int, NREAD>{}, cp, rd0);
+                  std::integral_constant<int, NREAD>{}, cp, rd0, NB_);
         stage = stage_next;
+      };
+      // The tile's k-steps.  With two workgroups per CU, a wave whose 32-row
+      // blocks lie partly or wholly past the tile's valid rows (a group's
+      // last tile) skips their MFMAs, which leaves the matrix core to the
+      // other workgroup's waves on its SIMD (int4 workload GEMM -2.5%,
+      // decode -1.2%; with one workgroup per CU it measured +0.4%).
+      auto ksteps = [&](auto NB_) {
+#pragma unroll 1
+        for (int kt = 0; kt < ktiles - STAGES; ++kt) kstep(kt, kt + STAGES, NB_);
+        set_sources(nxt);  // the remaining refills fetch the next tile's first k-slices
+#pragma unroll 1
+        for (int kt = ktiles - STAGES; kt < ktiles; ++kt) kstep(kt, kt + STAGES - ktiles, NB_);
       };
       while (true) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int jj = 0; jj < FN; ++jj) acc[i][jj] = v16i{0};
-#pragma unroll 1
-        for (int kt = 0; kt < ktiles - STAGES; ++kt) kstep(kt, kt + STAGES);
-        set_sources(nxt);  // the remaining refills fetch the next tile's first k-slices
-#pragma unroll 1
-        for (int kt = ktiles - STAGES; kt < ktiles; ++kt) kstep(kt, kt + STAGES - ktiles);
+        if constexpr (FM == 2 && OCC > 1) {
+          const int live_rows = __builtin_amdgcn_readfirstlane(cur.valid_rows) - wave_m * WTM;  // wave-uniform
+          if (live_rows > 32) ksteps(std::integral_constant<int, 2>{});
+          else if (live_rows > 0) ksteps(std::integral_constant<int, 1>{});
+          else ksteps(std::integral_constant<int, 0>{});
+        } else {
+          ksteps(std::integral_constant<int, FM>{});
+        }
         // the next tile's row and column inputs go to the other buffer before
         // this tile's stores fill the copy queue
         if (t_nxt >= 0) dma_rows(nxt, pb ^ 1);
@@ -1117,7 +1136,7 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
             else read_b(stage, kk + 1, r - FM, bf[nxt_f][r - FM]);
           };
           mfma_step(af[cur_f], bf[cur_f], acc, std::integral_constant<int, 0>{},
-                    std::integral_constant<int, FM + FN>{}, no_copy, rd);
+                    std::integral_constant<int, FM + FN>{}, no_copy, rd, std::integral_constant<int, FM>{});
         } else {
           if constexpr (INT4) {
             // int4 weights fetched on entering this stage, for the stage
@@ -1166,7 +1185,7 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
           };
           __builtin_amdgcn_sched_barrier(0);
           mfma_step(af[cur_f], bf[cur_f], acc, std::integral_constant<int, N_COPY>{},
-                    std::integral_constant<int, FM + FN>{}, cp, rd);
+                    std::integral_constant<int, FM + FN>{}, cp, rd, std::integral_constant<int, FM>{});
         }
       });
       stage = stage_next;
