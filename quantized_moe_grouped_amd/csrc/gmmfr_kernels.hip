@@ -1471,17 +1471,21 @@ __global__ __launch_bounds__(NT, NT == kThreads ? 2 : 1) void mx_gemm_kernel(KPa
 
   // one k-step on stage st (tile-local k-step kt): fragment reads, 8 MFMAs
   auto compute = [&](int st, int sub, int kt, int gs, int pr, v16f (&acc)[FM][FN]) {
-    // scale dword of row or column q: ring slot of this slice's pair, or (8-slice
-    // groups) word (kt/2)%4 of the group's slot
-    const uint32_t* sca = &sSA[0][0];
-    const uint32_t* scb = &sSB[0][0];
-    auto sc_word = [&](const uint32_t* base, int rows, int q) -> uint32_t {
-      if (grp8) return base[(((gs >> 3) % G8_SLOTS) * rows + q) * 4 + ((kt >> 1) & 3)];
-      return base[(pr % SC_SLOTS) * rows + q];
-    };
+    // E8M0 scale of this lane's block of row or column q: byte 2 (kt & 1) + h
+    // of the scale dword in the ring slot of this slice's pair, or (8-slice
+    // groups) of word (kt/2)%4 of the group's slot.  Read as one byte at a
+    // lane part q * (bytes per row or column) + h plus a wave-uniform part.
+    const int sc_qmul = grp8 ? 16 : 4;
+    const int sc_kb = 2 * (kt & 1);
+    const int sc_ua = grp8 ? ((gs >> 3) % G8_SLOTS) * BM * 16 + ((kt >> 1) & 3) * 4 + sc_kb
+                           : (pr % SC_SLOTS) * BM * 4 + sc_kb;
+    const int sc_ub = grp8 ? ((gs >> 3) % G8_SLOTS) * BN * 16 + ((kt >> 1) & 3) * 4 + sc_kb
+                           : (pr % SC_SLOTS) * BN * 4 + sc_kb;
+    const LDS_PTR(const uint8_t) sca = (const LDS_PTR(const uint8_t))(const void*)&sSA[0][0];
+    const LDS_PTR(const uint8_t) scb = (const LDS_PTR(const uint8_t))(const void*)&sSB[0][0];
+    auto sc_byte = [&](const LDS_PTR(const uint8_t) base, int u, int q) -> int { return base[q * sc_qmul + h + u]; };
     const int8_t* a_st = sA + st * A_BYTES;
     const int8_t* b_st = sB + st * B_BYTES;
-    const int sel = 8 * (2 * (kt & 1) + h);  // byte of this lane's block in the scale dword
     v8i af[FM];
     int sa[FM], sb[FN];
     const bool tail = half_tail && kt == ktiles - 1;  // k 32..63 of this step lie past k: zero A there
@@ -1493,7 +1497,7 @@ __global__ __launch_bounds__(NT, NT == kThreads ? 2 : 1) void mx_gemm_kernel(KPa
       v4i hi = *(const LDS_PTR(v4i))(a_st + r * BK + ((((sub << 2) | (2 + h)) ^ swz_a<BK>(r)) << 4));
       if (tail) hi = v4i{0, 0, 0, 0};
       af[i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      sa[i] = B8 ? 127 : (int)(sc_word(sca, BM, r) >> sel);
+      sa[i] = B8 ? 127 : sc_byte(sca, sc_ua, r);
     }
     v8i bf[FN];
 #pragma unroll
@@ -1522,7 +1526,7 @@ __global__ __launch_bounds__(NT, NT == kThreads ? 2 : 1) void mx_gemm_kernel(KPa
       } else {
         const v4i w = *(const LDS_PTR(v4i))(b_st + cl * B_COLB + ((h ^ swz_b4(cl)) << 4));
         bf[jj] = v8i{w.x, w.y, w.z, w.w, 0, 0, 0, 0};
-        sb[jj] = (int)(sc_word(scb, BN, cl) >> sel);
+        sb[jj] = sc_byte(scb, sc_ub, cl);
       }
     }
 #pragma unroll
