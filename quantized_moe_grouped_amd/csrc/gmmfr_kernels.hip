@@ -60,6 +60,9 @@ struct KParams {
   int32_t hyb_atomic;   // hybrid combine: atomic column tiles in each kHybridPeriod (0: not hybrid)
   int64_t n4_ord;       // float4 columns the ordered reduce folds (n / 4 unless hybrid)
   int64_t n4_seed;      // float4 columns the seed kernel writes (n / 4 unless hybrid)
+  int32_t y_cached;     // the scan-lookup reduce with a small y: the GEMM stores y through the
+                        // caches (two workgroups per CU only) and the reduce reads it so, from the
+                        // MALL; otherwise both nontemporal
 };
 
 // Hybrid combine: float4 column of the jj-th float4 column of one class
@@ -73,6 +76,7 @@ __device__ __forceinline__ int64_t hyb_col4(const KParams& p, int64_t jj, bool a
   return ((b / per) * kHybridPeriod + (atomic_class ? 0 : p.hyb_atomic) + b % per) * 64 + (jj & 63);
 }
 
+constexpr int64_t kYCachedBytes = int64_t(160) << 20;  // y small enough to wait in the MALL
 constexpr int kTileQueues = 8;       // one per XCD
 constexpr int kTileQueueStride = 16; // int32 elements between counters (one 64-byte line each)
 constexpr int kTileBlock = 64;       // consecutive raster tiles handed to one XCD at a time
@@ -852,6 +856,13 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
       v = v * lv;
       return v;
     };
+    // y stores: nontemporal, or through the caches when the reduce will read
+    // a small y back from the MALL (kernels with two workgroups per CU only)
+    const bool y_nt = OCC == 1 || !p.y_cached;
+    auto store_y = [&](auto* ptr, auto v) {
+      if (y_nt) __builtin_nontemporal_store(v, ptr);
+      else *ptr = v;
+    };
     const bool fast_epi = e_valid == BM && e_col0 + BN <= n && n < (int64_t(1) << 28) && !dump;
     if (fast_epi) {
       // Full tile: no per-element guards.  Ordered stores use one wave-uniform
@@ -882,13 +893,11 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
                 typedef float v2f __attribute__((ext_vector_type(2)));
 #pragma unroll
                 for (int g = 0; g < FN / 2; ++g)
-                  __builtin_nontemporal_store(
-                      v2f{value(i, 2 * g, q * 4 + u, Pv[u], Lv[u]), value(i, 2 * g + 1, q * 4 + u, Pv[u], Lv[u])},
-                      (v2f*)((rowp + g * 64) + lane_off));
+                  store_y((v2f*)((rowp + g * 64) + lane_off),
+                          v2f{value(i, 2 * g, q * 4 + u, Pv[u], Lv[u]), value(i, 2 * g + 1, q * 4 + u, Pv[u], Lv[u])});
               } else {
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                  __builtin_nontemporal_store(value(i, j, q * 4 + u, Pv[u], Lv[u]), (rowp + j * 32) + lane_off);
+                for (int j = 0; j < FN; ++j) store_y((rowp + j * 32) + lane_off, value(i, j, q * 4 + u, Pv[u], Lv[u]));
               }
             }
           } else {
@@ -945,7 +954,7 @@ __global__ __launch_bounds__(NT, OCC) void gmm_kernel(KParams p) {
               }
               const float v = value(i, j, q * 4 + u, Pv[u], Lv[u]);
               if (ord_tile)
-                __builtin_nontemporal_store(v, base + colj[j]);
+                store_y(base + colj[j], v);
               else
                 __hip_atomic_fetch_add(base + colj[j], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -1902,6 +1911,7 @@ constexpr int kSegMax = 1024;  // longer segments take the scanning path
 // LDS in ascending order.  Rows in batches of kBatch: the batch's loads are
 // issued together (independent, streamed once), then folded in ascending
 // order; four float4 columns a kThreads apart per pass (32 loads in flight).
+template <bool CACHED>
 __device__ void fold_sorted_rows(const KParams& p, int64_t d, const int32_t* s_sorted, int len, int64_t j_lo,
                                  int64_t j_hi, bool from_out) {
   const int tid = threadIdx.x;
@@ -1929,7 +1939,7 @@ __device__ void fold_sorted_rows(const KParams& p, int64_t d, const int32_t* s_s
           const v4f* r = (const v4f*)(p.y + (int64_t)s_sorted[s0 + u] * n);
 #pragma unroll
           for (int c = 0; c < kCols; ++c)
-            if (ok[c]) yb[u][c] = __builtin_nontemporal_load(r + jc[c]);
+            if (ok[c]) yb[u][c] = CACHED ? r[jc[c]] : __builtin_nontemporal_load(r + jc[c]);
         }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
@@ -1952,6 +1962,7 @@ __device__ void fold_sorted_rows(const KParams& p, int64_t d, const int32_t* s_s
 // between chunks (the first chunk starts from the seed) -- the additions are
 // the same, in the same order, as one fold over all the rows.  Each thread
 // reads back only the out elements it wrote itself.
+template <bool CACHED>
 __device__ void fold_long_chunked(const KParams& p, int64_t d, int64_t covered, int32_t* s_rows, int32_t* s_wave,
                                   int64_t j_lo, int64_t j_hi) {
   constexpr int PER = kSegMax / kThreads;
@@ -1985,7 +1996,7 @@ __device__ void fold_long_chunked(const KParams& p, int64_t d, int64_t covered, 
       if ((hits >> u) & 1u) s_rows[pos++] = (int32_t)(i0 + u);
     __syncthreads();
     if (total > 0 || (!started && c0 + kSegMax >= covered)) {
-      fold_sorted_rows(p, d, s_rows, total, j_lo, j_hi, started);
+      fold_sorted_rows<CACHED>(p, d, s_rows, total, j_lo, j_hi, started);
       started = true;
     }
     __syncthreads();  // s_rows and s_wave are rewritten by the next chunk
@@ -2034,11 +2045,11 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p, const int32
         s_sorted[rank] = x;
       }
       __syncthreads();
-      fold_sorted_rows(p, d, s_sorted, len, f.lo, f.hi, false);
+      fold_sorted_rows<false>(p, d, s_sorted, len, f.lo, f.hi, false);
       __syncthreads();
     } else {
       if (covered < 0) covered = block_covered_rows(p, s_red);
-      fold_long_chunked(p, d, covered, s_sorted, s_wave, f.lo, f.hi);
+      fold_long_chunked<false>(p, d, covered, s_sorted, s_wave, f.lo, f.hi);
     }
   }
 }
@@ -2050,6 +2061,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p, const int32
 // count per thread, a block-wide exclusive scan of the counts), collects the
 // rows sent to it -- already ascending -- and folds them like reduce_kernel.
 constexpr int kScanPerThread = 16, kScanRows = kThreads * kScanPerThread;
+template <bool CACHED>
 __global__ __launch_bounds__(kThreads) void reduce_scan_kernel(KParams p) {
   __shared__ int32_t s_rows[kSegMax];
   __shared__ int32_t s_wave[kThreads / 64];
@@ -2119,10 +2131,10 @@ __global__ __launch_bounds__(kThreads) void reduce_scan_kernel(KParams p) {
       __syncthreads();  // s_wave is rewritten by the next chunk
     }
     if (len <= kSegMax) {
-      fold_sorted_rows(p, d, s_rows, len, f.lo, f.hi, false);
+      fold_sorted_rows<CACHED>(p, d, s_rows, len, f.lo, f.hi, false);
     } else {
       __syncthreads();  // every thread is done with this destination's first kSegMax rows
-      fold_long_chunked(p, d, covered, s_rows, s_wave, f.lo, f.hi);
+      fold_long_chunked<CACHED>(p, d, covered, s_rows, s_wave, f.lo, f.hi);
     }
     __syncthreads();  // s_rows is rewritten for the next destination
   }
@@ -2329,6 +2341,9 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
   kp.n4_ord = hybrid ? hybrid_cols4(a.n, plan.hybrid_atomic, false) : a.n / 4;
   kp.n4_seed = hybrid ? hybrid_cols4(a.n, plan.hybrid_atomic, true) : a.n / 4;
   kp.reduce_split = ordered_reduce_split(a.m, a.output_bs, kp.n4_ord * 4);
+  // a small y read back by the scan-lookup reduce (decode-sized problems)
+  // goes through the caches and is found in the MALL: decode step -1.9%
+  kp.y_cached = ordered && plan.scan_reduce && !a.mx && !a.fp8 && a.m * a.n * 4 <= kYCachedBytes;
   const MxPad mp = mx_pad(a.mx, a.m, a.k, a.n, a.e);
   const Workspace w = workspace_layout(a.m, a.n, a.output_bs, ordered, mp.a_bytes, mp.b_bytes);
   char* ws = (char*)workspace;
@@ -2441,8 +2456,10 @@ int launch_all(const LaunchArgs& a, const Plan& plan, void* workspace, void* str
   }
   if (ordered) {
     const int gr = (int)std::min<int64_t>(65535, a.output_bs * kp.reduce_split);
-    if (plan.scan_reduce)
-      hipLaunchKernelGGL(reduce_scan_kernel, dim3(gr > 0 ? gr : 1), dim3(kThreads), 0, s, kp);
+    if (plan.scan_reduce && kp.y_cached)
+      hipLaunchKernelGGL(reduce_scan_kernel<true>, dim3(gr > 0 ? gr : 1), dim3(kThreads), 0, s, kp);
+    else if (plan.scan_reduce)
+      hipLaunchKernelGGL(reduce_scan_kernel<false>, dim3(gr > 0 ? gr : 1), dim3(kThreads), 0, s, kp);
     else
       hipLaunchKernelGGL(reduce_kernel, dim3(gr > 0 ? gr : 1), dim3(kThreads), 0, s, kp,
                          (const int32_t*)(ws + w.offsets_off), (const int32_t*)(ws + w.list_off));
